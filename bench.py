@@ -1,0 +1,265 @@
+"""Benchmark of the InfLLM v2 block-sparse attention hot path on one MI355X.
+
+Headline (`value`): batched 128K decode throughput, tokens/s, for the
+decode_128k_b8 workload (8 sequences, 32 query / 8 KV heads, head_dim 128,
+131072-token caches, top-K 32 plus the own block): one step = block scoring
+over the whole k̄ table, top-K selection, and sparse attention (split + LSE
+combine) for the 8 new tokens, with k̄ already built. A second leg times the
+32K causal sparse prefill (kernel pooling + fused score/top-K + attention) in
+TFLOP/s. Inputs are seeded synthetic tensors (synth) resident in HBM;
+decode steps rotate over independent copies of K, V and k̄ so that the
+256 MB last-level cache cannot serve a step from the previous one.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ algorithmic work
+def decode_bytes(w) -> dict:
+    """Bytes the method must move per decode step (selected blocks + own block + k̄ scan + q/out)."""
+    bg = w.batch * w.n_kv_heads
+    C = (w.kv_len - 1) // 64
+    kbar = bg * C * 3 * w.head_dim * 2
+    sel = min(C, w.top_k)
+    own_keys = (w.kv_len - 1) % 64 + 1
+    kv = bg * (sel * 64 + own_keys) * w.head_dim * 2 * 2
+    qo = w.batch * w.n_q_heads * w.head_dim * 2 * 2
+    return dict(score=kbar + w.batch * w.n_q_heads * w.head_dim * 2, attn=kv + qo, total=kbar + kv + qo)
+
+
+def prefill_flops(w) -> dict:
+    """Algorithmic flops of a sparse prefill: scoring over candidates when C > K, attention over
+    the selected blocks plus the causal part of the own block (dense rows below the threshold)."""
+    t = np.arange(w.seq_len, dtype=np.int64)
+    C = t // 64
+    D, Hq = w.head_dim, w.n_q_heads
+    dense = (t + 1) < w.dense_threshold if w.dense_threshold > 0 else np.zeros_like(t, bool)
+    keys = np.where(dense, t + 1, 64 * np.minimum(C, w.top_k) + t % 64 + 1)
+    attn = float((4 * D * Hq * keys).sum()) * w.batch
+    score = float((2 * D * Hq * 3 * C[C > w.top_k]).sum()) * w.batch
+    return dict(attn=attn, score=score, total=attn + score)
+
+
+# ------------------------------------------------------------------ timing helpers
+def timed_loop(fns_per_step, steps, warmup, torch):
+    """Run warmup steps, then `steps` timed steps; events between stages give per-stage times."""
+    nst = len(fns_per_step(0))
+    for s in range(warmup):
+        for f in fns_per_step(s):
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for s in range(steps):
+        fs = fns_per_step(s)
+        ev[s][0].record()
+        for i, f in enumerate(fs):
+            f()
+            ev[s][i + 1].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    stage_ms = [float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)])) for i in range(nst)]
+    return total_ms / steps, stage_ms, wall
+
+
+# ------------------------------------------------------------------ decode leg
+def bench_decode(w, steps, warmup, rotations, torch, lib, ops, synth):
+    log(f"decode: generating {w.name} inputs")
+    t = time.perf_counter()
+    d = synth.generate(w, seed=0, threads=16)
+    log(f"decode: generated in {time.perf_counter() - t:.1f}s; uploading {rotations} rotation(s)")
+    cfg = lib.make_cfg(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, top_k=w.top_k,
+                       dense_threshold=w.dense_threshold)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    q = dev(d["q"])
+    k0, v0 = dev(d["k"]), dev(d["v"])
+    kbar0 = ops.pool_kernels(cfg, k0, d["kv_cap"], d["kv_len"])
+    sets = [(k0, v0, kbar0)] + [(k0.clone(), v0.clone(), kbar0.clone()) for _ in range(rotations - 1)]
+    del d
+    kv_cap, kv_len, n_q = w.kv_cap, w.kv_len, 1
+    nblk = ops.nblk(kv_cap)
+    scores = torch.empty((w.batch, w.n_kv_heads, n_q, nblk), dtype=torch.float32, device="cuda")
+    idx = torch.empty((w.batch, w.n_kv_heads, n_q, w.top_k), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.batch, w.n_q_heads, n_q, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    nbytes = lib.infllmv2_decode_workspace_bytes(cfg, n_q, kv_len)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(s):
+        k, v, kbar = sets[s % len(sets)]
+        return [
+            lambda: lib.infllmv2_score_blocks(cfg, q, n_q, kv_len - 1, 0, kbar, kv_cap, scores, stream),
+            lambda: lib.infllmv2_topk_blocks(cfg, scores, None, None, n_q, kv_len - 1, 0, kv_cap, idx, stream),
+            lambda: lib.infllmv2_sparse_attn_decode(cfg, q, n_q, k, v, kv_cap, kv_len, idx, None, out, None,
+                                                    ws, nbytes, stream),
+        ]
+    log(f"decode: timing {steps} steps after {warmup} warmup")
+    ms, stage_ms, _ = timed_loop(step, steps, warmup, torch)
+    return dict(ms=ms, stage_ms=stage_ms, bytes=decode_bytes(w))
+
+
+# ------------------------------------------------------------------ prefill leg
+def bench_prefill(w, steps, warmup, torch, lib, ops, synth):
+    log(f"prefill: generating {w.name} inputs")
+    d = synth.generate(w, seed=0, threads=16)
+    cfg = lib.make_cfg(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, top_k=w.top_k,
+                       dense_threshold=w.dense_threshold)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    q, k, v = dev(d["q"]), dev(d["k"]), dev(d["v"])
+    T, kv_cap = w.seq_len, d["kv_cap"]
+    del d
+    kbar = torch.zeros((w.batch, w.n_kv_heads, ops.nblk(kv_cap), 3, w.head_dim), dtype=torch.bfloat16,
+                       device="cuda")
+    idx = torch.empty((w.batch, w.n_kv_heads, T, w.top_k), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.batch, w.n_q_heads, T, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(s):
+        return [
+            lambda: lib.infllmv2_pool_kernels(cfg, k, kv_cap, T, 0, kbar, stream),
+            lambda: lib.infllmv2_topk_blocks(cfg, None, q, kbar, T, 0, 0, kv_cap, idx, stream),
+            lambda: lib.infllmv2_sparse_attn_prefill(cfg, q, T, k, v, kv_cap, T, idx, out, None, stream),
+        ]
+    log(f"prefill: timing {steps} steps after {warmup} warmup")
+    ms, stage_ms, _ = timed_loop(step, steps, warmup, torch)
+    return dict(ms=ms, stage_ms=stage_ms, flops=prefill_flops(w))
+
+
+# ------------------------------------------------------------------ CPU baseline (oracle)
+def cpu_baseline_decode(w, budget_s, synth):
+    import oracle as orc
+    log("cpu baseline: generating inputs and the oracle's k̄ (untimed)")
+    d = synth.generate(w, seed=0, threads=16)
+    kbar = orc.pool(d["k"], d["kv_len"])
+    n, t0 = 0, time.perf_counter()
+    while True:
+        orc.sparse_forward(d["q"], d["k"], d["v"], kv_len=d["kv_len"], q_pos0=d["kv_len"] - 1,
+                           n_kv_heads=w.n_kv_heads, top_k=w.top_k, dense_threshold=w.dense_threshold,
+                           kbar=kbar)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return dict(value=w.batch * n / el, unit="tok/s", cores=orc.num_threads(), kind="oracle",
+                sample=f"{n} full decode steps of {w.name} ({w.batch} sequences, all "
+                       f"{w.batch * w.n_kv_heads} KV-group rows; k̄ precomputed as on the GPU), {el:.1f}s")
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rotations", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import trainable_block_sparse_infllm_amd as lib
+    from trainable_block_sparse_infllm_amd import ops
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    lib.lib()
+
+    wd = synth.WORKLOADS["decode_128k_b8"]
+    dec = bench_decode(wd, args.steps, args.warmup, args.rotations, torch, lib, ops, synth)
+    tok_s = wd.batch / (dec["ms"] * 1e-3)
+    names = ["score_blocks", "topk_blocks", "sparse_attn_decode"]
+    stage = dict(zip(names, dec["stage_ms"]))
+    b = dec["bytes"]
+    score_gbs = b["score"] / (stage["score_blocks"] * 1e-3) / 1e9
+    attn_gbs = b["attn"] / (stage["sparse_attn_decode"] * 1e-3) / 1e9
+    step_gbs = b["total"] / (dec["ms"] * 1e-3) / 1e9
+    dominant = "score_blocks" if stage["score_blocks"] >= stage["sparse_attn_decode"] else "sparse_attn_decode"
+    dom_gbs = score_gbs if dominant == "score_blocks" else attn_gbs
+    dom_bytes = b["score"] if dominant == "score_blocks" else b["attn"]
+    result = {
+        "metric": "128K sparse-attn decode tok/s + prefill TFLOP/s; % HBM/MFMA roofline",
+        "value": round(tok_s, 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wd.name, "batch": wd.batch, "kv_len": wd.kv_len, "q_heads": wd.n_q_heads,
+                   "kv_heads": wd.n_kv_heads, "head_dim": wd.head_dim, "top_k": wd.top_k,
+                   "block": 64, "kernel_window": 32, "kernel_stride": 16, "rotations": args.rotations},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": dom_bytes},
+        "step_hbm": {"algorithmic_bytes": b["total"], "achieved_gbs": round(step_gbs, 1),
+                     "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
+        "stages_ms": {k: round(v, 5) for k, v in stage.items()},
+    }
+    if not args.no_prefill:
+        wp = synth.WORKLOADS["prefill_32k"]
+        pre = bench_prefill(wp, max(3, args.steps // 5), max(1, args.warmup // 5), torch, lib, ops, synth)
+        f = pre["flops"]
+        pst = dict(zip(["pool_kernels", "topk_blocks_fused", "sparse_attn_prefill"], pre["stage_ms"]))
+        tf = f["total"] / (pre["ms"] * 1e-3) / 1e12
+        attn_tf = f["attn"] / (pst["sparse_attn_prefill"] * 1e-3) / 1e12
+        result["prefill"] = {
+            "workload": wp.name, "tflops": round(tf, 2), "ms_per_step": round(pre["ms"], 4),
+            "frac_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_gflop": round(f["total"] / 1e9, 2),
+            "stages_ms": {k: round(v, 4) for k, v in pst.items()},
+            "roofline": {"bound": "mfma", "kernel": "sparse_attn_prefill", "achieved": round(attn_tf, 2),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+        }
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = n
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_decode(wd, args.cpu_seconds, synth)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,165 @@
+/*
+ * infllmv2.h -- C ABI of an MI355X (gfx950) library for InfLLM v2 block-sparse
+ * attention: semantic-kernel pooling, block scoring, top-K block selection, and
+ * sparse (prefill, decode, draft-tree) and dense attention.
+ *
+ * The method (MiniCPM4 technical-report summary, QbitAI repost, section
+ * "Model architecture: InfLLM v2 native sparse attention"): the context is cut
+ * into fixed-size blocks; each block is represented by several fine-grained
+ * "semantic kernels"; a query's relevance to a block is the maximum of its
+ * relevance to the kernels the block contains (item 1); the query heads of
+ * one GQA group share one set of blocks (item 2); attention then runs over the
+ * selected blocks only, and short contexts keep dense attention. Tree-draft
+ * verification uses the same sparse kernel with a local attention mask stored
+ * as packed bits (same summary, section on fusing speculative sampling,
+ * quantization and long-context algorithms).
+ *
+ * Fixed readings used throughout (the pages leave them open):
+ *   - block_size 64; kernels are the means of 32-key windows at stride 16 that
+ *     lie inside a block (3 per block), rounded to bf16 (nearest even);
+ *   - block score R(j) = sum over the group's query heads of the max over
+ *     block j's kernels of the raw dot product q . kbar (no scaling);
+ *   - a query at absolute position p has candidates j < floor(p/64) (complete
+ *     blocks before its own block); its own block floor(p/64) is always
+ *     attended, causally, on top of the K selected blocks;
+ *   - top-K keeps the K highest scores (compared in fp32), the lower block
+ *     index first on equal scores; the output row is ascending and padded
+ *     with -1 when there are fewer than K candidates (then all are taken);
+ *   - a query row with fewer than dense_threshold visible keys attends all of
+ *     them; dense_threshold 0 disables the rule;
+ *   - softmax scale 1/sqrt(head_dim) unless given; bf16 outputs are rounded
+ *     to nearest even; lse is the natural log of the softmax denominator.
+ *
+ * Conventions for every entry point:
+ *   - bf16 tensors are passed as device pointers to raw 16-bit patterns;
+ *     all pointers are device pointers unless stated; all tensors are dense,
+ *     row-major, 16-byte aligned;
+ *   - layouts: q   [B][Hq][n_q][D]         (heads g*G .. g*G+G-1 form group g)
+ *              k,v [B][Hkv][kv_cap][D]     (rows >= kv_len are never read)
+ *              kbar [B][Hkv][nblk][3][D]   nblk = ceil(kv_cap / 64)
+ *              scores [B][Hkv][n_q][nblk]  fp32, -inf past a row's candidates
+ *              idx [B][Hkv][n_q][K]        int32
+ *              out [B][Hq][n_q][D]         bf16
+ *              lse [B][Hq][n_q]            fp32, optional (NULL: not written)
+ *              tree_mask [B][n_q]          uint64
+ *   - the caller owns every buffer; the library allocates nothing, keeps no
+ *     pointer after returning, and takes scratch memory only as an explicit
+ *     workspace argument;
+ *   - `stream` is a hipStream_t (NULL = the default stream); each call checks
+ *     its arguments on the host, enqueues its kernels and returns without
+ *     synchronizing; calls on different streams may run from different threads;
+ *   - return value: 0 on success or a negative INFLLMV2_* status. Argument
+ *     checks run before any HIP call, so a rejected call launches nothing.
+ *     infllmv2_last_error() (per thread) describes the last failure.
+ */
+#ifndef INFLLMV2_H
+#define INFLLMV2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define INFLLMV2_API __attribute__((visibility("default")))
+#else
+#define INFLLMV2_API
+#endif
+
+#define INFLLMV2_OK 0
+#define INFLLMV2_INVALID_ARGUMENT (-1)   /* null pointer, bad shape, misaligned pointer */
+#define INFLLMV2_UNSUPPORTED (-2)        /* valid request this build does not run (device, shape) */
+#define INFLLMV2_WORKSPACE_TOO_SMALL (-3)
+#define INFLLMV2_HIP_ERROR (-4)          /* a HIP runtime call or kernel launch failed */
+
+typedef struct infllmv2_cfg {
+  int32_t batch;            /* B >= 1 */
+  int32_t n_q_heads;        /* Hq, a multiple of n_kv_heads */
+  int32_t n_kv_heads;       /* Hkv >= 1; G = Hq / Hkv must divide 16 */
+  int32_t head_dim;         /* D: 64 or 128 */
+  int32_t block_size;       /* 64 */
+  int32_t kernel_size;      /* 32 */
+  int32_t kernel_stride;    /* 16 */
+  int32_t top_k;            /* K >= 1 */
+  int32_t dense_threshold;  /* rows with fewer visible keys attend densely; 0 = never */
+  float softmax_scale;      /* <= 0 selects 1/sqrt(head_dim) */
+} infllmv2_cfg;
+
+/* Semantic kernels of the complete blocks j in [first_block, kv_len/64):
+ * kbar[b][g][j][m][:] = bf16(mean of k[b][g][64j+16m .. 64j+16m+31][:]), m = 0..2.
+ * (QbitAI summary, "Model architecture: InfLLM v2", item 1: blocks are made of
+ * fine-grained semantic kernels.) first_block lets a decode loop extend the
+ * table when a block completes; blocks outside the range are not written. */
+INFLLMV2_API int infllmv2_pool_kernels(const infllmv2_cfg* cfg, const void* k, int64_t kv_cap, int64_t kv_len,
+                          int64_t first_block, void* kbar, void* stream);
+
+/* Block scores of every query row (QbitAI summary, "Model architecture:
+ * InfLLM v2", items 1 and 2): scores[b][g][i][j] = sum over the heads h of
+ * group g of max over m of q[b][h][i] . kbar[b][g][j][m], for j < floor(p_i/64);
+ * -inf for every other j < nblk. Positions: p_i = q_pos0 + i, or q_pos0 for
+ * every row when is_tree != 0 (all draft nodes score against the prefix). */
+INFLLMV2_API int infllmv2_score_blocks(const infllmv2_cfg* cfg, const void* q, int32_t n_q, int64_t q_pos0,
+                          int32_t is_tree, const void* kbar, int64_t kv_cap, float* scores,
+                          void* stream);
+
+/* Top-K blocks per (b, g, i) row (same summary and section: only the most
+ * relevant blocks enter attention). With scores != NULL the rows are read from
+ * a score tensor laid out as above; with scores == NULL the scores are computed
+ * on the fly from q and kbar (the prefill path) and never stored. idx rows are
+ * ascending, padded with -1. Positions as for infllmv2_score_blocks.
+ * Candidate count floor(p/64) may be at most 4096. */
+INFLLMV2_API int infllmv2_topk_blocks(const infllmv2_cfg* cfg, const float* scores, const void* q,
+                         const void* kbar, int32_t n_q, int64_t q_pos0, int32_t is_tree,
+                         int64_t kv_cap, int32_t* idx, void* stream);
+
+/* Sparse causal attention for a chunk of n_q queries at positions
+ * kv_len - n_q + i (a whole-sequence prefill has n_q == kv_len): each row
+ * attends the 64 keys of each block in its group's idx row plus its own block
+ * up to itself, or every visible key when it has fewer than dense_threshold of
+ * them (QbitAI summary, "Model architecture: InfLLM v2": sparse attention over
+ * the selected blocks in both prefill and decode, dense for short contexts). */
+INFLLMV2_API int infllmv2_sparse_attn_prefill(const infllmv2_cfg* cfg, const void* q, int32_t n_q,
+                                 const void* k, const void* v, int64_t kv_cap, int64_t kv_len,
+                                 const int32_t* idx, void* out, float* lse, void* stream);
+
+/* Workspace (bytes, device memory) that infllmv2_sparse_attn_decode needs. */
+INFLLMV2_API size_t infllmv2_decode_workspace_bytes(const infllmv2_cfg* cfg, int32_t n_q, int64_t kv_len);
+
+/* Sparse attention of n_q new tokens against a KV cache, split across the
+ * selected blocks and merged by log-sum-exp.
+ *   tree_mask == NULL: rows sit at positions kv_len - n_q + i, as in prefill.
+ *   tree_mask != NULL: draft-tree verification (QbitAI summary, section on
+ *     fusing speculative sampling with long-context algorithms: the sparse
+ *     kernel verifies tree drafts through a local mask kept as packed bits).
+ *     Node i occupies cache slot P + i, P = kv_len - n_q, n_q <= 64; it attends
+ *     its own selected blocks (chosen with is_tree = 1), the keys of block
+ *     floor(P/64) before P, and every slot P + j whose bit j is set in
+ *     tree_mask[b][i] (bit i must be set; bits j > i must be clear).
+ * workspace: device memory of at least infllmv2_decode_workspace_bytes(). */
+INFLLMV2_API int infllmv2_sparse_attn_decode(const infllmv2_cfg* cfg, const void* q, int32_t n_q,
+                                const void* k_cache, const void* v_cache, int64_t kv_cap,
+                                int64_t kv_len, const int32_t* idx, const uint64_t* tree_mask,
+                                void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* Dense attention of n_q queries at positions kv_len - n_q + i over the first
+ * kv_len keys, causal (key <= position) or not: the short-context path
+ * (QbitAI summary, "Model architecture: InfLLM v2": dense attention kept for
+ * short sequences) and the reference the sparse path reduces to when K covers
+ * every block. top_k and dense_threshold are ignored. */
+INFLLMV2_API int infllmv2_dense_attn(const infllmv2_cfg* cfg, const void* q, int32_t n_q, const void* k,
+                        const void* v, int64_t kv_cap, int64_t kv_len, int32_t causal, void* out,
+                        float* lse, void* stream);
+
+/* Static text for a status code. */
+INFLLMV2_API const char* infllmv2_strerror(int status);
+
+/* Message describing the last failed call on this thread ("" if none). */
+INFLLMV2_API const char* infllmv2_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* INFLLMV2_H */

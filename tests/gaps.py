@@ -20,7 +20,7 @@ def boundary_gaps(R, Cn, K):
     return gaps
 
 
-def open_gaps(d, orc, group_rows=None, min_gap=1e-3, max_attempts=64, kbar=None):
+def open_gaps(d, orc, group_rows=None, min_gap=1e-3, max_attempts=64, kbar=None, pos=None):
     """Redraw query tokens in-place in d["q"] until every listed row clears min_gap.
 
     Returns (kbar, number of token redraws, smallest gap seen after fixing)."""
@@ -28,7 +28,8 @@ def open_gaps(d, orc, group_rows=None, min_gap=1e-3, max_attempts=64, kbar=None)
     G, K = w.group, w.top_k
     if kbar is None:
         kbar = orc.pool(d["k"], d["kv_len"])
-    pos = orc.positions(w.mode, d["n_q"], d["q_pos0"])
+    if pos is None:
+        pos = orc.positions(w.mode, d["n_q"], d["q_pos0"])
     pending = orc.all_group_rows(w.batch, w.n_kv_heads, d["n_q"]) if group_rows is None else \
         np.asarray(group_rows, dtype=np.int32).reshape(-1, 3)
     redrawn = 0

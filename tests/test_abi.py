@@ -1,0 +1,137 @@
+"""The C ABI without a GPU: the library loads, exports what the header declares,
+and rejects bad arguments before any HIP call."""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "infllmv2.h")
+
+
+@pytest.fixture(scope="module")
+def t():
+    import trainable_block_sparse_infllm_amd as pkg
+    if not os.path.exists(pkg.LIB_PATH):
+        from trainable_block_sparse_infllm_amd import build
+        build.build()
+    pkg.lib()
+    return pkg
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"INFLLMV2_API\s+[\w\s\*]*?\b(infllmv2_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_exports(t):
+    assert declared_functions() == sorted(t.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(t):
+    out = subprocess.run(["nm", "-D", "--defined-only", t.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (infllmv2_\w+)$", out, re.M))
+    assert set(declared_functions()) <= exported
+    for name in declared_functions():
+        assert hasattr(t.lib(), name)
+
+
+def test_internal_symbols_are_hidden(t):
+    out = subprocess.run(["nm", "-D", "--defined-only", t.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    assert "launch_attn_rows" not in out and "launch_decode" not in out
+
+
+def cfg_ok(t, **kw):
+    base = dict(batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, top_k=16, dense_threshold=1024)
+    base.update(kw)
+    return t.make_cfg(**base)
+
+
+A = 0x10000   # 16-byte aligned fake device addresses: never dereferenced on a rejected call
+B = 0x20000
+
+
+def call(t, name, *args):
+    import ctypes
+    fn = getattr(t.lib(), name)
+    args = [ctypes.byref(a) if hasattr(a, "_fields_") else a for a in args]
+    return fn(*args), t.infllmv2_last_error()
+
+
+CASES = [
+    # (entry point, cfg overrides, args after cfg, expected status, message fragment)
+    ("infllmv2_pool_kernels", None, (A, 64, 64, 0, B, None), -1, "cfg is NULL"),
+    ("infllmv2_pool_kernels", {}, (None, 64, 64, 0, B, None), -1, "k is NULL"),
+    ("infllmv2_pool_kernels", {}, (A + 2, 64, 64, 0, B, None), -1, "aligned"),
+    ("infllmv2_pool_kernels", {}, (A, 64, 65, 0, B, None), -1, "exceeds kv_cap"),
+    ("infllmv2_pool_kernels", {}, (A, 128, 128, 3, B, None), -1, "first_block"),
+    ("infllmv2_pool_kernels", dict(n_q_heads=30), (A, 64, 64, 0, B, None), -1, "multiple"),
+    ("infllmv2_pool_kernels", dict(head_dim=96), (A, 64, 64, 0, B, None), -2, "head_dim"),
+    ("infllmv2_pool_kernels", dict(block_size=128), (A, 128, 128, 0, B, None), -2, "block 64"),
+    ("infllmv2_pool_kernels", dict(kernel_size=33), (A, 64, 64, 0, B, None), -1, "geometry"),
+    ("infllmv2_pool_kernels", dict(n_q_heads=24, n_kv_heads=1), (A, 64, 64, 0, B, None), -2, "divide 16"),
+    ("infllmv2_score_blocks", {}, (A, 0, 0, 0, B, 64, A, None), -1, "n_q"),
+    ("infllmv2_score_blocks", {}, (A, 1, -1, 0, B, 64, A, None), -1, "q_pos0"),
+    ("infllmv2_score_blocks", {}, (A, 1, 640, 0, B, 64, A, None), -1, "beyond kv_cap"),
+    ("infllmv2_score_blocks", {}, (A, 65, 0, 1, B, 8192, A, None), -1, "64 nodes"),
+    ("infllmv2_score_blocks", {}, (A, 1, 0, 0, B, 64, A + 2, None), -1, "scores"),
+    ("infllmv2_topk_blocks", dict(top_k=0), (A, None, None, 1, 0, 0, 64, B, None), -1, "top_k"),
+    ("infllmv2_topk_blocks", {}, (None, None, B, 1, 0, 0, 64, B, None), -1, "q is NULL"),
+    ("infllmv2_topk_blocks", {}, (A, None, None, 1, 0, 0, 64, None, None), -1, "idx is NULL"),
+    ("infllmv2_topk_blocks", {}, (A, None, None, 1, 300000, 0, 1 << 20, B, None), -2, "4096"),
+    ("infllmv2_sparse_attn_prefill", {}, (A, 65, A, A, 64, 64, B, A, None, None), -1, "n_q"),
+    ("infllmv2_sparse_attn_prefill", {}, (A, 64, A, A, 64, 64, None, A, None, None), -1, "idx is NULL"),
+    ("infllmv2_sparse_attn_prefill", dict(top_k=1024), (A, 64, A, A, 64, 64, B, A, None, None), -2, "top_k"),
+    ("infllmv2_sparse_attn_prefill", {}, (A, 64, A, A, 64, 64, B, A, A + 1, None), -1, "lse"),
+    ("infllmv2_sparse_attn_decode", {}, (A, 1, A, A, 64, 64, B, None, A, None, A + 16, 1 << 30, None), -1, "workspace is not 256"),
+    ("infllmv2_sparse_attn_decode", {}, (A, 1, A, A, 64, 64, B, None, A, None, 0x100000, 16, None), -3, "workspace"),
+    ("infllmv2_sparse_attn_decode", {}, (A, 65, A, A, 128, 128, B, None, A, None, 0x100000, 1 << 30, None), -1, "64 query rows"),
+    ("infllmv2_sparse_attn_decode", {}, (A, 2, A, A, 128, 128, B, A + 4, A, None, 0x100000, 1 << 30, None), -1, "tree_mask"),
+    ("infllmv2_dense_attn", {}, (A, 1, A, A, 64, 0, 1, B, None, None), -1, "kv_len"),
+    ("infllmv2_dense_attn", {}, (A, 1, A, None, 64, 64, 1, B, None, None), -1, "v is NULL"),
+    ("infllmv2_dense_attn", dict(softmax_scale=float("nan")), (A, 1, A, A, 64, 64, 1, B, None, None), -1, "finite"),
+]
+
+
+@pytest.mark.parametrize("name,over,args,status,frag", CASES)
+def test_rejected_before_any_hip_call(t, name, over, args, status, frag):
+    cfg = None if over is None else cfg_ok(t, **over)
+    rc, msg = call(t, name, cfg, *args)
+    assert rc == status, msg
+    assert frag in msg and name in msg
+
+
+def test_strerror(t):
+    assert t.infllmv2_strerror(0) == "ok"
+    assert t.infllmv2_strerror(-1) == "invalid argument"
+    assert t.infllmv2_strerror(-2) == "unsupported"
+    assert t.infllmv2_strerror(-3) == "workspace too small"
+    assert t.infllmv2_strerror(-4) == "HIP error"
+    assert t.infllmv2_strerror(7) == "unknown status"
+
+
+def test_workspace_bytes(t):
+    cfg = cfg_ok(t, batch=8, top_k=32)
+    n1 = t.infllmv2_decode_workspace_bytes(cfg, 1, 131072)
+    n16 = t.infllmv2_decode_workspace_bytes(cfg, 16, 131088)
+    assert n1 > 0 and n16 > n1
+    assert t.infllmv2_decode_workspace_bytes(cfg, 0, 10) == 0
+    assert t.infllmv2_decode_workspace_bytes(cfg, 5, 3) == 0
+
+
+def test_binding_raises_with_status(t):
+    cfg = cfg_ok(t)
+    with pytest.raises(t.InfLLMv2Error) as e:
+        t.infllmv2_dense_attn(cfg, A, 1, A, None, 64, 64, 1, B, None, stream=0)
+    assert e.value.status == -1 and "v is NULL" in e.value.message
+
+
+def test_valid_call_without_gpu_reports_hip_error(t):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    rc, msg = call(t, "infllmv2_pool_kernels", cfg_ok(t), A, 64, 64, 0, B, None)
+    assert rc == -4 and "HIP error" in msg

@@ -1,0 +1,13 @@
+"""InfLLM v2 block-sparse attention for MI355X (gfx950): Python side of the C ABI.
+
+The compute path lives in libinfllmv2.so (hand-written HIP kernels); this
+package only marshals arguments (see capi.py) and offers small helpers that
+allocate outputs with torch and call the C entry points in order.
+"""
+from .capi import (  # noqa: F401
+    EXPORTS, InfLLMv2Error, infllmv2_cfg, make_cfg, lib, LIB_PATH,
+    infllmv2_pool_kernels, infllmv2_score_blocks, infllmv2_topk_blocks,
+    infllmv2_sparse_attn_prefill, infllmv2_decode_workspace_bytes,
+    infllmv2_sparse_attn_decode, infllmv2_dense_attn, infllmv2_strerror, infllmv2_last_error,
+)
+from . import ops  # noqa: F401

@@ -1,0 +1,461 @@
+// Sparse attention of a few new tokens against a long KV cache: decode steps
+// and draft-tree verification. (MiniCPM4 technical-report summary, QbitAI
+// repost, section "Model architecture: InfLLM v2": sparse attention speeds up
+// decoding too, and the blocks read per token stay constant as the context
+// grows; section on fusing speculative sampling with long-context algorithms:
+// the sparse kernel verifies tree drafts through a local mask kept as bits.)
+//
+// HBM-bound: per (b, g) the kernel reads each needed 64-key block of K and V
+// once (64*D*2*2 bytes) and serves all n_q*G query rows of the group with it.
+// The blocks of the union are split across workgroups (flash-decoding style);
+// each writes an unnormalized partial (m, l, O) per row, and a combine kernel
+// merges the partials by log-sum-exp.
+//
+//   union (n_q > 1 only): per (b, g), the ascending list of blocks any row
+//     needs, each with a bitmask of the rows (tokens) that need it;
+//   split: one wavefront per (b, g, split of SB union entries). K fragments
+//     go from HBM straight into MFMA registers (A operand of S^T = K Q^T);
+//     V goes through LDS stored transposed (A operand of O^T = V^T P^T);
+//   combine: one wavefront per (b, h, row).
+#include <algorithm>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace infllmv2 {
+
+namespace {
+
+constexpr int kVst = 64 + 4;  // V^T row stride in LDS (bf16)
+
+struct DecodeLayout {
+  int64_t bgs, max_e, nsplit, rows_pad;
+  size_t off_union, off_mask, off_count, off_ml, off_o, total;
+};
+
+DecodeLayout decode_layout(const Dims& d, int n_q, int64_t kv_len) {
+  DecodeLayout L{};
+  L.bgs = int64_t(d.B) * d.Hkv;
+  const int64_t P = kv_len - n_q;
+  const int64_t last_blk = (kv_len - 1) / kBlock;
+  const bool maybe_dense = d.dense_thr > 0 && P + 1 < d.dense_thr;
+  if (n_q == 1) {
+    L.max_e = maybe_dense ? last_blk + 1 : int64_t(d.K) + 1;
+  } else {
+    const int64_t local = last_blk - P / kBlock + 1;
+    L.max_e = maybe_dense ? last_blk + 1 : std::min(last_blk + 1, int64_t(n_q) * d.K + local);
+  }
+  const int64_t sb = std::max<int64_t>(1, (L.bgs * L.max_e + 4095) / 4096);
+  L.nsplit = (L.max_e + sb - 1) / sb;
+  L.rows_pad = (int64_t(n_q) * d.G + 15) / 16 * 16;
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  size_t off = 0;
+  L.off_union = off;
+  off = al(off + (n_q > 1 ? size_t(L.bgs * L.max_e) * 4 : 0));
+  L.off_mask = off;
+  off = al(off + (n_q > 1 ? size_t(L.bgs * L.max_e) * 8 : 0));
+  L.off_count = off;
+  off = al(off + size_t(L.bgs) * 4);
+  L.off_ml = off;
+  off = al(off + size_t(L.bgs * L.nsplit * L.rows_pad) * 2 * 4);
+  L.off_o = off;
+  off = al(off + size_t(L.bgs * L.nsplit * L.rows_pad) * d.D * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ union
+__global__ __launch_bounds__(256) void decode_union_kernel(
+    const int32_t* __restrict__ idx, const uint64_t* __restrict__ tree_mask,
+    int32_t* __restrict__ u_blk, uint64_t* __restrict__ u_mask, int32_t* __restrict__ u_count,
+    int Hkv, int n_q, int K, int64_t kv_len, int is_tree, int dense_thr, int64_t max_e) {
+  extern __shared__ uint64_t nm[];          // [last_blk + 1] row masks per block
+  __shared__ int s_cnt[256];
+  const int bg = blockIdx.x;
+  const int b = bg / Hkv;
+  const int tid = threadIdx.x;
+  const int64_t P = kv_len - n_q;
+  const int nb = int((kv_len - 1) / kBlock) + 1;
+  for (int j = tid; j < nb; j += 256) nm[j] = 0ull;
+  __syncthreads();
+  for (int e = tid; e < n_q * K; e += 256) {
+    const int i = e / K;
+    const int64_t own = (is_tree ? P : P + i) / kBlock;
+    const int j = idx[(int64_t(bg) * n_q + i) * K + e % K];
+    if (j >= 0 && j < own) atomicOr(reinterpret_cast<unsigned long long*>(&nm[j]), 1ull << i);
+  }
+  for (int i = tid; i < n_q; i += 256) {
+    const int64_t own = (is_tree ? P : P + i) / kBlock;
+    bool dense;
+    if (is_tree) {
+      dense = dense_thr > 0 && P + __popcll(tree_mask[int64_t(b) * n_q + i]) < dense_thr;
+    } else {
+      dense = dense_thr > 0 && P + i + 1 < dense_thr;
+      atomicOr(reinterpret_cast<unsigned long long*>(&nm[own]), 1ull << i);
+    }
+    if (dense)
+      for (int64_t j = 0; j < own; ++j) atomicOr(reinterpret_cast<unsigned long long*>(&nm[j]), 1ull << i);
+  }
+  if (is_tree) {
+    const uint64_t all = n_q >= 64 ? ~0ull : ((1ull << n_q) - 1ull);
+    for (int64_t j = P / kBlock + tid; j < nb; j += 256)
+      atomicOr(reinterpret_cast<unsigned long long*>(&nm[j]), all);
+  }
+  __syncthreads();
+  // ascending compaction: thread t scans blocks [t*per, (t+1)*per)
+  const int per = (nb + 255) / 256;
+  const int lo = min(nb, tid * per), hi = min(nb, lo + per);
+  int c = 0;
+  for (int j = lo; j < hi; ++j) c += nm[j] != 0ull;
+  s_cnt[tid] = c;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {      // inclusive scan
+    const int x = tid >= o ? s_cnt[tid - o] : 0;
+    __syncthreads();
+    s_cnt[tid] += x;
+    __syncthreads();
+  }
+  int pos = s_cnt[tid] - c;
+  for (int j = lo; j < hi; ++j) {
+    if (nm[j] != 0ull && pos < max_e) {
+      u_blk[int64_t(bg) * max_e + pos] = j;
+      u_mask[int64_t(bg) * max_e + pos] = nm[j];
+      ++pos;
+    }
+  }
+  if (tid == 255) u_count[bg] = min<int64_t>(s_cnt[255], max_e);
+}
+
+// ------------------------------------------------------------------ split
+template <int D, int NSTD>
+__global__ __launch_bounds__(64) void decode_split_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ idx, const uint64_t* __restrict__ tree_mask,
+    const int32_t* __restrict__ u_blk, const uint64_t* __restrict__ u_mask,
+    const int32_t* __restrict__ u_count, float* __restrict__ part_ml, float* __restrict__ part_o,
+    int Hq, int Hkv, int G, int n_q, int64_t kv_cap, int64_t kv_len, int K, int dense_thr,
+    int is_tree, int sb, int nsplit, int max_e, int rows_pad, float scale_log2) {
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  __shared__ __align__(16) uint16_t vt[D * kVst];
+  const int l = lane_id();
+  const int r16 = l % 16, kg = l / 16;
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = item % nsplit;
+  const int bg = item / nsplit;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int row0 = blockIdx.y * 16 * NSTD;
+  const int64_t P = kv_len - n_q;
+  const uint16_t* kbase = k + int64_t(bg) * kv_cap * D;
+  const uint16_t* vbase = v + int64_t(bg) * kv_cap * D;
+
+  int n_e;
+  bool dense1 = false;
+  int64_t own1 = 0;
+  if (n_q == 1) {
+    own1 = (kv_len - 1) / kBlock;
+    dense1 = dense_thr > 0 && kv_len < dense_thr;
+    n_e = dense1 ? int(own1) + 1 : K + 1;
+  } else {
+    n_e = u_count[bg];
+  }
+  const int u0 = split * sb;
+  const int u1 = min(u0 + sb, n_e);
+
+  // rows of this lane: sub-tile s, row r16 -> (node, head)
+  int node_of[NSTD];
+  uint64_t tmask[NSTD];
+  bf16x8 qf[NSTD][KS];
+#pragma unroll
+  for (int s = 0; s < NSTD; ++s) {
+    const int row = row0 + s * 16 + r16;
+    const int node = row / G, hh = row % G;
+    node_of[s] = node < n_q ? node : -1;
+    tmask[s] = (is_tree && node < n_q) ? tree_mask[int64_t(b) * n_q + node] : 0ull;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 x = {0, 0, 0, 0};
+      if (node < n_q) x = ldg16(q + ((int64_t(b) * Hq + g * G + hh) * n_q + node) * D + ks * 32 + kg * 8);
+      qf[s][ks] = as_bf16x8(x);
+    }
+  }
+
+  f32x4 oacc[NSTD][DT];
+  float m_run[NSTD], l_run[NSTD];
+#pragma unroll
+  for (int s = 0; s < NSTD; ++s) {
+    m_run[s] = -INFINITY;
+    l_run[s] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[s][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int u = u0; u < u1; ++u) {
+    int64_t j;
+    uint64_t nmask;
+    if (n_q == 1) {
+      j = dense1 ? u : (u < K ? idx[int64_t(bg) * K + u] : own1);
+      if (!dense1 && u < K && (j < 0 || j >= own1)) continue;
+      nmask = 1ull;
+    } else {
+      j = u_blk[int64_t(bg) * max_e + u];
+      nmask = u_mask[int64_t(bg) * max_e + u];
+    }
+    const int64_t key0 = j * kBlock;
+
+    // K fragments straight from HBM: lane feeds key 16*kt + r16, d = 32*ks + 8*kg .. +7
+    bf16x8 kf[4][KS];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int64_t key = key0 + kt * 16 + r16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 x = {0, 0, 0, 0};
+        if (key < kv_len) x = ldg16(kbase + key * D + ks * 32 + kg * 8);
+        kf[kt][ks] = as_bf16x8(x);
+      }
+    }
+    // V: 2 keys x 8 d per piece -> LDS transposed
+    constexpr int VP = 32 * (D / 8) / 64;
+    uint4 vr[VP][2];
+#pragma unroll
+    for (int x = 0; x < VP; ++x) {
+      const int p = l + 64 * x;
+      const int dg = p % (D / 8), rp = p / (D / 8);
+      const int64_t key = key0 + 2 * rp;
+      vr[x][0] = key < kv_len ? ldg16(vbase + key * D + dg * 8) : uint4{0, 0, 0, 0};
+      vr[x][1] = key + 1 < kv_len ? ldg16(vbase + (key + 1) * D + dg * 8) : uint4{0, 0, 0, 0};
+    }
+    __syncthreads();                       // previous block's V^T reads are done
+    {
+      uint32_t* vt32 = reinterpret_cast<uint32_t*>(vt);
+#pragma unroll
+      for (int x = 0; x < VP; ++x) {
+        const int p = l + 64 * x;
+        const int dg = p % (D / 8), rp = p / (D / 8);
+        const uint32_t a[4] = {vr[x][0].x, vr[x][0].y, vr[x][0].z, vr[x][0].w};
+        const uint32_t c[4] = {vr[x][1].x, vr[x][1].y, vr[x][1].z, vr[x][1].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vt32[((8 * dg + 2 * e) * kVst) / 2 + rp] = (a[e] & 0xFFFFu) | (c[e] << 16);
+          vt32[((8 * dg + 2 * e + 1) * kVst) / 2 + rp] = (a[e] >> 16) | (c[e] & 0xFFFF0000u);
+        }
+      }
+    }
+    __syncthreads();
+
+    bool sub_on[NSTD], row_on[NSTD];
+#pragma unroll
+    for (int s = 0; s < NSTD; ++s) {
+      row_on[s] = node_of[s] >= 0 && ((nmask >> node_of[s]) & 1ull);
+      sub_on[s] = ballot64(row_on[s]) != 0ull;
+    }
+    f32x4 sacc[NSTD][4];
+#pragma unroll
+    for (int s = 0; s < NSTD; ++s) {
+      if (!sub_on[s]) continue;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) a = mfma16(kf[kt][ks], qf[s][ks], a);
+        sacc[s][kt] = a;
+      }
+    }
+    bf16x8 pf[NSTD][2];
+#pragma unroll
+    for (int s = 0; s < NSTD; ++s) {
+      if (!sub_on[s]) continue;
+      const int node = node_of[s];
+      const int64_t p_row = P + (node < 0 ? 0 : node);
+      float mb = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t key = key0 + kt * 16 + kg * 4 + i;
+          bool ok;
+          if (is_tree)
+            ok = key < P || (key < kv_len && ((tmask[s] >> (key - P)) & 1ull));
+          else
+            ok = key <= p_row;
+          const float x = (row_on[s] && ok) ? sacc[s][kt][i] * scale_log2 : -INFINITY;
+          sacc[s][kt][i] = x;
+          mb = fmaxf(mb, x);
+        }
+      mb = fmaxf(mb, __shfl_xor(mb, 16));
+      mb = fmaxf(mb, __shfl_xor(mb, 32));
+      const float m_new = fmaxf(m_run[s], mb);
+      const bool none = m_new == -INFINITY;
+      const float alpha = none ? 1.f : exp2f(m_run[s] - m_new);
+      float ps = 0.f;
+      float pv[4][4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = none ? 0.f : exp2f(sacc[s][kt][i] - m_new);
+          pv[kt][i] = e;
+          ps += e;
+        }
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      l_run[s] = l_run[s] * alpha + ps;
+      m_run[s] = m_new;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[s][dt][i] *= alpha;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        uint4 uu;
+        uu.x = pack_bf16x2(pv[2 * k2][0], pv[2 * k2][1]);
+        uu.y = pack_bf16x2(pv[2 * k2][2], pv[2 * k2][3]);
+        uu.z = pack_bf16x2(pv[2 * k2 + 1][0], pv[2 * k2 + 1][1]);
+        uu.w = pack_bf16x2(pv[2 * k2 + 1][2], pv[2 * k2 + 1][3]);
+        pf[s][k2] = as_bf16x8(uu);
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const uint16_t* vr2 = vt + (dt * 16 + r16) * kVst + k2 * 32 + kg * 4;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vr2);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vr2 + 16);
+        const bf16x8 vf = as_bf16x8(uint4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+        for (int s = 0; s < NSTD; ++s) {
+          if (!sub_on[s]) continue;
+          oacc[s][dt] = mfma16(vf, pf[s][k2], oacc[s][dt]);
+        }
+      }
+    }
+  }
+
+  // partials: ml[bg][split][row] = (m, l); o[bg][split][row][d] (unnormalized)
+#pragma unroll
+  for (int s = 0; s < NSTD; ++s) {
+    const int row = row0 + s * 16 + r16;
+    if (row >= rows_pad) continue;
+    const int64_t pr = (int64_t(bg) * nsplit + split) * rows_pad + row;
+    if (kg == 0) {
+      part_ml[pr * 2 + 0] = m_run[s];
+      part_ml[pr * 2 + 1] = l_run[s];
+    }
+    if (m_run[s] != -INFINITY) {
+      float* dst = part_o + pr * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<float4*>(dst + dt * 16 + kg * 4) =
+            make_float4(oacc[s][dt][0], oacc[s][dt][1], oacc[s][dt][2], oacc[s][dt][3]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ combine
+template <int D>
+__global__ __launch_bounds__(256) void decode_combine_kernel(
+    const float* __restrict__ part_ml, const float* __restrict__ part_o,
+    const int32_t* __restrict__ u_count, uint16_t* __restrict__ out, float* __restrict__ lse,
+    int Hq, int Hkv, int G, int n_q, int nsplit, int sb, int n_e1, int rows_pad, int64_t nrows) {
+  constexpr int CPL = D / kWave;
+  const int l = lane_id();
+  const int64_t rid = int64_t(blockIdx.x) * 4 + threadIdx.x / kWave;   // (b, h, i)
+  if (rid >= nrows) return;
+  const int i = int(rid % n_q);
+  const int h = int((rid / n_q) % Hq);
+  const int b = int(rid / (int64_t(n_q) * Hq));
+  const int g = h / G;
+  const int bg = b * Hkv + g;
+  const int row = i * G + h % G;
+  const int n_e = n_q == 1 ? n_e1 : u_count[bg];
+  const int ns = min(nsplit, (n_e + sb - 1) / sb);
+  float m = -INFINITY, lsum = 0.f;
+  float acc[CPL];
+#pragma unroll
+  for (int x = 0; x < CPL; ++x) acc[x] = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const int64_t pr = (int64_t(bg) * nsplit + s) * rows_pad + row;
+    const float ms = part_ml[pr * 2 + 0];
+    if (ms == -INFINITY) continue;
+    const float ls = part_ml[pr * 2 + 1];
+    const float m_new = fmaxf(m, ms);
+    const float a = exp2f(m - m_new), c = exp2f(ms - m_new);
+    const float* src = part_o + pr * D + CPL * l;
+#pragma unroll
+    for (int x = 0; x < CPL; ++x) acc[x] = acc[x] * a + src[x] * c;
+    lsum = lsum * a + ls * c;
+    m = m_new;
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  uint16_t* dst = out + rid * D + CPL * l;
+#pragma unroll
+  for (int x = 0; x < CPL; ++x) dst[x] = f2bf(acc[x] * inv);
+  if (lse && l == 0) lse[rid] = (m + log2f(lsum)) * 0.69314718055994531f;
+}
+
+size_t decode_workspace_bytes(const Dims& d, int n_q, int64_t kv_len) {
+  return decode_layout(d, n_q, kv_len).total;
+}
+
+hipError_t launch_decode(const Dims& d, const uint16_t* q, int n_q, const uint16_t* k,
+                         const uint16_t* v, int64_t kv_cap, int64_t kv_len, const int32_t* idx,
+                         const uint64_t* tree_mask, uint16_t* out, float* lse, void* ws,
+                         size_t ws_bytes, hipStream_t s) {
+  const DecodeLayout L = decode_layout(d, n_q, kv_len);
+  if (ws_bytes < L.total) return hipErrorInvalidValue;
+  char* base = static_cast<char*>(ws);
+  int32_t* u_blk = reinterpret_cast<int32_t*>(base + L.off_union);
+  uint64_t* u_mask = reinterpret_cast<uint64_t*>(base + L.off_mask);
+  int32_t* u_count = reinterpret_cast<int32_t*>(base + L.off_count);
+  float* part_ml = reinterpret_cast<float*>(base + L.off_ml);
+  float* part_o = reinterpret_cast<float*>(base + L.off_o);
+  const int is_tree = tree_mask != nullptr;
+  const int sb = int((L.max_e + L.nsplit - 1) / L.nsplit);
+  if (n_q > 1) {
+    const int nb = int((kv_len - 1) / kBlock) + 1;
+    const size_t lds = size_t(nb) * 8;
+    if (lds > 64 * 1024) return hipErrorInvalidValue;
+    decode_union_kernel<<<dim3(unsigned(L.bgs)), 256, lds, s>>>(
+        idx, tree_mask, u_blk, u_mask, u_count, d.Hkv, n_q, d.K, kv_len, is_tree, d.dense_thr,
+        L.max_e);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int rows = n_q * d.G;
+  const int nstd_total = (rows + 15) / 16;
+  const int nstd = nstd_total >= 2 ? 2 : nstd_total;
+  const unsigned ygroups = unsigned((nstd_total + nstd - 1) / nstd);
+  const dim3 grid(unsigned(L.bgs * L.nsplit), ygroups);
+  const float sl2 = d.scale * 1.4426950408889634f;
+  const int n_e1 = int(L.max_e);
+#define SPLIT_CASE(DD, NN)                                                                        \
+  if (d.D == DD && nstd == NN) {                                                                  \
+    decode_split_kernel<DD, NN><<<grid, 64, 0, s>>>(q, k, v, idx, tree_mask, u_blk, u_mask,       \
+                                                    u_count, part_ml, part_o, d.Hq, d.Hkv, d.G,  \
+                                                    n_q, kv_cap, kv_len, d.K, d.dense_thr,       \
+                                                    is_tree, sb, int(L.nsplit), int(L.max_e),    \
+                                                    int(L.rows_pad), sl2);                       \
+  } else
+  SPLIT_CASE(128, 1) SPLIT_CASE(128, 2) SPLIT_CASE(64, 1) SPLIT_CASE(64, 2)
+  { return hipErrorInvalidValue; }
+#undef SPLIT_CASE
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t nrows = int64_t(d.B) * d.Hq * n_q;
+  const dim3 cgrid(unsigned((nrows + 3) / 4));
+  if (d.D == 128)
+    decode_combine_kernel<128><<<cgrid, 256, 0, s>>>(part_ml, part_o, u_count, out, lse, d.Hq,
+                                                     d.Hkv, d.G, n_q, int(L.nsplit), sb, n_e1,
+                                                     int(L.rows_pad), nrows);
+  else
+    decode_combine_kernel<64><<<cgrid, 256, 0, s>>>(part_ml, part_o, u_count, out, lse, d.Hq,
+                                                    d.Hkv, d.G, n_q, int(L.nsplit), sb, n_e1,
+                                                    int(L.rows_pad), nrows);
+  return hipGetLastError();
+}
+
+}  // namespace infllmv2

@@ -1,0 +1,111 @@
+// Device-side helpers shared by the gfx950 kernels: bf16 conversion, MFMA
+// fragment types, wavefront reductions, and the XCD-aware grid remap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace infllmv2 {
+
+constexpr int kWave = 64;     // CDNA wavefront width
+constexpr int kBlock = 64;    // tokens per context block
+constexpr int kKpb = 3;       // semantic kernels per block (window 32, stride 16)
+constexpr int kNumXcd = 8;    // MI355X: 8 accelerator complex dies, one L2 each
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// float -> bf16 bits, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f2bf(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+}
+
+// Exact double (a mean of bf16 values) -> bf16 bits, round to nearest even.
+__device__ __forceinline__ uint16_t d2bf(double x) {
+  uint64_t u = __double_as_longlong(x);
+  const uint16_t sign = uint16_t((u >> 48) & 0x8000u);
+  u &= 0x7FFFFFFFFFFFFFFFull;
+  if (u > 0x7FF0000000000000ull) return 0x7FC0;                 // NaN
+  if (u < 0x3810000000000000ull) {                              // |x| < 2^-126: quantum 2^-133
+    const double a = __longlong_as_double(u);
+    return sign | uint16_t(rint(a * 0x1p133));                  // 0..128 (128 = smallest normal)
+  }
+  u += 0x00001FFFFFFFFFFFull + ((u >> 45) & 1ull);              // round at bit 45 (7 kept bits)
+  const int e = int(u >> 52) - 1023;
+  if (e > 127) return sign | 0x7F80;                            // overflow -> inf
+  return sign | uint16_t(((e + 127) << 7) | int((u >> 45) & 0x7Fu));
+}
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &v, sizeof r);
+  return r;
+}
+
+__device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+template <int W>
+__device__ __forceinline__ float xor_max(float v) {
+#pragma unroll
+  for (int o = 1; o < W; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+template <int W>
+__device__ __forceinline__ float xor_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < W; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ int wave_min_i32(int v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v = min(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint32_t popc64(uint64_t x) { return __popcll(x); }
+
+// Lanes below this one whose bit is set in `mask`.
+__device__ __forceinline__ uint32_t mbcnt64(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
+
+// Order-preserving map fp32 -> uint32 (larger float -> larger key; -inf lowest
+// among non-NaN values).
+__device__ __forceinline__ uint32_t ordered_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on
+// XCD i % 8). Renumber them so that each XCD receives one contiguous range of
+// work items: neighbouring items (same KV group) then share one L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  const int per = nblocks / kNumXcd;
+  const int rem = nblocks % kNumXcd;
+  const int xcd = bid % kNumXcd;
+  const int slot = bid / kNumXcd;
+  // XCDs 0..rem-1 own per+1 items, the rest own per.
+  const int base = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
+  return base + slot;
+}
+
+}  // namespace infllmv2

@@ -1,0 +1,39 @@
+// Internal launchers: one per kernel family. The C ABI layer (api.cpp) checks
+// arguments and picks template instances; these functions only enqueue work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace infllmv2 {
+
+struct Dims {
+  int B, Hq, Hkv, G, D, K, dense_thr;
+  float scale;
+};
+
+hipError_t launch_pool(const Dims& d, const uint16_t* k, int64_t kv_cap, int64_t nblk,
+                       int64_t first, int64_t last, uint16_t* kbar, hipStream_t s);
+
+hipError_t launch_scores(const Dims& d, const uint16_t* q, int n_q, int64_t q_pos0, int is_tree,
+                         const uint16_t* kbar, int64_t nblk, float* scores, hipStream_t s);
+
+hipError_t launch_topk_from_scores(const Dims& d, const float* scores, int n_q, int64_t q_pos0,
+                                   int is_tree, int64_t nblk, int32_t* idx, hipStream_t s);
+
+hipError_t launch_topk_fused(const Dims& d, const uint16_t* q, const uint16_t* kbar, int n_q,
+                             int64_t q_pos0, int is_tree, int64_t nblk, int32_t* idx, hipStream_t s);
+
+// mode: 0 sparse (idx + dense threshold), 1 dense causal, 2 dense without mask.
+hipError_t launch_attn_rows(const Dims& d, int mode, const uint16_t* q, int n_q, const uint16_t* k,
+                            const uint16_t* v, int64_t kv_cap, int64_t kv_len, const int32_t* idx,
+                            uint16_t* out, float* lse, hipStream_t s);
+
+size_t decode_workspace_bytes(const Dims& d, int n_q, int64_t kv_len);
+
+hipError_t launch_decode(const Dims& d, const uint16_t* q, int n_q, const uint16_t* k,
+                         const uint16_t* v, int64_t kv_cap, int64_t kv_len, const int32_t* idx,
+                         const uint64_t* tree_mask, uint16_t* out, float* lse, void* ws,
+                         size_t ws_bytes, hipStream_t s);
+
+}  // namespace infllmv2

@@ -1,0 +1,244 @@
+// Top-K block selection (MiniCPM4 technical-report summary, QbitAI repost,
+// section "Model architecture: InfLLM v2": only the most relevant context
+// blocks take part in attention; item 2: one block set per GQA group).
+//
+// Rule: with at most K candidates all are taken; otherwise the K highest
+// scores, compared as fp32, with the lower block index first on equal scores.
+// Rows are written ascending and padded with -1.
+//
+// One wavefront selects one row whose n <= 64*KPL candidates sit in registers
+// (candidate j in lane j % 64, slot j / 64). The K-th largest score key T is
+// found bit by bit from the most significant end, each step counting the keys
+// >= a trial value with one ballot per slot; the row is then emitted in index
+// order with ballot/mbcnt compaction, taking every key > T and the first
+// K - #(> T) keys equal to T. All decisions are integer comparisons on
+// order-preserving score keys, so the choice is exact for the given scores.
+//
+// Two producers feed it: a score tensor (decode, trees), or scores computed
+// in the same workgroup with MFMA and kept in LDS (prefill; never stored).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace infllmv2 {
+
+template <int KPL>
+__device__ __forceinline__ void wave_topk(const uint32_t (&key)[KPL], int n, int K,
+                                          int32_t* __restrict__ out) {
+  const int l = lane_id();
+  if (n <= K) {
+    for (int t = l; t < K; t += kWave) out[t] = t < n ? t : -1;
+    return;
+  }
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int r = 0; r < KPL; ++r) cnt += popc64(ballot64(key[r] >= cand));
+    if (cnt >= uint32_t(K)) T = cand;
+  }
+  uint32_t ngt = 0;
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) ngt += popc64(ballot64(key[r] > T));
+  const uint32_t take_eq = uint32_t(K) - ngt;
+  uint32_t base = 0, eq_seen = 0;
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) {
+    const bool eq = key[r] == T;
+    const uint64_t eqm = ballot64(eq);
+    const bool take = key[r] > T || (eq && eq_seen + mbcnt64(eqm) < take_eq);
+    const uint64_t tm = ballot64(take);
+    if (take) out[base + mbcnt64(tm)] = r * kWave + l;
+    base += popc64(tm);
+    eq_seen += popc64(eqm);
+  }
+}
+
+// ---------------------------------------------------------------- from scores
+template <int KPL>
+__global__ __launch_bounds__(256) void topk_scores_kernel(const float* __restrict__ scores,
+                                                          int32_t* __restrict__ idx, int64_t rows,
+                                                          int n_q, int64_t q_pos0, int is_tree,
+                                                          int64_t nblk, int K) {
+  const int l = lane_id();
+  const int64_t row = int64_t(blockIdx.x) * 4 + threadIdx.x / kWave;
+  if (row >= rows) return;
+  const int node = int(row % n_q);
+  const int64_t pos = is_tree ? q_pos0 : q_pos0 + node;
+  int64_t C = pos / kBlock;
+  if (C > nblk) C = nblk;
+  const float* src = scores + row * nblk;
+  uint32_t key[KPL];
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) {
+    const int64_t j = int64_t(r) * kWave + l;
+    key[r] = j < C ? ordered_key(src[j]) : 0u;
+  }
+  wave_topk<KPL>(key, int(C), K, idx + row * K);
+}
+
+// ---------------------------------------------------------- fused prefill path
+// Workgroup: 4 wavefronts, 16*NT query columns = TQ = 16*NT/G tokens of one
+// (b, g). Waves split the 16-block chunks of the k̄ table (MFMA, max over the
+// 3 kernel slots, head sum by shuffles) and park the scores in LDS
+// sc[TQ][64*KPL]; then each wave selects the rows of TQ/4 tokens.
+template <int D, int NT, int KPL>
+__global__ __launch_bounds__(256) void topk_fused_kernel(const uint16_t* __restrict__ q,
+                                                         const uint16_t* __restrict__ kbar,
+                                                         int32_t* __restrict__ idx, int Hq, int Hkv,
+                                                         int G, int n_q, int64_t q_pos0,
+                                                         int is_tree, int64_t nblk, int K,
+                                                         int ntile) {
+  constexpr int KS = D / 32;
+  constexpr int LDSC = KPL * kWave;
+  extern __shared__ float sc[];
+  const int w = threadIdx.x / kWave;
+  const int l = lane_id();
+  const int r16 = l % 16, kg = l / 16;
+  const int TQ = 16 * NT / G;
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = item % ntile;
+  const int bg = item / ntile;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int tok0 = tile * TQ;
+  const int ntok = min(TQ, n_q - tok0);
+  const int64_t pos_last = is_tree ? q_pos0 : q_pos0 + tok0 + ntok - 1;
+  int64_t Cmax = pos_last / kBlock;
+  if (Cmax > nblk) Cmax = nblk;
+
+  if (Cmax > K) {
+    bf16x8 qf[NT][KS];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int c = nt * 16 + r16;
+      const int t = c / G, hh = c % G;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 v = {0, 0, 0, 0};
+        if (t < ntok)
+          v = ldg16(q + ((int64_t(b) * Hq + g * G + hh) * n_q + tok0 + t) * D + ks * 32 + kg * 8);
+        qf[nt][ks] = as_bf16x8(v);
+      }
+    }
+    const int nchunk = int((Cmax + 15) / 16);
+    for (int ch = w; ch < nchunk; ch += 4) {
+      const int64_t j0 = int64_t(ch) * 16;
+      const int64_t jrow = j0 + r16;
+      const bool row_ok = jrow < Cmax;
+      const uint16_t* kb = kbar + ((int64_t(bg) * nblk + (row_ok ? jrow : 0)) * kKpb) * D + kg * 8;
+      f32x4 best[NT];
+#pragma unroll
+      for (int m = 0; m < kKpb; ++m) {
+        bf16x8 af[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          uint4 v = {0, 0, 0, 0};
+          if (row_ok) v = ldg16(kb + m * D + ks * 32);
+          af[ks] = as_bf16x8(v);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) acc = mfma16(af[ks], qf[nt][ks], acc);
+          if (m == 0) {
+            best[nt] = acc;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) best[nt][i] = fmaxf(best[nt][i], acc[i]);
+          }
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = best[nt][i];
+          for (int o = 1; o < G; o <<= 1) v += __shfl_xor(v, o);
+          best[nt][i] = v;
+        }
+        const int c = nt * 16 + r16;
+        if (c % G == 0) {
+          float* dst = sc + (c / G) * LDSC;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t j = j0 + kg * 4 + i;
+            if (j < LDSC) dst[j] = best[nt][i];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  for (int t = w; t < ntok; t += 4) {
+    const int64_t pos = is_tree ? q_pos0 : q_pos0 + tok0 + t;
+    int64_t C = pos / kBlock;
+    if (C > nblk) C = nblk;
+    uint32_t key[KPL];
+#pragma unroll
+    for (int r = 0; r < KPL; ++r) {
+      const int j = r * kWave + l;
+      key[r] = (C > K && j < C) ? ordered_key(sc[t * LDSC + j]) : 0u;
+    }
+    wave_topk<KPL>(key, int(C), K, idx + ((int64_t(bg) * n_q + tok0 + t) * K));
+  }
+}
+
+static int pick_kpl(int64_t cmax) {
+  int kpl = 1;
+  while (int64_t(kpl) * kWave < cmax) kpl <<= 1;
+  return kpl;
+}
+
+hipError_t launch_topk_from_scores(const Dims& d, const float* scores, int n_q, int64_t q_pos0,
+                                   int is_tree, int64_t nblk, int32_t* idx, hipStream_t s) {
+  const int64_t rows = int64_t(d.B) * d.Hkv * n_q;
+  const int64_t pos_last = is_tree ? q_pos0 : q_pos0 + n_q - 1;
+  int64_t cmax = pos_last / kBlock;
+  if (cmax > nblk) cmax = nblk;
+  const int kpl = pick_kpl(cmax);
+  const dim3 grid(unsigned((rows + 3) / 4));
+#define TOPK_CASE(P)                                                                           \
+  if (kpl == P) {                                                                              \
+    topk_scores_kernel<P><<<grid, 256, 0, s>>>(scores, idx, rows, n_q, q_pos0, is_tree, nblk, \
+                                               d.K);                                           \
+    return hipGetLastError();                                                                  \
+  }
+  TOPK_CASE(1) TOPK_CASE(2) TOPK_CASE(4) TOPK_CASE(8) TOPK_CASE(16) TOPK_CASE(32) TOPK_CASE(64)
+#undef TOPK_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_topk_fused(const Dims& d, const uint16_t* q, const uint16_t* kbar, int n_q,
+                             int64_t q_pos0, int is_tree, int64_t nblk, int32_t* idx,
+                             hipStream_t s) {
+  const int64_t pos_last = is_tree ? q_pos0 : q_pos0 + n_q - 1;
+  int64_t cmax = pos_last / kBlock;
+  if (cmax > nblk) cmax = nblk;
+  const int kpl = pick_kpl(cmax);
+  // Columns per workgroup: largest of 64/32/16 whose score tile fits 64 KB of LDS.
+  int nt = 4;
+  while (nt > 1 && int64_t(16 * nt / d.G) * kpl * kWave * 4 > 65536) nt >>= 1;
+  if (16 * nt < d.G) return hipErrorInvalidValue;
+  const int tq = 16 * nt / d.G;
+  const int ntile = (n_q + tq - 1) / tq;
+  const size_t lds = size_t(tq) * kpl * kWave * sizeof(float);
+  if (lds > 65536) return hipErrorInvalidValue;
+  const dim3 grid(unsigned(int64_t(d.B) * d.Hkv * ntile));
+#define FUSED_CASE(DD, NN, P)                                                                   \
+  if (d.D == DD && nt == NN && kpl == P) {                                                      \
+    topk_fused_kernel<DD, NN, P><<<grid, 256, lds, s>>>(q, kbar, idx, d.Hq, d.Hkv, d.G, n_q,   \
+                                                        q_pos0, is_tree, nblk, d.K, ntile);     \
+    return hipGetLastError();                                                                   \
+  }
+#define FUSED_D(DD, NN) \
+  FUSED_CASE(DD, NN, 1) FUSED_CASE(DD, NN, 2) FUSED_CASE(DD, NN, 4) FUSED_CASE(DD, NN, 8) \
+  FUSED_CASE(DD, NN, 16) FUSED_CASE(DD, NN, 32) FUSED_CASE(DD, NN, 64)
+  FUSED_D(128, 4) FUSED_D(128, 2) FUSED_D(128, 1) FUSED_D(64, 4) FUSED_D(64, 2) FUSED_D(64, 1)
+#undef FUSED_D
+#undef FUSED_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace infllmv2

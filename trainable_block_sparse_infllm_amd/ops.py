@@ -1,0 +1,87 @@
+"""Call sequences over the C ABI: allocate outputs with torch, call the entry points in order.
+
+Every step runs in the HIP library; these helpers only allocate and marshal.
+bf16 tensors may be torch.bfloat16 or 16-bit integer tensors holding bf16 bits.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import capi
+
+
+def _bf16_like(shape, ref):
+    return torch.empty(shape, dtype=torch.bfloat16, device=ref.device)
+
+
+def nblk(kv_cap: int, block: int = 64) -> int:
+    return (kv_cap + block - 1) // block
+
+
+class Workspace:
+    """A reusable device buffer for the decode entry point (grown on demand)."""
+
+    def __init__(self, device):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int):
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+def pool_kernels(cfg, k, kv_cap, kv_len, first_block=0, kbar=None, stream=None):
+    B, Hkv, _, D = k.shape
+    if kbar is None:
+        kbar = torch.zeros((B, Hkv, nblk(kv_cap), 3, D), dtype=torch.bfloat16, device=k.device)
+    capi.infllmv2_pool_kernels(cfg, k, kv_cap, kv_len, first_block, kbar, stream)
+    return kbar
+
+
+def sparse_prefill(cfg, q, k, v, *, with_lse=True, stream=None):
+    """Whole-sequence prefill: kernels -> fused score/top-K -> sparse attention."""
+    B, Hq, T, D = q.shape
+    kv_cap = k.shape[2]
+    kbar = pool_kernels(cfg, k, kv_cap, T, stream=stream)
+    idx = torch.empty((B, cfg.n_kv_heads, T, cfg.top_k), dtype=torch.int32, device=q.device)
+    capi.infllmv2_topk_blocks(cfg, None, q, kbar, T, 0, 0, kv_cap, idx, stream)
+    out = _bf16_like((B, Hq, T, D), q)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device) if with_lse else None
+    capi.infllmv2_sparse_attn_prefill(cfg, q, T, k, v, kv_cap, T, idx, out, lse, stream)
+    return dict(kbar=kbar, idx=idx, out=out, lse=lse)
+
+
+def decode(cfg, q, k_cache, v_cache, kbar, kv_len, *, tree_mask=None, ws: Workspace | None = None,
+           with_lse=True, stream=None):
+    """n_q new tokens (tree nodes when tree_mask is given): scores -> top-K -> split attention."""
+    B, Hq, n_q, D = q.shape
+    kv_cap = k_cache.shape[2]
+    is_tree = tree_mask is not None
+    q_pos0 = kv_len - n_q if is_tree else kv_len - n_q
+    scores = torch.empty((B, cfg.n_kv_heads, n_q, nblk(kv_cap)), dtype=torch.float32, device=q.device)
+    capi.infllmv2_score_blocks(cfg, q, n_q, q_pos0, is_tree, kbar, kv_cap, scores, stream)
+    idx = torch.empty((B, cfg.n_kv_heads, n_q, cfg.top_k), dtype=torch.int32, device=q.device)
+    capi.infllmv2_topk_blocks(cfg, scores, None, None, n_q, q_pos0, is_tree, kv_cap, idx, stream)
+    out = _bf16_like((B, Hq, n_q, D), q)
+    lse = torch.empty((B, Hq, n_q), dtype=torch.float32, device=q.device) if with_lse else None
+    nbytes = capi.infllmv2_decode_workspace_bytes(cfg, n_q, kv_len)
+    ws = ws or Workspace(q.device)
+    buf = ws.get(nbytes)
+    capi.infllmv2_sparse_attn_decode(cfg, q, n_q, k_cache, v_cache, kv_cap, kv_len, idx, tree_mask, out, lse,
+                                     buf, buf.numel(), stream)
+    return dict(scores=scores, idx=idx, out=out, lse=lse)
+
+
+def dense(cfg, q, k, v, kv_len, *, causal=True, with_lse=True, stream=None):
+    B, Hq, n_q, D = q.shape
+    out = _bf16_like((B, Hq, n_q, D), q)
+    lse = torch.empty((B, Hq, n_q), dtype=torch.float32, device=q.device) if with_lse else None
+    capi.infllmv2_dense_attn(cfg, q, n_q, k, v, k.shape[2], kv_len, causal, out, lse, stream)
+    return dict(out=out, lse=lse)
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)
