@@ -136,7 +136,6 @@ def test_topk_from_fp32_scores_is_exact_with_ties():
     B, Hkv, n_q, nblk, K = 2, 3, 5, 300, 16
     R = np.round(rng.standard_normal((B * Hkv * n_q, nblk)) * 4) / 4
     q_pos0 = 64 * 250
-    C = np.full(B * Hkv * n_q, (q_pos0 + np.arange(n_q)) // 64).reshape(B * Hkv, n_q).T.T.ravel()
     C = np.tile((q_pos0 + np.arange(n_q)) // 64, B * Hkv)
     for r in range(R.shape[0]):
         R[r, C[r]:] = -np.inf

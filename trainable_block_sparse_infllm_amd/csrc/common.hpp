@@ -39,7 +39,7 @@ __device__ __forceinline__ uint16_t d2bf(double x) {
     const double a = __longlong_as_double(u);
     return sign | uint16_t(rint(a * 0x1p133));                  // 0..128 (128 = smallest normal)
   }
-  u += 0x00001FFFFFFFFFFFull + ((u >> 45) & 1ull);              // round at bit 45 (7 kept bits)
+  u += 0x00000FFFFFFFFFFFull + ((u >> 45) & 1ull);              // RNE: half of 2^45, minus 1, plus lsb
   const int e = int(u >> 52) - 1023;
   if (e > 127) return sign | 0x7F80;                            // overflow -> inf
   return sign | uint16_t(((e + 127) << 7) | int((u >> 45) & 0x7Fu));
