@@ -26,8 +26,6 @@ namespace infllmv2 {
 
 namespace {
 
-constexpr int kVst = 64 + 4;  // V^T row stride in LDS (bf16)
-
 struct DecodeLayout {
   int64_t bgs, max_e, nsplit, rows_pad;
   size_t off_union, off_mask, off_count, off_ml, off_o, total;
@@ -129,17 +127,47 @@ __global__ __launch_bounds__(256) void decode_union_kernel(
 }
 
 // ------------------------------------------------------------------ split
+// V tile in LDS, row-major (64 keys x D), 16-byte pieces XOR-swizzled by key:
+// piece p of row r holds V[r][8*(p ^ sw(r)) .. +7] with sw(r) = 2*((r >> 2) & 3).
+// It is filled straight from HBM (global_load_lds, 1 KB per wavefront
+// instruction). A V^T fragment element V[key][d] is one 2-byte read; the four
+// 16-lane groups of a fragment read use keys 4 apart, so the swizzle sends
+// them to distinct pieces and the read is free of bank conflicts. For these
+// keys sw(key) = 2*kg, a per-lane constant, so every address is a base plus a
+// compile-time offset.
+// 16 zero bytes in device memory: the source of rows past kv_len.
+__device__ __align__(16) const uint32_t kZero16[4] = {0u, 0u, 0u, 0u};
+
+template <int D>
+__device__ __forceinline__ void load_v_tile(const uint16_t* vbase, int64_t key0, int64_t kv_len,
+                                            uint16_t* vt) {
+  constexpr int PPR = D / 8;                 // 16-byte pieces per row
+  constexpr int RPI = kWave / PPR;           // rows per 1 KB instruction
+  const int l = lane_id();
+#pragma unroll
+  for (int x = 0; x < kBlock / RPI; ++x) {
+    const int r = x * RPI + l / PPR;
+    const int piece = l % PPR;
+    const int64_t key = key0 + r;
+    const int sw = ((r >> 2) & 3) << 1;
+    const void* src = key < kv_len ? static_cast<const void*>(vbase + key * D + ((piece ^ sw) << 3))
+                                   : static_cast<const void*>(kZero16);
+    load_lds16(src, vt + x * RPI * D);
+  }
+}
+
 template <int D, int NSTD>
-__global__ __launch_bounds__(64) void decode_split_kernel(
+__global__ __launch_bounds__(64, NSTD == 1 ? 2 : 1) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, const uint64_t* __restrict__ tree_mask,
     const int32_t* __restrict__ u_blk, const uint64_t* __restrict__ u_mask,
     const int32_t* __restrict__ u_count, float* __restrict__ part_ml, float* __restrict__ part_o,
-    int Hq, int Hkv, int G, int n_q, int64_t kv_cap, int64_t kv_len, int K, int dense_thr,
-    int is_tree, int sb, int nsplit, int max_e, int rows_pad, float scale_log2) {
+    int Hq, int Hkv, int G, int n_q, int64_t kv_cap,
+    int64_t kv_len, int K, int dense_thr, int is_tree, int sb, int nsplit, int max_e, int rows_pad,
+    float scale_log2) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
-  __shared__ __align__(16) uint16_t vt[D * kVst];
+  __shared__ __align__(16) uint16_t vt[kBlock * D];
   const int l = lane_id();
   const int r16 = l % 16, kg = l / 16;
   const int item = xcd_remap(blockIdx.x, gridDim.x);
@@ -205,6 +233,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     }
     const int64_t key0 = j * kBlock;
 
+    wait_lds();                                    // previous block's V reads are done
+    load_v_tile<D>(vbase, key0, kv_len, vt);       // V -> LDS, no registers
     // K fragments straight from HBM: lane feeds key 16*kt + r16, d = 32*ks + 8*kg .. +7
     bf16x8 kf[4][KS];
 #pragma unroll
@@ -217,34 +247,6 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
         kf[kt][ks] = as_bf16x8(x);
       }
     }
-    // V: 2 keys x 8 d per piece -> LDS transposed
-    constexpr int VP = 32 * (D / 8) / 64;
-    uint4 vr[VP][2];
-#pragma unroll
-    for (int x = 0; x < VP; ++x) {
-      const int p = l + 64 * x;
-      const int dg = p % (D / 8), rp = p / (D / 8);
-      const int64_t key = key0 + 2 * rp;
-      vr[x][0] = key < kv_len ? ldg16(vbase + key * D + dg * 8) : uint4{0, 0, 0, 0};
-      vr[x][1] = key + 1 < kv_len ? ldg16(vbase + (key + 1) * D + dg * 8) : uint4{0, 0, 0, 0};
-    }
-    __syncthreads();                       // previous block's V^T reads are done
-    {
-      uint32_t* vt32 = reinterpret_cast<uint32_t*>(vt);
-#pragma unroll
-      for (int x = 0; x < VP; ++x) {
-        const int p = l + 64 * x;
-        const int dg = p % (D / 8), rp = p / (D / 8);
-        const uint32_t a[4] = {vr[x][0].x, vr[x][0].y, vr[x][0].z, vr[x][0].w};
-        const uint32_t c[4] = {vr[x][1].x, vr[x][1].y, vr[x][1].z, vr[x][1].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vt32[((8 * dg + 2 * e) * kVst) / 2 + rp] = (a[e] & 0xFFFFu) | (c[e] << 16);
-          vt32[((8 * dg + 2 * e + 1) * kVst) / 2 + rp] = (a[e] >> 16) | (c[e] & 0xFFFF0000u);
-        }
-      }
-    }
-    __syncthreads();
 
     bool sub_on[NSTD], row_on[NSTD];
 #pragma unroll
@@ -318,14 +320,23 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
         pf[s][k2] = as_bf16x8(uu);
       }
     }
+    wait_vmem();                                   // the V tile has landed in LDS
+    const uint16_t* vlane = vt + 4 * kg * D + r16;  // key 4*kg, column r16 (swizzle applied per dt)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
+      const uint16_t* vcol = vlane + ((dt ^ kg) << 4);
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        const uint16_t* vr2 = vt + (dt * 16 + r16) * kVst + k2 * 32 + kg * 4;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr2);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr2 + 16);
-        const bf16x8 vf = as_bf16x8(uint4{lo.x, lo.y, hi.x, hi.y});
+        // key slots (kg, jj): key = 32*k2 + 16*(jj/4) + 4*kg + jj%4, matching pf's packing
+        uint32_t w4[4];
+#pragma unroll
+        for (int hp = 0; hp < 4; ++hp) {
+          const int koff = 32 * k2 + 16 * (hp / 2) + 2 * (hp % 2);   // jj = 2*hp
+          const uint32_t lo = vcol[koff * D];
+          const uint32_t hi = vcol[(koff + 1) * D];
+          w4[hp] = lo | (hi << 16);
+        }
+        const bf16x8 vf = as_bf16x8(uint4{w4[0], w4[1], w4[2], w4[3]});
 #pragma unroll
         for (int s = 0; s < NSTD; ++s) {
           if (!sub_on[s]) continue;
@@ -356,6 +367,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
 }
 
 // ------------------------------------------------------------------ combine
+// One wavefront per output row (b, h, i): the split maxima and sums are read
+// with lanes over splits (one round trip), then each lane accumulates its D/64
+// columns over the splits with independent loads, weights broadcast by shuffle.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     const float* __restrict__ part_ml, const float* __restrict__ part_o,
@@ -373,28 +387,42 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   const int row = i * G + h % G;
   const int n_e = n_q == 1 ? n_e1 : u_count[bg];
   const int ns = min(nsplit, (n_e + sb - 1) / sb);
-  float m = -INFINITY, lsum = 0.f;
+  const int64_t pr0 = int64_t(bg) * nsplit * rows_pad + row;   // split s at pr0 + s * rows_pad
+  float M = -INFINITY;
+  for (int s0 = 0; s0 < ns; s0 += kWave) {
+    const int s = s0 + l;
+    const float ms = s < ns ? part_ml[(pr0 + int64_t(s) * rows_pad) * 2] : -INFINITY;
+    M = fmaxf(M, xor_max<kWave>(ms));
+  }
+  float L = 0.f;
   float acc[CPL];
 #pragma unroll
   for (int x = 0; x < CPL; ++x) acc[x] = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const int64_t pr = (int64_t(bg) * nsplit + s) * rows_pad + row;
-    const float ms = part_ml[pr * 2 + 0];
-    if (ms == -INFINITY) continue;
-    const float ls = part_ml[pr * 2 + 1];
-    const float m_new = fmaxf(m, ms);
-    const float a = exp2f(m - m_new), c = exp2f(ms - m_new);
-    const float* src = part_o + pr * D + CPL * l;
+  for (int s0 = 0; s0 < ns; s0 += kWave) {
+    const int s = s0 + l;
+    float wgt = 0.f, ls = 0.f;
+    if (s < ns) {
+      const float ms = part_ml[(pr0 + int64_t(s) * rows_pad) * 2];
+      ls = part_ml[(pr0 + int64_t(s) * rows_pad) * 2 + 1];
+      wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
+    }
+    L += xor_sum<kWave>(wgt * ls);
+    const int cnt = min(kWave, ns - s0);
+#pragma unroll 8
+    for (int t = 0; t < cnt; ++t) {
+      const float wt = __shfl(wgt, t);
+      const float* src = part_o + (pr0 + int64_t(s0 + t) * rows_pad) * D + CPL * l;
+      if (wt != 0.f) {
 #pragma unroll
-    for (int x = 0; x < CPL; ++x) acc[x] = acc[x] * a + src[x] * c;
-    lsum = lsum * a + ls * c;
-    m = m_new;
+        for (int x = 0; x < CPL; ++x) acc[x] += wt * src[x];
+      }
+    }
   }
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
   uint16_t* dst = out + rid * D + CPL * l;
 #pragma unroll
   for (int x = 0; x < CPL; ++x) dst[x] = f2bf(acc[x] * inv);
-  if (lse && l == 0) lse[rid] = (m + log2f(lsum)) * 0.69314718055994531f;
+  if (lse && l == 0) lse[rid] = (M + log2f(L)) * 0.69314718055994531f;
 }
 
 size_t decode_workspace_bytes(const Dims& d, int n_q, int64_t kv_len) {

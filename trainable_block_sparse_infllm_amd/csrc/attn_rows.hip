@@ -343,9 +343,11 @@ static hipError_t launch_rows_t(const Dims& d, int mode, const uint16_t* q, int 
   const size_t lds = size_t(2 * S::BUF) * 2 + 8 * sizeof(int) + size_t(TQ) * (mode == 0 ? d.K : 0) * 4;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   auto kern = attn_rows_kernel<D, G, NST>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-  if (e != hipSuccess) return e;
+  // raise the dynamic-LDS limit of this instance once (the largest request any call can make)
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     160 * 1024);
+  if (attr != hipSuccess) return attr;
   const dim3 grid(unsigned(int64_t(d.B) * d.Hkv * ntile));
   kern<<<grid, 256, lds, s>>>(q, k, v, idx, out, lse, d.Hq, d.Hkv, n_q, kv_cap, kv_len, d.K,
                               d.dense_thr, mode, d.scale * 1.4426950408889634f, ntile);

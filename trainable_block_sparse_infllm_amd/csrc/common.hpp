@@ -57,6 +57,23 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+typedef __attribute__((address_space(1))) void gas_void;   // global address space
+typedef __attribute__((address_space(3))) void las_void;   // LDS address space
+
+// Direct HBM -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
+// lane l's 16 bytes land at lds_base + 16*l; lds_base must be wave-uniform.
+// Completion is tracked by the vector-memory counter only (see wait_vmem).
+__device__ __forceinline__ void load_lds16(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((gas_void*)gsrc, (las_void*)lds_base, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(0): every vector-memory load of this wave, including the
+// direct-to-LDS ones the compiler does not track, has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// s_waitcnt lgkmcnt(0): every LDS access of this wave has completed.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 template <int W>
 __device__ __forceinline__ float xor_max(float v) {
 #pragma unroll
