@@ -135,9 +135,6 @@ __global__ __launch_bounds__(256) void decode_union_kernel(
 // them to distinct pieces and the read is free of bank conflicts. For these
 // keys sw(key) = 2*kg, a per-lane constant, so every address is a base plus a
 // compile-time offset.
-// 16 zero bytes in device memory: the source of rows past kv_len.
-__device__ __align__(16) const uint32_t kZero16[4] = {0u, 0u, 0u, 0u};
-
 template <int D>
 __device__ __forceinline__ void load_v_tile(const uint16_t* vbase, int64_t key0, int64_t kv_len,
                                             uint16_t* vt) {
@@ -151,7 +148,7 @@ __device__ __forceinline__ void load_v_tile(const uint16_t* vbase, int64_t key0,
     const int64_t key = key0 + r;
     const int sw = ((r >> 2) & 3) << 1;
     const void* src = key < kv_len ? static_cast<const void*>(vbase + key * D + ((piece ^ sw) << 3))
-                                   : static_cast<const void*>(kZero16);
+                                   : static_cast<const void*>(kZeroPiece);
     load_lds16(src, vt + x * RPI * D);
   }
 }
@@ -204,9 +201,8 @@ __global__ __launch_bounds__(64, NSTD == 1 ? 2 : 1) void decode_split_kernel(
     tmask[s] = (is_tree && node < n_q) ? tree_mask[int64_t(b) * n_q + node] : 0ull;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      uint4 x = {0, 0, 0, 0};
-      if (node < n_q) x = ldg16(q + ((int64_t(b) * Hq + g * G + hh) * n_q + node) * D + ks * 32 + kg * 8);
-      qf[s][ks] = as_bf16x8(x);
+      const uint16_t* qrow = q + ((int64_t(b) * Hq + g * G + hh) * n_q + (node < n_q ? node : 0)) * D;
+      qf[s][ks] = as_bf16x8(ldg16_if(node < n_q, qrow + ks * 32 + kg * 8));
     }
   }
 
@@ -241,11 +237,8 @@ __global__ __launch_bounds__(64, NSTD == 1 ? 2 : 1) void decode_split_kernel(
     for (int kt = 0; kt < 4; ++kt) {
       const int64_t key = key0 + kt * 16 + r16;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        uint4 x = {0, 0, 0, 0};
-        if (key < kv_len) x = ldg16(kbase + key * D + ks * 32 + kg * 8);
-        kf[kt][ks] = as_bf16x8(x);
-      }
+      for (int ks = 0; ks < KS; ++ks)
+        kf[kt][ks] = as_bf16x8(ldg16_if(key < kv_len, kbase + key * D + ks * 32 + kg * 8));
     }
 
     bool sub_on[NSTD], row_on[NSTD];
@@ -356,13 +349,11 @@ __global__ __launch_bounds__(64, NSTD == 1 ? 2 : 1) void decode_split_kernel(
       part_ml[pr * 2 + 0] = m_run[s];
       part_ml[pr * 2 + 1] = l_run[s];
     }
-    if (m_run[s] != -INFINITY) {
-      float* dst = part_o + pr * D;
+    float* dst = part_o + pr * D;       // zeros when the row saw no key in this split
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<float4*>(dst + dt * 16 + kg * 4) =
-            make_float4(oacc[s][dt][0], oacc[s][dt][1], oacc[s][dt][2], oacc[s][dt][3]);
-    }
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(dst + dt * 16 + kg * 4) =
+          make_float4(oacc[s][dt][0], oacc[s][dt][1], oacc[s][dt][2], oacc[s][dt][3]);
   }
 }
 
@@ -391,7 +382,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   float M = -INFINITY;
   for (int s0 = 0; s0 < ns; s0 += kWave) {
     const int s = s0 + l;
-    const float ms = s < ns ? part_ml[(pr0 + int64_t(s) * rows_pad) * 2] : -INFINITY;
+    const float ms = ldf_or_neginf(s < ns, part_ml + (pr0 + int64_t(s) * rows_pad) * 2);
     M = fmaxf(M, xor_max<kWave>(ms));
   }
   float L = 0.f;
@@ -400,22 +391,18 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   for (int x = 0; x < CPL; ++x) acc[x] = 0.f;
   for (int s0 = 0; s0 < ns; s0 += kWave) {
     const int s = s0 + l;
-    float wgt = 0.f, ls = 0.f;
-    if (s < ns) {
-      const float ms = part_ml[(pr0 + int64_t(s) * rows_pad) * 2];
-      ls = part_ml[(pr0 + int64_t(s) * rows_pad) * 2 + 1];
-      wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
-    }
+    const float* ml = part_ml + (pr0 + int64_t(s) * rows_pad) * 2;
+    const float ms = ldf_or_neginf(s < ns, ml);
+    const float ls = ldf_or_zero(s < ns, ml + 1);
+    const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
     L += xor_sum<kWave>(wgt * ls);
     const int cnt = min(kWave, ns - s0);
 #pragma unroll 8
     for (int t = 0; t < cnt; ++t) {
-      const float wt = __shfl(wgt, t);
+      const float wt = __shfl(wgt, t);   // 0 for splits whose row saw no key (their O is 0)
       const float* src = part_o + (pr0 + int64_t(s0 + t) * rows_pad) * D + CPL * l;
-      if (wt != 0.f) {
 #pragma unroll
-        for (int x = 0; x < CPL; ++x) acc[x] += wt * src[x];
-      }
+      for (int x = 0; x < CPL; ++x) acc[x] += wt * src[x];
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;

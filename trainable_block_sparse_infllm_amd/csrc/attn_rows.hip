@@ -59,15 +59,15 @@ struct KVStage {
       const int p = tid + 256 * x;
       const int row = p / (D / 8), c8 = p % (D / 8);
       const int64_t key = key0 + row;
-      kr[x] = key < kv_len ? ldg16(kbase + key * D + c8 * 8) : uint4{0, 0, 0, 0};
+      kr[x] = ldg16_if(key < kv_len, kbase + key * D + c8 * 8);
     }
 #pragma unroll
     for (int x = 0; x < VPAIRS; ++x) {
       const int p = tid + 256 * x;
       const int dg = p % (D / 8), rp = p / (D / 8);
       const int64_t key = key0 + 2 * rp;
-      vr[x][0] = key < kv_len ? ldg16(vbase + key * D + dg * 8) : uint4{0, 0, 0, 0};
-      vr[x][1] = key + 1 < kv_len ? ldg16(vbase + (key + 1) * D + dg * 8) : uint4{0, 0, 0, 0};
+      vr[x][0] = ldg16_if(key < kv_len, vbase + key * D + dg * 8);
+      vr[x][1] = ldg16_if(key + 1 < kv_len, vbase + (key + 1) * D + dg * 8);
     }
   }
 
@@ -147,9 +147,8 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(
     const int h = g * G + r16 % G;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      uint4 x = {0, 0, 0, 0};
-      if (t < n_q) x = ldg16(q + ((int64_t(b) * Hq + h) * n_q + t) * D + ks * 32 + kg * 8);
-      qf[s][ks] = as_bf16x8(x);
+      const uint16_t* qrow = q + ((int64_t(b) * Hq + h) * n_q + (t < n_q ? t : 0)) * D;
+      qf[s][ks] = as_bf16x8(ldg16_if(t < n_q, qrow + ks * 32 + kg * 8));
     }
   }
   __syncthreads();

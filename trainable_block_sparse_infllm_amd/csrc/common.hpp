@@ -57,6 +57,32 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Guarded loads without branches. A guarded load reads either the real
+// location or a device-global constant holding the neutral value (zeros, -inf)
+// and uses the result unconditionally: the choice is made on the address, so a
+// run of guarded loads issues back to back instead of one round trip each (a
+// select on the loaded value would be turned back into a conditional load).
+// The constant's address goes through an empty asm, which hides what it points
+// to: otherwise the compiler folds the load of the constant and recreates the
+// value select. (The asm holds no instruction and no load.)
+static __device__ __align__(16) const uint32_t kZeroPiece[4] = {0u, 0u, 0u, 0u};
+static __device__ const float kNegInf = -INFINITY;
+static __device__ const float kZeroF = 0.f;
+
+template <typename T>
+__device__ __forceinline__ const T* opaque(const T* p) {
+  asm("" : "+v"(p));
+  return p;
+}
+
+__device__ __forceinline__ uint4 ldg16_if(bool ok, const void* p) {
+  const void* z = opaque(static_cast<const void*>(kZeroPiece));
+  return *reinterpret_cast<const uint4*>(ok ? p : z);
+}
+
+__device__ __forceinline__ float ldf_or_neginf(bool ok, const float* p) { return *(ok ? p : opaque(&kNegInf)); }
+__device__ __forceinline__ float ldf_or_zero(bool ok, const float* p) { return *(ok ? p : opaque(&kZeroF)); }
+
 typedef __attribute__((address_space(1))) void gas_void;   // global address space
 typedef __attribute__((address_space(3))) void las_void;   // LDS address space
 

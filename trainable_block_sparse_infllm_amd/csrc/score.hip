@@ -44,10 +44,8 @@ __global__ __launch_bounds__(64) void score_kernel(const uint16_t* __restrict__ 
     const int node = c / G, hh = c % G;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      uint4 v = {0, 0, 0, 0};
-      if (node < n_q)
-        v = ldg16(q + ((int64_t(b) * Hq + g * G + hh) * n_q + node) * D + ks * 32 + kg * 8);
-      qf[nt][ks] = as_bf16x8(v);
+      const uint16_t* qrow = q + ((int64_t(b) * Hq + g * G + hh) * n_q + (node < n_q ? node : 0)) * D;
+      qf[nt][ks] = as_bf16x8(ldg16_if(node < n_q, qrow + ks * 32 + kg * 8));
     }
   }
 
@@ -60,11 +58,7 @@ __global__ __launch_bounds__(64) void score_kernel(const uint16_t* __restrict__ 
   for (int m = 0; m < kKpb; ++m) {
     bf16x8 af[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 v = {0, 0, 0, 0};
-      if (row_ok) v = ldg16(kb + m * D + ks * 32);
-      af[ks] = as_bf16x8(v);
-    }
+    for (int ks = 0; ks < KS; ++ks) af[ks] = as_bf16x8(ldg16_if(row_ok, kb + m * D + ks * 32));
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};

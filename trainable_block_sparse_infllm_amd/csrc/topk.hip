@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void topk_scores_kernel(const float* __restric
 #pragma unroll
   for (int r = 0; r < KPL; ++r) {
     const int64_t j = int64_t(r) * kWave + l;
-    key[r] = j < C ? ordered_key(src[j]) : 0u;
+    key[r] = ordered_key(ldf_or_neginf(j < C, src + j));   // -inf keys rank below every score
   }
   wave_topk<KPL>(key, int(C), K, idx + row * K, scratch[threadIdx.x / kWave]);
 }
@@ -150,7 +150,10 @@ __global__ __launch_bounds__(256) void topk_fused_kernel(const uint16_t* __restr
   constexpr int LDSC = KPL * kWave;
   extern __shared__ float sc[];
   __shared__ uint32_t scratch[4][2 * kWave];
+  __shared__ float s_neginf;
   const int w = threadIdx.x / kWave;
+  if (threadIdx.x == 0) s_neginf = -INFINITY;
+  __syncthreads();
   const int l = lane_id();
   const int r16 = l % 16, kg = l / 16;
   const int TQ = 16 * NT / G;
@@ -172,10 +175,8 @@ __global__ __launch_bounds__(256) void topk_fused_kernel(const uint16_t* __restr
       const int t = c / G, hh = c % G;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        uint4 v = {0, 0, 0, 0};
-        if (t < ntok)
-          v = ldg16(q + ((int64_t(b) * Hq + g * G + hh) * n_q + tok0 + t) * D + ks * 32 + kg * 8);
-        qf[nt][ks] = as_bf16x8(v);
+        const uint16_t* qrow = q + ((int64_t(b) * Hq + g * G + hh) * n_q + tok0 + (t < ntok ? t : 0)) * D;
+        qf[nt][ks] = as_bf16x8(ldg16_if(t < ntok, qrow + ks * 32 + kg * 8));
       }
     }
     const int nchunk = int((Cmax + 15) / 16);
@@ -189,11 +190,7 @@ __global__ __launch_bounds__(256) void topk_fused_kernel(const uint16_t* __restr
       for (int m = 0; m < kKpb; ++m) {
         bf16x8 af[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          uint4 v = {0, 0, 0, 0};
-          if (row_ok) v = ldg16(kb + m * D + ks * 32);
-          af[ks] = as_bf16x8(v);
-        }
+        for (int ks = 0; ks < KS; ++ks) af[ks] = as_bf16x8(ldg16_if(row_ok, kb + m * D + ks * 32));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -237,7 +234,7 @@ __global__ __launch_bounds__(256) void topk_fused_kernel(const uint16_t* __restr
 #pragma unroll
     for (int r = 0; r < KPL; ++r) {
       const int j = r * kWave + l;
-      key[r] = (C > K && j < C) ? ordered_key(sc[t * LDSC + j]) : 0u;
+      key[r] = ordered_key(*((C > K && j < C) ? &sc[t * LDSC + j] : opaque(&s_neginf)));
     }
     wave_topk<KPL>(key, int(C), K, idx + ((int64_t(bg) * n_q + tok0 + t) * K), scratch[w]);
   }
