@@ -124,7 +124,9 @@ INFLLMV2_API int infllmv2_sparse_attn_prefill(const infllmv2_cfg* cfg, const voi
                                  const void* k, const void* v, int64_t kv_cap, int64_t kv_len,
                                  const int32_t* idx, void* out, float* lse, void* stream);
 
-/* Workspace (bytes, device memory) that infllmv2_sparse_attn_decode needs. */
+/* Workspace (bytes, device memory) that infllmv2_sparse_attn_decode needs.
+ * No initial contents are required; calls that share a workspace must not
+ * overlap in time. */
 INFLLMV2_API size_t infllmv2_decode_workspace_bytes(const infllmv2_cfg* cfg, int32_t n_q, int64_t kv_len);
 
 /* Sparse attention of n_q new tokens against a KV cache, split across the

@@ -250,3 +250,23 @@ def test_pool_incremental_blocks_match():
     lib.infllmv2_pool_kernels(cfg, k, d["kv_cap"], 3000, 15, kbar)   # extend to 46 blocks
     torch.cuda.synchronize()
     assert np.array_equal(host_u16(kbar)[:, :, :46], kbar_o[:, :, :46])
+
+
+def test_decode_workspace_reused_across_shapes():
+    """Consecutive decode calls share one workspace (arrival counters must come back to zero)."""
+    ws = ops.Workspace(torch.device("cuda"))
+    for i, (B, Hkv, L) in enumerate([(1, 2, 3000), (2, 4, 5000), (1, 2, 3000), (3, 4, 4100)]):
+        w = D0.scaled(name=f"ws{i}", batch=B, n_q_heads=4 * Hkv, n_kv_heads=Hkv, seq_len=L, top_k=8, n_plant=8)
+        note(f"workspace reuse call {i}: B{B} Hkv{Hkv} kv_len{L}")
+        d = synth.generate(w, seed=20 + i)
+        kbar_o, _, _ = open_gaps(d, orc)
+        ref = orc.sparse_forward(d["q"], d["k"], d["v"], kv_len=L, q_pos0=L - 1, n_kv_heads=Hkv, top_k=8,
+                                 dense_threshold=w.dense_threshold, kbar=kbar_o)
+        cfg = cfg_of(w)
+        k = dev_bf16(d["k"])
+        kbar = ops.pool_kernels(cfg, k, d["kv_cap"], L)
+        res = ops.decode(cfg, dev_bf16(d["q"]), k, dev_bf16(d["v"]), kbar, L, ws=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(res["idx"].cpu().numpy(), ref["idx"])
+        hr = ref["head_rows"]
+        assert_close_rows(host_f64(res["out"])[hr[:, 0], hr[:, 1], hr[:, 2]], ref["out"], f"call {i}")

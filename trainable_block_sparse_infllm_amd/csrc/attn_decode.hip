@@ -27,7 +27,7 @@ namespace infllmv2 {
 namespace {
 
 struct DecodeLayout {
-  int64_t bgs, max_e, nsplit, rows_pad;
+  int64_t bgs, max_e, nsplit, rows;
   size_t off_union, off_mask, off_count, off_ml, off_o, total;
 };
 
@@ -45,7 +45,7 @@ DecodeLayout decode_layout(const Dims& d, int n_q, int64_t kv_len) {
   }
   const int64_t sb = std::max<int64_t>(1, (L.bgs * L.max_e + 4095) / 4096);
   L.nsplit = (L.max_e + sb - 1) / sb;
-  L.rows_pad = (int64_t(n_q) * d.G + 15) / 16 * 16;
+  L.rows = int64_t(n_q) * d.G;
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   size_t off = 0;
   L.off_union = off;
@@ -55,9 +55,9 @@ DecodeLayout decode_layout(const Dims& d, int n_q, int64_t kv_len) {
   L.off_count = off;
   off = al(off + size_t(L.bgs) * 4);
   L.off_ml = off;
-  off = al(off + size_t(L.bgs * L.nsplit * L.rows_pad) * 2 * 4);
+  off = al(off + size_t(L.bgs * L.nsplit * L.rows) * 2 * 4);
   L.off_o = off;
-  off = al(off + size_t(L.bgs * L.nsplit * L.rows_pad) * d.D * 4);
+  off = al(off + size_t(L.bgs * L.nsplit * L.rows) * d.D * 4);
   L.total = off;
   return L;
 }
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(64, NSTD == 1 ? 2 : 1) void decode_split_kernel(
     const int32_t* __restrict__ u_blk, const uint64_t* __restrict__ u_mask,
     const int32_t* __restrict__ u_count, float* __restrict__ part_ml, float* __restrict__ part_o,
     int Hq, int Hkv, int G, int n_q, int64_t kv_cap,
-    int64_t kv_len, int K, int dense_thr, int is_tree, int sb, int nsplit, int max_e, int rows_pad,
+    int64_t kv_len, int K, int dense_thr, int is_tree, int sb, int nsplit, int max_e, int rows,
     float scale_log2) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
@@ -343,8 +343,8 @@ __global__ __launch_bounds__(64, NSTD == 1 ? 2 : 1) void decode_split_kernel(
 #pragma unroll
   for (int s = 0; s < NSTD; ++s) {
     const int row = row0 + s * 16 + r16;
-    if (row >= rows_pad) continue;
-    const int64_t pr = (int64_t(bg) * nsplit + split) * rows_pad + row;
+    if (row >= rows) continue;
+    const int64_t pr = (int64_t(bg) * nsplit + split) * rows + row;
     if (kg == 0) {
       part_ml[pr * 2 + 0] = m_run[s];
       part_ml[pr * 2 + 1] = l_run[s];
@@ -358,14 +358,14 @@ __global__ __launch_bounds__(64, NSTD == 1 ? 2 : 1) void decode_split_kernel(
 }
 
 // ------------------------------------------------------------------ combine
-// One wavefront per output row (b, h, i): the split maxima and sums are read
-// with lanes over splits (one round trip), then each lane accumulates its D/64
-// columns over the splits with independent loads, weights broadcast by shuffle.
+// One wavefront per output row (b, h, i), in two round trips: lanes over splits
+// read every split's (m, l), then every lane issues the loads of its D/64
+// columns for all splits of the chunk before using any of them.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     const float* __restrict__ part_ml, const float* __restrict__ part_o,
     const int32_t* __restrict__ u_count, uint16_t* __restrict__ out, float* __restrict__ lse,
-    int Hq, int Hkv, int G, int n_q, int nsplit, int sb, int n_e1, int rows_pad, int64_t nrows) {
+    int Hq, int Hkv, int G, int n_q, int nsplit, int sb, int n_e1, int rows, int64_t nrows) {
   constexpr int CPL = D / kWave;
   const int l = lane_id();
   const int64_t rid = int64_t(blockIdx.x) * 4 + threadIdx.x / kWave;   // (b, h, i)
@@ -378,31 +378,37 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   const int row = i * G + h % G;
   const int n_e = n_q == 1 ? n_e1 : u_count[bg];
   const int ns = min(nsplit, (n_e + sb - 1) / sb);
-  const int64_t pr0 = int64_t(bg) * nsplit * rows_pad + row;   // split s at pr0 + s * rows_pad
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < ns; s0 += kWave) {
-    const int s = s0 + l;
-    const float ms = ldf_or_neginf(s < ns, part_ml + (pr0 + int64_t(s) * rows_pad) * 2);
-    M = fmaxf(M, xor_max<kWave>(ms));
-  }
-  float L = 0.f;
+  const int64_t pr0 = int64_t(bg) * nsplit * rows + row;   // split s at pr0 + s * rows
+  float M = -INFINITY, L = 0.f;
   float acc[CPL];
 #pragma unroll
   for (int x = 0; x < CPL; ++x) acc[x] = 0.f;
   for (int s0 = 0; s0 < ns; s0 += kWave) {
     const int s = s0 + l;
-    const float* ml = part_ml + (pr0 + int64_t(s) * rows_pad) * 2;
+    const float* ml = part_ml + (pr0 + int64_t(s) * rows) * 2;
     const float ms = ldf_or_neginf(s < ns, ml);
     const float ls = ldf_or_zero(s < ns, ml + 1);
-    const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
-    L += xor_sum<kWave>(wgt * ls);
-    const int cnt = min(kWave, ns - s0);
-#pragma unroll 8
-    for (int t = 0; t < cnt; ++t) {
-      const float wt = __shfl(wgt, t);   // 0 for splits whose row saw no key (their O is 0)
-      const float* src = part_o + (pr0 + int64_t(s0 + t) * rows_pad) * D + CPL * l;
+    float o[kWave][CPL];                       // this lane's columns of every split in the chunk
 #pragma unroll
-      for (int x = 0; x < CPL; ++x) acc[x] += wt * src[x];
+    for (int t = 0; t < kWave; ++t) {
+      const bool ok = s0 + t < ns;
+      const float* src = part_o + (pr0 + int64_t(s0 + t) * rows) * D + CPL * l;
+#pragma unroll
+      for (int x = 0; x < CPL; ++x) o[t][x] = ldf_or_zero(ok, src + x);
+    }
+    __builtin_amdgcn_sched_barrier(0);         // all loads of the chunk are in flight
+    const float m_new = fmaxf(M, xor_max<kWave>(ms));
+    const float a = M == -INFINITY ? 0.f : exp2f(M - m_new);
+    const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - m_new);   // 0 where the row saw no key
+    L = L * a + xor_sum<kWave>(wgt * ls);
+#pragma unroll
+    for (int x = 0; x < CPL; ++x) acc[x] *= a;
+    M = m_new;
+#pragma unroll
+    for (int t = 0; t < kWave; ++t) {
+      const float wt = __shfl(wgt, t);
+#pragma unroll
+      for (int x = 0; x < CPL; ++x) acc[x] += wt * o[t][x];
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -453,7 +459,7 @@ hipError_t launch_decode(const Dims& d, const uint16_t* q, int n_q, const uint16
                                                     u_count, part_ml, part_o, d.Hq, d.Hkv, d.G,  \
                                                     n_q, kv_cap, kv_len, d.K, d.dense_thr,       \
                                                     is_tree, sb, int(L.nsplit), int(L.max_e),    \
-                                                    int(L.rows_pad), sl2);                       \
+                                                    int(L.rows), sl2);                           \
   } else
   SPLIT_CASE(128, 1) SPLIT_CASE(128, 2) SPLIT_CASE(64, 1) SPLIT_CASE(64, 2)
   { return hipErrorInvalidValue; }
@@ -465,11 +471,11 @@ hipError_t launch_decode(const Dims& d, const uint16_t* q, int n_q, const uint16
   if (d.D == 128)
     decode_combine_kernel<128><<<cgrid, 256, 0, s>>>(part_ml, part_o, u_count, out, lse, d.Hq,
                                                      d.Hkv, d.G, n_q, int(L.nsplit), sb, n_e1,
-                                                     int(L.rows_pad), nrows);
+                                                     int(L.rows), nrows);
   else
     decode_combine_kernel<64><<<cgrid, 256, 0, s>>>(part_ml, part_o, u_count, out, lse, d.Hq,
                                                     d.Hkv, d.G, n_q, int(L.nsplit), sb, n_e1,
-                                                    int(L.rows_pad), nrows);
+                                                    int(L.rows), nrows);
   return hipGetLastError();
 }
 

@@ -65,23 +65,38 @@ __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast
 // The constant's address goes through an empty asm, which hides what it points
 // to: otherwise the compiler folds the load of the constant and recreates the
 // value select. (The asm holds no instruction and no load.)
-static __device__ __align__(16) const uint32_t kZeroPiece[4] = {0u, 0u, 0u, 0u};
-static __device__ const float kNegInf = -INFINITY;
-static __device__ const float kZeroF = 0.f;
+// (Declared without const so they live in the global address space, like the
+// tensors they stand in for: the load then stays a global load, not a flat one.)
+static __device__ __align__(16) uint32_t kZeroPiece[4] = {0u, 0u, 0u, 0u};
+static __device__ float kNegInf = -INFINITY;
+static __device__ float kZeroF = 0.f;
 
-template <typename T>
-__device__ __forceinline__ const T* opaque(const T* p) {
-  asm("" : "+v"(p));
-  return p;
+typedef __attribute__((address_space(1))) const uint32_t g_u32;   // global-space views
+typedef __attribute__((address_space(1))) const float g_float;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4_t g_u32x4;
+
+__device__ __forceinline__ uint64_t opaque_addr(const void* p) {
+  uint64_t a = reinterpret_cast<uint64_t>(p);
+  asm("" : "+v"(a));
+  return a;
 }
 
 __device__ __forceinline__ uint4 ldg16_if(bool ok, const void* p) {
-  const void* z = opaque(static_cast<const void*>(kZeroPiece));
-  return *reinterpret_cast<const uint4*>(ok ? p : z);
+  const g_u32x4* z = (const g_u32x4*)opaque_addr(kZeroPiece);
+  const u32x4_t v = *(ok ? (const g_u32x4*)p : z);
+  return uint4{v.x, v.y, v.z, v.w};
 }
 
-__device__ __forceinline__ float ldf_or_neginf(bool ok, const float* p) { return *(ok ? p : opaque(&kNegInf)); }
-__device__ __forceinline__ float ldf_or_zero(bool ok, const float* p) { return *(ok ? p : opaque(&kZeroF)); }
+__device__ __forceinline__ float ldf_or_neginf(bool ok, const float* p) {
+  const g_float* z = (const g_float*)opaque_addr(&kNegInf);
+  return *(ok ? (const g_float*)p : z);
+}
+
+__device__ __forceinline__ float ldf_or_zero(bool ok, const float* p) {
+  const g_float* z = (const g_float*)opaque_addr(&kZeroF);
+  return *(ok ? (const g_float*)p : z);
+}
 
 typedef __attribute__((address_space(1))) void gas_void;   // global address space
 typedef __attribute__((address_space(3))) void las_void;   // LDS address space

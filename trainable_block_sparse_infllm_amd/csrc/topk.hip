@@ -125,12 +125,16 @@ __global__ __launch_bounds__(256) void topk_scores_kernel(const float* __restric
   int64_t C = pos / kBlock;
   if (C > nblk) C = nblk;
   const float* src = scores + row * nblk;
-  uint32_t key[KPL];
+  float val[KPL];
 #pragma unroll
   for (int r = 0; r < KPL; ++r) {
     const int64_t j = int64_t(r) * kWave + l;
-    key[r] = ordered_key(ldf_or_neginf(j < C, src + j));   // -inf keys rank below every score
+    val[r] = ldf_or_neginf(j < C, src + j);      // -inf keys rank below every score
   }
+  __builtin_amdgcn_sched_barrier(0);             // all loads issue before the first use
+  uint32_t key[KPL];
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) key[r] = ordered_key(val[r]);
   wave_topk<KPL>(key, int(C), K, idx + row * K, scratch[threadIdx.x / kWave]);
 }
 
@@ -234,7 +238,8 @@ __global__ __launch_bounds__(256) void topk_fused_kernel(const uint16_t* __restr
 #pragma unroll
     for (int r = 0; r < KPL; ++r) {
       const int j = r * kWave + l;
-      key[r] = ordered_key(*((C > K && j < C) ? &sc[t * LDSC + j] : opaque(&s_neginf)));
+      const float* src = (C > K && j < C) ? &sc[t * LDSC + j] : &s_neginf;
+      key[r] = ordered_key(*src);
     }
     wave_topk<KPL>(key, int(C), K, idx + ((int64_t(bg) * n_q + tok0 + t) * K), scratch[w]);
   }
