@@ -35,6 +35,12 @@ PREFILL_CASES = {
                          n_plant=2),
     "g16_d64": P0.scaled(name="p_g16", n_q_heads=16, n_kv_heads=1, head_dim=64, seq_len=300, top_k=2,
                          dense_threshold=0, n_plant=1),
+    "g1_d128": P0.scaled(name="p_g1_128", n_q_heads=2, n_kv_heads=2, seq_len=700, top_k=3,
+                         dense_threshold=200, n_plant=2),
+    "g2_d128_b2": P0.scaled(name="p_g2_128", batch=2, n_q_heads=4, n_kv_heads=2, seq_len=900, top_k=5,
+                            dense_threshold=0, n_plant=3),
+    "g16_d128": P0.scaled(name="p_g16_128", n_q_heads=16, n_kv_heads=1, seq_len=300, top_k=2,
+                          dense_threshold=0, n_plant=1),
     "short_no_candidates": P0.scaled(name="p_short", n_q_heads=8, n_kv_heads=2, seq_len=50, top_k=4,
                                      dense_threshold=0, n_plant=0),
     "tiny_prefill_2k": W["tiny_prefill_2k"],
@@ -112,6 +118,27 @@ def test_prefill_attention_with_oracle_indices():
     torch.cuda.synchronize()
     hr = ref["head_rows"]
     assert_close_rows(host_f64(out)[hr[:, 0], hr[:, 1], hr[:, 2]], ref["out"], "prefill attention")
+
+
+@pytest.mark.parametrize("n_q,kv_len,thr", [(300, 1500, 1300), (64, 2000, 0), (37, 1111, 0)])
+def test_prefill_attention_chunk_with_oracle_indices(n_q, kv_len, thr):
+    """A chunk of n_q queries at the end of a longer context (positions
+    kv_len - n_q .. kv_len - 1), block indices from the oracle."""
+    w = PREFILL_CASES["g4_d128_ragged_thr"].scaled(name="p_chunk", seq_len=kv_len, dense_threshold=thr)
+    note(f"prefill chunk n_q{n_q} kv_len{kv_len} thr{thr}")
+    d = synth.generate(w, seed=4)
+    qn = np.ascontiguousarray(d["q"][:, :, kv_len - n_q:])
+    ref = orc.sparse_forward(qn, d["k"], d["v"], kv_len=kv_len, q_pos0=kv_len - n_q, n_kv_heads=w.n_kv_heads,
+                             top_k=w.top_k, dense_threshold=thr)
+    cfg = cfg_of(w)
+    out = torch.empty((w.batch, w.n_q_heads, n_q, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.batch, w.n_q_heads, n_q), dtype=torch.float32, device="cuda")
+    lib.infllmv2_sparse_attn_prefill(cfg, dev_bf16(qn), n_q, dev_bf16(d["k"]), dev_bf16(d["v"]),
+                                     d["kv_cap"], kv_len, dev_i32(ref["idx"]), out, lse)
+    torch.cuda.synchronize()
+    hr = ref["head_rows"]
+    assert_close_rows(host_f64(out)[hr[:, 0], hr[:, 1], hr[:, 2]], ref["out"], "prefill chunk")
+    assert np.abs(host_f64(lse)[hr[:, 0], hr[:, 1], hr[:, 2]] - ref["lse"]).max() <= LSE_ABS
 
 
 def test_prefill_32k_full_size_sampled_rows():
@@ -210,7 +237,8 @@ def test_tree_128k_full_size():
 
 # ---------------------------------------------------------------------------- dense
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("dims", [(8, 2, 128, 700, 700), (4, 1, 64, 333, 1000), (16, 2, 64, 65, 4000)])
+@pytest.mark.parametrize("dims", [(8, 2, 128, 700, 700), (4, 1, 64, 333, 1000), (16, 2, 64, 65, 4000),
+                                  (8, 2, 128, 150, 1100), (4, 4, 128, 97, 513), (16, 1, 128, 40, 300)])
 def test_dense_attention(causal, dims):
     Hq, Hkv, D, n_q, kv_len = dims
     w = P0.scaled(name="dense", n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, seq_len=kv_len, n_plant=0)

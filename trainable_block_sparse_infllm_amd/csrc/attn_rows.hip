@@ -356,6 +356,8 @@ static hipError_t launch_rows_t(const Dims& d, int mode, const uint16_t* q, int 
 hipError_t launch_attn_rows(const Dims& d, int mode, const uint16_t* q, int n_q, const uint16_t* k,
                             const uint16_t* v, int64_t kv_cap, int64_t kv_len, const int32_t* idx,
                             uint16_t* out, float* lse, hipStream_t s) {
+  if (prefill128_stages(d, mode, kv_len) > 0)
+    return launch_prefill128(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s);
 #define ROWS_CASE(DD, GG, NN)                                                                    \
   if (d.D == DD && d.G == GG)                                                                    \
     return launch_rows_t<DD, GG, NN>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s);

@@ -29,6 +29,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
 }
 
+// Two floats -> packed bf16 pair (lo in the low half) with the hardware
+// round-to-nearest-even conversion (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const bf16x2_t b = __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t);
+  uint32_t u;
+  __builtin_memcpy(&u, &b, sizeof u);
+  return u;
+}
+
 // Exact double (a mean of bf16 values) -> bf16 bits, round to nearest even.
 __device__ __forceinline__ uint16_t d2bf(double x) {
   uint64_t u = __double_as_longlong(x);
@@ -136,6 +147,32 @@ __device__ __forceinline__ int wave_min_i32(int v) {
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Reductions over the four 16-lane rows of a wavefront (lanes l, l^16, l^32,
+// l^48), with the gfx950 row-swap instructions instead of LDS-routed shuffles:
+// permlane16_swap(x, x) leaves rows (0,0,2,2) in one result and (1,1,3,3) in
+// the other, permlane32_swap(x, x) rows (0,1,0,1) and (2,3,2,3).
+__device__ __forceinline__ float rows4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Lane 0's value of a 64-bit quantity, as a wave-uniform (scalar) value.
+// (readfirstlane works on 32-bit ints; each half is zero-extended.)
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(x))));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(x >> 32))));
+  return uint64_t(lo) | (uint64_t(hi) << 32);
+}
 
 __device__ __forceinline__ uint32_t popc64(uint64_t x) { return __popcll(x); }
 

@@ -29,6 +29,14 @@ hipError_t launch_attn_rows(const Dims& d, int mode, const uint16_t* q, int n_q,
                             const uint16_t* v, int64_t kv_cap, int64_t kv_len, const int32_t* idx,
                             uint16_t* out, float* lse, hipStream_t s);
 
+// head_dim 128 prefill / dense attention over a per-tile block union staged
+// through an LDS ring. prefill128_stages() returns the ring depth for the
+// shape, or 0 if it does not fit (then launch_attn_rows is used).
+int prefill128_stages(const Dims& d, int mode, int64_t kv_len);
+hipError_t launch_prefill128(const Dims& d, int mode, const uint16_t* q, int n_q,
+                             const uint16_t* k, const uint16_t* v, int64_t kv_cap, int64_t kv_len,
+                             const int32_t* idx, uint16_t* out, float* lse, hipStream_t s);
+
 size_t decode_workspace_bytes(const Dims& d, int n_q, int64_t kv_len);
 
 hipError_t launch_decode(const Dims& d, const uint16_t* q, int n_q, const uint16_t* k,
