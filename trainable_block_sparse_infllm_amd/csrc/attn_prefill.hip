@@ -10,33 +10,31 @@
 //           p + 1 < dense_threshold;
 //   mode 1 (dense causal): keys 0..p;      mode 2 (dense): keys 0..kv_len-1.
 //
-// Work layout. A workgroup (4 wavefronts) owns TQ <= 64 consecutive tokens of
-// one (b, g); a wavefront owns NST sub-tiles of 16 MFMA rows (16/G tokens x G
-// heads: one token's heads share a key set). On the 32K workload 64
-// consecutive tokens need ~45 distinct blocks between them while each needs
-// 17, so the tile walks that union once and reuses every staged block for all
-// of its tokens that need it:
+// Work layout. A workgroup of NW wavefronts owns TQ <= 64 consecutive tokens
+// of one (b, g); each wavefront owns one sub-tile of 32 MFMA rows (32/G tokens
+// x G heads; one token's heads share a key set). The products run on the
+// 32x32x16 bf16 MFMA, which on gfx950 sustains twice the rate of the 16x16x32
+// form. On the 32K workload 64 consecutive tokens need ~45 distinct blocks
+// between them while each needs 17, so the tile walks that union once and
+// every staged block serves all of the tile's tokens that need it:
 //
 //   1. union: the tile's blocks are listed in ascending order, each with a
 //      64-bit mask of the tile's tokens that attend it. Own blocks and dense
 //      prefixes are ranges, so their mask bits are computed; only selected
 //      blocks go through an LDS bitmap. A tile whose tokens are all dense
-//      needs no list at all: block u is entry u;
+//      needs no list: block u is entry u;
 //   2. a ring of NSTAGE LDS stages holds K and V of upcoming blocks, filled
 //      straight from HBM (global_load_lds, no staging registers), so
 //      NSTAGE - 1 blocks are in flight while one is computed; one barrier per
 //      block;
-//   3. per block, each wavefront runs its sub-tiles that hold a token needing
-//      it: S^T = K Q^T (MFMA 16x16x32 bf16; A = K fragments from LDS, B = Q
-//      in registers), online softmax in the exp2 domain with the rows of other
-//      tokens masked, O^T += V^T P^T (A = V^T fragments from the transpose
-//      read ds_read_b64_tr_b16 of the row-major V tile, B = P^T taken from
-//      the S^T accumulators).
+//   3. per block, a wavefront whose tokens need it computes S^T = K Q^T
+//      (A = K fragments from LDS, B = Q in registers), the masked online
+//      softmax in the exp2 domain, and O^T += V^T P^T (A = V^T fragments from
+//      the transpose read ds_read_b64_tr_b16 of the row-major V tile, B = P^T
+//      taken from the S^T accumulators without data movement).
 //
 // LDS tiles are row-major 64 x 128 bf16 whose 16-byte pieces are XOR-swizzled
-// per row by swz(r) = ((r & 7) << 1) | ((r >> 3) & 1): the 16 rows of a K
-// fragment read land in 16 distinct piece slots, and the 4 rows x 2 pieces of
-// each 16-lane transpose read in 8.
+// per row by swz(r) = ((r & 7) << 1) | ((r >> 3) & 1).
 #include <algorithm>
 
 #include "common.hpp"
@@ -50,53 +48,71 @@ constexpr int kD = 128;
 constexpr int kTileBytes = kBlock * kD * 2;   // one K or V tile
 constexpr int kStageBytes = 2 * kTileBytes;   // K then V
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) char lds_char;
 
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
-// Keys key0 .. key0+63 of K and V -> one LDS stage (8 direct loads per
-// thread). Chunk c (1 KB, rows 4c..4c+3) is loaded by wavefront c % 4; lane
-// l's 16 bytes land in slot l % 16 of row 4c + l / 16, so it fetches the global
-// piece stored in that slot. Rows past kv_len repeat row kv_len - 1 (finite
-// data; their scores are masked).
+// Shape of one instance: TPS tokens per wavefront (32 MFMA rows), NW
+// wavefronts, TQ tokens per workgroup, LPS direct loads per thread per stage.
+template <int G>
+struct PrefillShape {
+  static constexpr int TPS = 32 / G;
+  static constexpr int NW = TPS >= 8 ? 64 / TPS : 8;
+  static constexpr int TQ = NW * TPS;
+  static constexpr int NT = 64 * NW;
+  static constexpr int LPS = 32 / NW;
+  static_assert(TQ <= 64, "token masks are 64-bit");
+};
+
+// Keys key0 .. key0+63 of K and V -> one LDS stage. The stage is 32 chunks of
+// 1 KB (chunk c < 16: K rows 4c..4c+3, else V rows 4(c-16)..); wavefront w
+// loads chunks w, w + NW, ... Lane l's 16 bytes land in slot l % 16 of row
+// 4c + l / 16, so it fetches the global piece stored in that slot. Rows past
+// kv_len repeat row kv_len - 1 (finite data; their scores are masked).
+template <int NW>
 __device__ __forceinline__ void issue_stage(char* stage, const uint16_t* kbase,
                                            const uint16_t* vbase, int64_t key0, int64_t kv_len,
                                            int w, int l) {
+  constexpr int LPS = 32 / NW;
   if (key0 + kBlock <= kv_len) {
-    const uint16_t* kb = kbase + key0 * kD;
-    const uint16_t* vb = vbase + key0 * kD;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int c = x * 4 + w;
-      const int row = 4 * c + l / 16;
-      const int off = row * kD + ((l % 16) ^ swz(row)) * 8;
-      load_lds16(kb + off, stage + c * 1024);
-      load_lds16(vb + off, stage + kTileBytes + c * 1024);
+    for (int x = 0; x < LPS; ++x) {
+      const int c = x * NW + w;
+      const int row = 4 * (c % 16) + l / 16;
+      const uint16_t* src = (c < 16 ? kbase : vbase) + key0 * kD;
+      load_lds16(src + row * kD + ((l % 16) ^ swz(row)) * 8, stage + c * 1024);
     }
   } else {
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int c = x * 4 + w;
-      const int row = 4 * c + l / 16;
+    for (int x = 0; x < LPS; ++x) {
+      const int c = x * NW + w;
+      const int row = 4 * (c % 16) + l / 16;
       const int64_t key = min(key0 + row, kv_len - 1);
-      const int64_t off = key * kD + ((l % 16) ^ swz(row)) * 8;
-      load_lds16(kbase + off, stage + c * 1024);
-      load_lds16(vbase + off, stage + kTileBytes + c * 1024);
+      const uint16_t* src = c < 16 ? kbase : vbase;
+      load_lds16(src + key * kD + ((l % 16) ^ swz(row)) * 8, stage + c * 1024);
     }
   }
 }
 
-// s_waitcnt vmcnt(8 * stages): stages complete in issue order, so an entry has
-// landed once only the stages issued after it (8 loads each) are pending.
+// s_waitcnt vmcnt(n), n = LPS * stages: stages complete in issue order, so an
+// entry has landed once only the stages issued after it are pending.
+template <int LPS>
 __device__ __forceinline__ void wait_stages_pending(int stages) {
+  // vmcnt field: bits 3:0 and 15:14; expcnt and lgkmcnt left at their maximum
+#define INFLLMV2_VMCNT(n) (0x0F70 | ((n) & 15) | ((((n) >> 4) & 3) << 14))
   switch (stages) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;                   // vmcnt(0)
-    case 1: __builtin_amdgcn_s_waitcnt(0x0F70 | 8); break;               // vmcnt(8)
-    case 2: __builtin_amdgcn_s_waitcnt(0x0F70 | (1 << 14)); break;       // vmcnt(16)
-    default: __builtin_amdgcn_s_waitcnt(0x0F70 | 8 | (1 << 14)); break;  // vmcnt(24)
+    case 0: __builtin_amdgcn_s_waitcnt(INFLLMV2_VMCNT(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(INFLLMV2_VMCNT(LPS)); break;
+    default: __builtin_amdgcn_s_waitcnt(INFLLMV2_VMCNT(2 * LPS)); break;
   }
+#undef INFLLMV2_VMCNT
 }
 
 // Bits lo .. hi-1 of a token mask, clamped to tokens 0 .. n-1 (n <= 64).
@@ -108,8 +124,6 @@ __device__ __forceinline__ uint64_t range_bits(int64_t lo, int64_t hi, int n) {
   const uint64_t ones = len >= 64 ? ~0ull : ((1ull << len) - 1ull);
   return ones << int(lo);
 }
-
-}  // namespace
 
 // LDS reads inside the ring loop go through these helpers: the __restrict__
 // parameter gives each inlined read an alias scope, which tells the compiler
@@ -126,7 +140,7 @@ __device__ __forceinline__ bf16x8 lds_read_k(const char* __restrict__ tile, int 
   return as_bf16x8(*reinterpret_cast<const uint4*>(tile + off));
 }
 
-// V^T fragment: two transpose reads (keys +0 and +16 of the fragment's row).
+// V^T fragment: two transpose reads (the key groups q = 0 and q = 1).
 __device__ __forceinline__ bf16x8 lds_read_vt(const lds_char* __restrict__ tile, int off0, int off1) {
   v4i16 h[2];
   h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + off0));
@@ -145,19 +159,31 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int G, int NST>
-__global__ __launch_bounds__(256) void prefill_attn_kernel(
+// Max / sum over lanes l and l ^ 32 (the two halves of a 32-row MFMA column).
+__device__ __forceinline__ float halves_max(float x) {
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+}  // namespace
+
+template <int G>
+__global__ __launch_bounds__(PrefillShape<G>::NT) void prefill_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ out, float* __restrict__ lse, int Hq,
     int Hkv, int n_q, int64_t kv_cap, int64_t kv_len, int K, int dense_thr, int mode,
     float scale_log2, int ntile, int umax, int nstage) {
-  constexpr int KS = kD / 32;          // k-steps over D for S
-  constexpr int DT = kD / 16;          // 16-wide d tiles of O
-  constexpr int TPS = 16 / G;          // tokens per sub-tile
-  constexpr int TPW = NST * TPS;       // tokens per wavefront
-  constexpr int TQ = 4 * TPW;          // tokens per workgroup
-  static_assert(TQ <= 64, "token masks are 64-bit");
-  constexpr float kRescale = 8.f;      // log2 headroom before the running max is moved
+  using Sh = PrefillShape<G>;
+  constexpr int TPS = Sh::TPS, NW = Sh::NW, TQ = Sh::TQ, NT = Sh::NT, LPS = Sh::LPS;
+  constexpr int WPT = (256 + NT - 1) / NT;   // bitmap words per thread
+  constexpr int DS = kD / 16;                // k-steps of S^T = K Q^T
+  constexpr int DT = kD / 32;                // 32-wide d tiles of O^T
+  constexpr float kRescale = 8.f;            // log2 headroom before the running max is moved
 
   extern __shared__ __align__(16) char smem[];
   char* ring = smem;                                                            // [nstage]
@@ -165,12 +191,12 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
   int32_t* u_blk = reinterpret_cast<int32_t*>(u_mask + umax);                   // [umax]
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(u_blk + umax);                 // [256]
   int32_t* wbase = reinterpret_cast<int32_t*>(bitmap + 256);                    // [256]
-  int32_t* wtot = wbase + 256;                                                  // [4]
+  int32_t* wtot = wbase + 256;                                                  // [NW]
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int l = lane_id();
-  const int r16 = l % 16, kg = l / 16;
+  const int r32 = l % 32, hl = l / 32;        // MFMA column (row of the sub-tile), lane half
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   const int tile = item % ntile;
   const int bg = item / ntile;
@@ -187,16 +213,16 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
   const uint16_t* kbase = k + int64_t(bg) * kv_cap * kD;
   const uint16_t* vbase = v + int64_t(bg) * kv_cap * kD;
 
-  // Q fragments (B operand of S^T = K Q^T), loaded first so their latency
-  // overlaps the union construction.
-  bf16x8 qf[NST][KS];
+  // This lane's query row: token tok0 + w*TPS + r32/G, head g*G + r32%G. Its
+  // Q^T fragments (B operand, k-slots 8*hl .. 8*hl+7 of each 16-wide d step)
+  // are loaded first so their latency overlaps the union construction.
+  const int my_t = tok0 + w * TPS + r32 / G;
+  bf16x8 qf[DS];
+  {
+    const int h = g * G + r32 % G;
+    const uint16_t* qrow = q + ((int64_t(b) * Hq + h) * n_q + (my_t < n_q ? my_t : 0)) * kD;
 #pragma unroll
-  for (int s = 0; s < NST; ++s) {
-    const int t = tok0 + w * TPW + s * TPS + r16 / G;
-    const int h = g * G + r16 % G;
-    const uint16_t* qrow = q + ((int64_t(b) * Hq + h) * n_q + (t < n_q ? t : 0)) * kD;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[s][ks] = as_bf16x8(ldg16_if(t < n_q, qrow + ks * 32 + kg * 8));
+    for (int ds = 0; ds < DS; ++ds) qf[ds] = as_bf16x8(ldg16_if(my_t < n_q, qrow + ds * 16 + hl * 8));
   }
 
   // Tokens of this tile attending block j through their own block or a dense prefix.
@@ -213,20 +239,24 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
   } else {
     const int nwords = int(own_hi / 32) + 1;    // <= 256, checked on the host
     const int64_t rlo = dend > 0 ? 0 : own_lo;  // range part: [rlo, own_hi]
-    if (tid < nwords) {
-      const int64_t w0 = int64_t(tid) * 32;
-      bitmap[tid] = uint32_t(range_bits(rlo - w0, own_hi + 1 - w0, 32));
-    }
+    for (int i = tid; i < nwords; i += NT)
+      bitmap[i] = uint32_t(range_bits(rlo - int64_t(i) * 32, own_hi + 1 - int64_t(i) * 32, 32));
     __syncthreads();
-    for (int e = tid; e < ntok * K; e += 256) {
+    for (int e = tid; e < ntok * K; e += NT) {
       const int t = e / K;
       if (t < dend) continue;
       const int j = idx[(int64_t(bg) * n_q + tok0 + t) * K + e % K];
       if (j >= 0 && j < (base + t) / kBlock) atomicOr(&bitmap[j >> 5], 1u << (j & 31));
     }
     __syncthreads();
-    // exclusive prefix of the words' popcounts, then compaction
-    const int c = tid < nwords ? __popc(bitmap[tid]) : 0;
+    // exclusive prefix of the words' popcounts (thread t owns words t*WPT ..),
+    // then each thread lists its words' blocks in order
+    int c = 0;
+#pragma unroll
+    for (int x = 0; x < WPT; ++x) {
+      const int i = tid * WPT + x;
+      if (i < nwords) c += __popc(bitmap[i]);
+    }
     int incl = c;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -235,16 +265,21 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
     }
     if (l == kWave - 1) wtot[w] = incl;
     __syncthreads();
-    int before = 0;
-    for (int x = 0; x < w; ++x) before += wtot[x];
-    U = min(wtot[0] + wtot[1] + wtot[2] + wtot[3], umax);
-    if (tid < nwords) {
-      const int ex = before + incl - c;
-      wbase[tid] = ex;
-      uint32_t bits = bitmap[tid];
-      int pos = ex;
+    int before = 0, total = 0;
+    for (int x = 0; x < NW; ++x) {
+      before += x < w ? wtot[x] : 0;
+      total += wtot[x];
+    }
+    U = min(total, umax);
+    int pos = before + incl - c;
+#pragma unroll
+    for (int x = 0; x < WPT; ++x) {
+      const int i = tid * WPT + x;
+      if (i >= nwords) break;
+      wbase[i] = pos;
+      uint32_t bits = bitmap[i];
       while (bits) {
-        const int j = tid * 32 + __ffs(bits) - 1;
+        const int j = i * 32 + __ffs(bits) - 1;
         bits &= bits - 1;
         if (pos < umax) {
           u_blk[pos] = j;
@@ -254,7 +289,7 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
       }
     }
     __syncthreads();
-    for (int e = tid; e < ntok * K; e += 256) {
+    for (int e = tid; e < ntok * K; e += NT) {
       const int t = e / K;
       if (t < dend) continue;
       const int j = idx[(int64_t(bg) * n_q + tok0 + t) * K + e % K];
@@ -272,72 +307,62 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
 
   // ---------------------------------------------------------------- ring prologue
   for (int p = 0; p < nstage - 1 && p < U; ++p)
-    issue_stage(ring + p * kStageBytes, kbase, vbase, blk_of(p) * kBlock, kv_len, w, l);
+    issue_stage<NW>(ring + p * kStageBytes, kbase, vbase, blk_of(p) * kBlock, kv_len, w, l);
 
-  f32x4 oacc[NST][DT];
-  float m_run[NST], l_run[NST];
+  f32x16 oacc[DT];
 #pragma unroll
-  for (int s = 0; s < NST; ++s) {
-    m_run[s] = -INFINITY;
-    l_run[s] = 0.f;
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[s][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const int64_t row_p = base + w * TPS + r32 / G;      // this lane's row position
+  const int64_t p_first = base + w * TPS;              // the wavefront's first token
+
+  // Lane parts of the fragment offsets. K fragment (kt, ds): row 32*kt + r32,
+  // piece 2*ds + hl; swz(row) = swz(r32), so the offset is
+  // 8192*kt + (k_lane ^ (ds << 5)). V^T fragment (dt, ks), group q: lane k of
+  // each 16-lane group reads V[16*ks + 8*q + 4*hl + k/4][32*dt + 16*((l/16)%2) + 4*(k%4)];
+  // the row's swizzle depends on (q, lane) only, so the offset is
+  // 4096*ks + (v_lane[q] ^ (dt << 6)).
+  const int k_lane = r32 * (kD * 2) + ((hl ^ swz(r32)) << 4);
+  int v_lane[2];
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq) {
+    const int j = l % 16;
+    const int row = 8 * qq + 4 * hl + j / 4;
+    const int piece = 2 * ((l / 16) % 2) + (j % 4) / 2;
+    v_lane[qq] = row * (kD * 2) + ((piece ^ swz(row)) << 4) + 8 * (j & 1);
   }
-  // position of this lane's row in sub-tile s: base + w*TPW + s*TPS + r16/G
-  const int64_t row_p0 = base + w * TPW + r16 / G;
-
-  // lane parts of the fragment offsets (see the reads in the loop)
-  const int k_lane = r16 * (kD * 2) + ((kg ^ swz(r16)) << 4);
-  const int v_row = 4 * kg + r16 / 4;
-  const int v_lane = v_row * (kD * 2) + ((((r16 % 4) >> 1) ^ swz(v_row)) << 4) + 8 * (r16 & 1);
 
   // ---------------------------------------------------------------- 2/3. ring + compute
   int cur = 0;                                    // ring slot of entry u
   int nxt = nstage - 1;                           // ring slot of entry u + nstage - 1
   for (int u = 0; u < U; ++u) {
-    wait_stages_pending(min(nstage - 2, U - 1 - u));
+    wait_stages_pending<LPS>(min(nstage - 2, U - 1 - u));
     wait_lds();
     ring_barrier();                               // entry u landed for every wave; slot nxt is free
     if (u + nstage - 1 < U)
-      issue_stage(ring + nxt * kStageBytes, kbase, vbase, blk_of(u + nstage - 1) * kBlock, kv_len,
-                  w, l);
+      issue_stage<NW>(ring + nxt * kStageBytes, kbase, vbase, blk_of(u + nstage - 1) * kBlock,
+                      kv_len, w, l);
     const char* kt_b = ring + cur * kStageBytes;
     const lds_char* vt_b = (const lds_char*)(ring + cur * kStageBytes + kTileBytes);
     cur = cur + 1 == nstage ? 0 : cur + 1;
     nxt = nxt + 1 == nstage ? 0 : nxt + 1;
     const int64_t key0 = blk_of(u) * kBlock;
-    uint64_t tmask;
-    if (tile_dense) {
-      tmask = range_mask(key0 / kBlock);
-    } else {
-      tmask = uniform_u64(lds_read(u_mask + u));
-    }
-    tmask >>= w * TPW;
-    uint32_t son = 0;                             // sub-tiles holding a token that needs the block
-#pragma unroll
-    for (int s = 0; s < NST; ++s)
-      if ((tmask >> (s * TPS)) & ((1ull << TPS) - 1ull)) son |= 1u << s;
-    if (son == 0) continue;
+    const uint64_t tmask = tile_dense ? range_mask(key0 / kBlock) : uniform_u64(lds_read(u_mask + u));
+    const uint32_t bits = uint32_t(tmask >> (w * TPS)) & uint32_t((1ull << TPS) - 1ull);
+    if (bits == 0) continue;                      // no token of this wavefront needs the block
 
-    // S^T = K Q^T, 16 keys at a time: K fragment (kt, ks) of lane (r16, kg)
-    // is row 16*kt + r16, piece 4*ks + kg; swz(row) = swz(r16), so its offset
-    // is 4096*kt + (k_lane ^ (ks << 6)). Each fragment serves every active
-    // sub-tile.
-    f32x4 sacc[NST][4];
+    // S^T = K Q^T: two 32-key tiles. Accumulator register r of lane l holds
+    // key 32*kt + 8*(r/4) + 4*hl + r%4 of row r32.
+    f32x16 sacc[2];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      bf16x8 kf[KS];
+    for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[ks] = lds_read_k(kt_b + kt * 4096, k_lane ^ (ks << 6));
+      for (int e = 0; e < 16; ++e) sacc[kt][e] = 0.f;
 #pragma unroll
-      for (int s = 0; s < NST; ++s) {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
-        if (son & (1u << s)) {
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) a = mfma16(kf[ks], qf[s][ks], a);
-        }
-        sacc[s][kt] = a;
-      }
+      for (int ds = 0; ds < DS; ++ds)
+        sacc[kt] = mfma32(lds_read_k(kt_b + kt * 8192, k_lane ^ (ds << 5)), qf[ds], sacc[kt]);
     }
 
     // Masked online softmax in the exp2 domain. A row whose token does not
@@ -346,111 +371,102 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(
     // key. The running max (log2 units) moves only when a row's block max
     // exceeds it by more than kRescale, so O and l are rescaled rarely;
     // exponents stay <= kRescale and the final O / l is unchanged.
-    // P^T is packed as the B operand of the PV product: key slot (kg, jj)
-    // holds key 32*k2 + 16*(jj/4) + 4*kg + jj%4.
-    bf16x8 pf[NST][2];
+    const bool row_on = (bits >> (r32 / G)) & 1u;
+    const bool causal = mode == 2 ? key0 + kBlock > kv_len : key0 + kBlock - 1 > p_first;
+    if (causal) {
+      const int64_t rel = (mode == 2 ? kv_len - 1 : row_p) - key0;   // last visible key
+      const int lim = int(rel < 63 ? rel : 63);
 #pragma unroll
-    for (int s = 0; s < NST; ++s) {
-      if (!(son & (1u << s))) continue;
-      const uint32_t bits = uint32_t(tmask >> (s * TPS)) & ((1u << TPS) - 1u);
-      const bool row_on = (bits >> (r16 / G)) & 1u;
-      const int64_t p_first = base + w * TPW + s * TPS;  // first token of the sub-tile
-      const bool causal = mode == 2 ? key0 + kBlock > kv_len : key0 + kBlock - 1 > p_first;
-      if (causal) {
-        // last visible key of this row, block-relative
-        const int64_t rel = (mode == 2 ? kv_len - 1 : row_p0 + s * TPS) - key0;
-        const int lim = int(rel < 63 ? rel : 63);
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sacc[s][kt][i] = (kt * 16 + kg * 4 + i <= lim) ? sacc[s][kt][i] : -INFINITY;
-      }
-      float mb = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mb = fmaxf(mb, sacc[s][kt][i]);
-      mb = rows4_max(row_on ? mb : -INFINITY);
-      const bool grow = mb * scale_log2 > m_run[s] + kRescale;
-      if (ballot64(grow)) {
-        const float m_new = mb * scale_log2;
-        const float alpha = grow ? exp2f(m_run[s] - m_new) : 1.f;   // 0 on a row's first block
-        if (grow) m_run[s] = m_new;
-        l_run[s] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) oacc[s][dt][i] *= alpha;
-      }
-      // exp2 argument <= kRescale; results below 2^-126 flush to zero
-      const float bias = !row_on ? -INFINITY : (m_run[s] == -INFINITY ? 0.f : -m_run[s]);
-      float ps = 0.f;
-      float pv[4][4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[s][kt][i], scale_log2, bias));
-          pv[kt][i] = e;
-          ps += e;
-        }
-      l_run[s] += rows4_sum(ps);
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        uint4 uu;
-        uu.x = cvt_pk_bf16(pv[2 * k2][0], pv[2 * k2][1]);
-        uu.y = cvt_pk_bf16(pv[2 * k2][2], pv[2 * k2][3]);
-        uu.z = cvt_pk_bf16(pv[2 * k2 + 1][0], pv[2 * k2 + 1][1]);
-        uu.w = cvt_pk_bf16(pv[2 * k2 + 1][2], pv[2 * k2 + 1][3]);
-        pf[s][k2] = as_bf16x8(uu);
-      }
+        for (int e = 0; e < 16; ++e)
+          sacc[kt][e] = (32 * kt + 8 * (e / 4) + 4 * hl + e % 4 <= lim) ? sacc[kt][e] : -INFINITY;
     }
+    float mb = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mb = fmaxf(mb, sacc[kt][e]);
+    mb = halves_max(row_on ? mb : -INFINITY);
+    const bool grow = mb * scale_log2 > m_run + kRescale;
+    if (ballot64(grow)) {
+      const float m_new = mb * scale_log2;
+      const float alpha = grow ? exp2f(m_run - m_new) : 1.f;   // 0 on a row's first block
+      if (grow) m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+    }
+    // exp2 argument <= kRescale; results below 2^-126 flush to zero
+    const float bias = !row_on ? -INFINITY : (m_run == -INFINITY ? 0.f : -m_run);
+    float ps = 0.f;
+    // P^T as the B operand of k-step ks (keys 16*ks ..): k-slot jj of lane
+    // half hl holds key 16*ks + 8*(jj/4) + 4*hl + jj%4, i.e. accumulator
+    // registers 8*(ks%2) .. 8*(ks%2)+7 of sacc[ks/2].
+    bf16x8 pf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float pv[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        pv[jj] = __builtin_amdgcn_exp2f(fmaf(sacc[ks / 2][8 * (ks % 2) + jj], scale_log2, bias));
+        ps += pv[jj];
+      }
+      uint4 uu;
+      uu.x = cvt_pk_bf16(pv[0], pv[1]);
+      uu.y = cvt_pk_bf16(pv[2], pv[3]);
+      uu.z = cvt_pk_bf16(pv[4], pv[5]);
+      uu.w = cvt_pk_bf16(pv[6], pv[7]);
+      pf[ks] = as_bf16x8(uu);
+    }
+    l_run += halves_sum(ps);
 
     // O^T += V^T P^T. In a transpose read each 16-lane group returns, to lane
     // j, element j%4 of the 8-byte chunks addressed by lanes j/4 + 4*i
-    // (i = 0..3); pointing lane k of group kg at
-    // V[32*k2 + 16*hh + 4*kg + k/4][16*dt + 4*(k%4)] thus hands lane j the V^T
-    // entries (d = 16*dt + j, keys 32*k2 + 16*hh + 4*kg + i), matching P^T's key
-    // slots. The swizzle of those rows depends on the lane only, so the offset
-    // is 8192*k2 + 4096*hh + (v_lane ^ (dt << 5)).
+    // (i = 0..3); with lane k pointing at V[kb + k/4][d0 + 4*(k%4)], lane j
+    // receives V^T entries (d0 + j, keys kb .. kb+3), matching P^T's k-slots.
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const bf16x8 vf = lds_read_vt(vt_b + k2 * 8192, v_lane ^ (dt << 5), (v_lane ^ (dt << 5)) + 4096);
-#pragma unroll
-        for (int s = 0; s < NST; ++s)
-          if (son & (1u << s)) oacc[s][dt] = mfma16(vf, pf[s][k2], oacc[s][dt]);
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 vf = lds_read_vt(vt_b + ks * 4096, v_lane[0] ^ (dt << 6), v_lane[1] ^ (dt << 6));
+        oacc[dt] = mfma32(vf, pf[ks], oacc[dt]);
       }
-    }
   }
 
   // ---------------------------------------------------------------- epilogue
+  // oacc[dt] register r of lane l: d = 32*dt + 8*(r/4) + 4*hl + r%4 of row r32.
+  if (my_t < n_q) {
+    const int h = g * G + r32 % G;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    uint16_t* dst = out + ((int64_t(b) * Hq + h) * n_q + my_t) * kD;
 #pragma unroll
-  for (int s = 0; s < NST; ++s) {
-    const int t = tok0 + w * TPW + s * TPS + r16 / G;
-    if (t >= n_q) continue;
-    const int h = g * G + r16 % G;
-    const float inv = l_run[s] > 0.f ? 1.f / l_run[s] : 0.f;
-    uint16_t* dst = out + ((int64_t(b) * Hq + h) * n_q + t) * kD;
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      uint2 uu;
-      uu.x = cvt_pk_bf16(oacc[s][dt][0] * inv, oacc[s][dt][1] * inv);
-      uu.y = cvt_pk_bf16(oacc[s][dt][2] * inv, oacc[s][dt][3] * inv);
-      *reinterpret_cast<uint2*>(dst + dt * 16 + kg * 4) = uu;
-    }
-    if (lse && kg == 0)
-      lse[(int64_t(b) * Hq + h) * n_q + t] = (m_run[s] + log2f(l_run[s])) * 0.69314718055994531f;
+      for (int rb = 0; rb < 4; ++rb) {
+        uint2 uu;
+        uu.x = cvt_pk_bf16(oacc[dt][4 * rb] * inv, oacc[dt][4 * rb + 1] * inv);
+        uu.y = cvt_pk_bf16(oacc[dt][4 * rb + 2] * inv, oacc[dt][4 * rb + 3] * inv);
+        *reinterpret_cast<uint2*>(dst + 32 * dt + 8 * rb + 4 * hl) = uu;
+      }
+    if (lse && hl == 0)
+      lse[(int64_t(b) * Hq + h) * n_q + my_t] = (m_run + log2f(l_run)) * 0.69314718055994531f;
   }
 }
 
 namespace {
 
-int prefill_nst(int G) { return G == 1 ? 1 : 2; }
-
-int prefill_tq(int G) { return 4 * prefill_nst(G) * (16 / G); }
+int prefill_tq(int G) {
+  switch (G) {
+    case 1: return PrefillShape<1>::TQ;
+    case 2: return PrefillShape<2>::TQ;
+    case 4: return PrefillShape<4>::TQ;
+    case 8: return PrefillShape<8>::TQ;
+    default: return PrefillShape<16>::TQ;
+  }
+}
 
 // Largest number of union entries one tile can list (tiles whose tokens are
 // all dense list none): the selected blocks of TQ tokens plus at most 2 own
@@ -465,7 +481,7 @@ int64_t prefill_umax(const Dims& d, int mode, int64_t nb) {
 }
 
 size_t prefill_lds(int nstage, int64_t umax) {
-  return size_t(nstage) * kStageBytes + size_t(umax) * 12 + 512 * 4 + 16;
+  return size_t(nstage) * kStageBytes + size_t(umax) * 12 + 512 * 4 + 64;
 }
 
 }  // namespace
@@ -480,24 +496,24 @@ int prefill128_stages(const Dims& d, int mode, int64_t kv_len) {
   return 0;
 }
 
-template <int G, int NST>
+template <int G>
 static hipError_t launch_prefill_t(const Dims& d, int mode, const uint16_t* q, int n_q,
                                    const uint16_t* k, const uint16_t* v, int64_t kv_cap,
                                    int64_t kv_len, const int32_t* idx, uint16_t* out, float* lse,
                                    hipStream_t s) {
-  constexpr int TQ = 4 * NST * (16 / G);
-  const int ntile = (n_q + TQ - 1) / TQ;
+  using Sh = PrefillShape<G>;
+  const int ntile = (n_q + Sh::TQ - 1) / Sh::TQ;
   const int64_t nb = (kv_len - 1) / kBlock + 1;
   const int nstage = prefill128_stages(d, mode, kv_len);
   if (nstage == 0) return hipErrorInvalidValue;
   const int64_t umax = prefill_umax(d, mode, nb);
-  auto kern = prefill_attn_kernel<G, NST>;
+  auto kern = prefill_attn_kernel<G>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      160 * 1024);
   if (attr != hipSuccess) return attr;
   const dim3 grid(unsigned(int64_t(d.B) * d.Hkv * ntile));
-  kern<<<grid, 256, prefill_lds(nstage, umax), s>>>(
+  kern<<<grid, Sh::NT, prefill_lds(nstage, umax), s>>>(
       q, k, v, idx, out, lse, d.Hq, d.Hkv, n_q, kv_cap, kv_len, d.K, d.dense_thr, mode,
       d.scale * 1.4426950408889634f, ntile, int(umax), nstage);
   return hipGetLastError();
@@ -507,11 +523,11 @@ hipError_t launch_prefill128(const Dims& d, int mode, const uint16_t* q, int n_q
                              const uint16_t* k, const uint16_t* v, int64_t kv_cap, int64_t kv_len,
                              const int32_t* idx, uint16_t* out, float* lse, hipStream_t s) {
   switch (d.G) {
-    case 1: return launch_prefill_t<1, 1>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s);
-    case 2: return launch_prefill_t<2, 2>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s);
-    case 4: return launch_prefill_t<4, 2>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s);
-    case 8: return launch_prefill_t<8, 2>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s);
-    case 16: return launch_prefill_t<16, 2>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s);
+    case 1: return launch_prefill_t<1>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s);
+    case 2: return launch_prefill_t<2>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s);
+    case 4: return launch_prefill_t<4>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s);
+    case 8: return launch_prefill_t<8>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s);
+    case 16: return launch_prefill_t<16>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s);
     default: return hipErrorInvalidValue;
   }
 }
