@@ -59,6 +59,98 @@ def prefill_flops(w) -> dict:
     return dict(attn=attn, score=score, total=attn + score)
 
 
+# ------------------------------------------------------------------ measured HBM traffic
+# Kernels launched by each timed entry point, and the sources their code comes from.
+ENTRY_KERNELS = {
+    "score_blocks": (("score_kernel",), ("score.hip",)),
+    "sparse_attn_decode": (("decode_split_kernel", "decode_combine_kernel", "decode_union_kernel"),
+                           ("attn_decode.hip",)),
+    "sparse_attn_prefill": (("prefill_attn_kernel",), ("attn_prefill.hip",)),
+    "topk_blocks_fused": (("topk_fused_kernel",), ("topk.hip",)),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "trainable_block_sparse_infllm_amd", "csrc")
+
+
+def source_hash(entry: str) -> str:
+    """Hash of the sources an entry point's kernels are compiled from (with the shared headers)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ENTRY_KERNELS[entry][1] + ("common.hpp", "launch.hpp"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(entry: str):
+    """HBM bytes per launch of an entry point from the stored counter runs, or None when none
+    were taken or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    e = t.get("entries", {}).get(entry)
+    if not e or e.get("source_hash") != source_hash(entry):
+        return None
+    return e["bytes_per_launch"]
+
+
+def _short(name: str) -> str:
+    import re
+    return re.sub(r"\(.*$", "", name).replace("void ", "").replace("infllmv2::", "")
+
+
+def summarize_trace(db: str, title: str, command: str) -> str:
+    """Markdown table of per-kernel durations from a rocprofv3 --kernel-trace database."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, count(*), sum(duration), avg(duration), min(duration), max(duration) "
+                       "from kernels group by name order by sum(duration) desc").fetchall()
+    tot = sum(r[2] for r in rows)
+    out = [f"# {title}", "", "Command (from the repository root, one MI355X):", "", "```", command, "```", "",
+           "| kernel | calls | avg us | min us | max us | total us | % |", "|---|---|---|---|---|---|---|"]
+    for n, c, sm, a, mn, mx in rows:
+        out.append(f"| `{_short(n)}` | {c} | {a / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} | "
+                   f"{sm / 1e3:.1f} | {100 * sm / tot:.1f} |")
+    return "\n".join(out) + "\n"
+
+
+def _pmc_per_kernel(db: str, counter: str) -> dict:
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = con.execute("select kernel_name, value from counters_collection where counter_name = ?",
+                       (counter,)).fetchall()
+    agg = {}
+    for name, val in rows:
+        agg.setdefault(_short(name), []).append(float(val))
+    return agg
+
+
+def summarize_pmc(fetch_db: str, write_db: str, copy_bytes: int) -> dict:
+    """Per-launch HBM traffic of each entry point from FETCH_SIZE / WRITE_SIZE runs (KiB per
+    dispatch). Each counter is scaled by what it reads for the largest plain copies in the same run
+    (copy_bytes each way), which calibrates the counter against bytes actually moved."""
+    fetch, write = _pmc_per_kernel(fetch_db, "FETCH_SIZE"), _pmc_per_kernel(write_db, "WRITE_SIZE")
+    cf = max(fetch.get("__amd_rocclr_copyBuffer", [0.0]))
+    cw = max(write.get("__amd_rocclr_copyBuffer", [0.0]))
+    if cf <= 0 or cw <= 0:
+        raise SystemExit("no plain copy in the counter runs to calibrate against")
+    ff, fw = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    entries = {}
+    for entry, (kernels, _) in ENTRY_KERNELS.items():
+        per = {}
+        for kn in kernels:
+            fk = [v for n, vs in fetch.items() if n.startswith(kn) for v in vs]
+            wk = [v for n, vs in write.items() if n.startswith(kn) for v in vs]
+            if fk and wk:
+                per[kn] = dict(fetch_kib=sum(fk) / len(fk), write_kib=sum(wk) / len(wk), dispatches=len(fk))
+        if per:
+            b = sum(ff * k["fetch_kib"] * 1024 + fw * k["write_kib"] * 1024 for k in per.values())
+            entries[entry] = dict(kernels=per, bytes_per_launch=round(b), source_hash=source_hash(entry))
+    return dict(fetch_factor=round(ff, 4), write_factor=round(fw, 4), copy_bytes=copy_bytes, entries=entries)
+
+
 # ------------------------------------------------------------------ timing helpers
 def timed_loop(fns_per_step, steps, warmup, torch):
     """Run warmup steps, then `steps` timed steps; events between stages give per-stage times."""
@@ -209,7 +301,24 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
+    ap.add_argument("--summarize-trace", metavar="DB",
+                    help="print a markdown summary of a rocprofv3 --kernel-trace database and exit")
+    ap.add_argument("--title", default="kernel trace")
+    ap.add_argument("--command", default="")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="write profiles/traffic.json from FETCH_SIZE and WRITE_SIZE runs of this bench and exit")
     args = ap.parse_args()
+    if args.summarize_trace:
+        sys.stdout.write(summarize_trace(args.summarize_trace, args.title, args.command))
+        return
+    if args.summarize_pmc:
+        # the decode leg clones the 2 GiB K and V caches of decode_128k_b8 for its rotations
+        t = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], copy_bytes=1 << 31)
+        os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+        with open(TRAFFIC_FILE, "w") as fh:
+            json.dump(t, fh, indent=1)
+        print(json.dumps(t, indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for {args.gpus})",
               file=sys.stderr)
@@ -256,7 +365,8 @@ def main():
                    "kv_heads": wd.n_kv_heads, "head_dim": wd.head_dim, "top_k": wd.top_k,
                    "block": 64, "kernel_window": 32, "kernel_stride": 16, "rotations": args.rotations},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(dominant),
                      "algorithmic_bytes_per_launch": dom_bytes},
         "step_hbm": {"algorithmic_bytes": b["total"], "achieved_gbs": round(step_gbs, 1),
                      "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
@@ -275,7 +385,8 @@ def main():
             "stages_ms": {k: round(v, 4) for k, v in pst.items()},
             "roofline": {"bound": "mfma", "kernel": "sparse_attn_prefill", "achieved": round(attn_tf, 2),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+                         "frac": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic("sparse_attn_prefill")},
         }
     if args.copy_calibration:
         n = 1 << 30
