@@ -175,6 +175,61 @@ def test_topk_from_fp32_scores_is_exact_with_ties():
     assert np.array_equal(idx.cpu().numpy().reshape(-1, K), ref)
 
 
+def _fused_topk_chunk(w, L, n_q, tree, seed, periodic=0):
+    """Scores + top-K of n_q query rows at the end of an L-token context (tree: all
+    rows at position L - n_q) through the fused entry point, and the oracle's."""
+    d = synth.generate(w, seed=seed)
+    if periodic:
+        for j in range(periodic, L // 64):
+            d["k"][:, :, 64 * j:64 * j + 64] = d["k"][:, :, 64 * (j % periodic):64 * (j % periodic) + 64]
+    P = L - n_q
+    qn = np.ascontiguousarray(d["q"][:, :, P:])
+    pos = np.full(n_q, P, dtype=np.int64) if tree else P + np.arange(n_q, dtype=np.int64)
+    kbar_o = orc.pool(d["k"], L)
+    rows = orc.all_group_rows(w.batch, w.n_kv_heads, n_q)
+    if not periodic:
+        dd = dict(d, q=qn, n_q=n_q, q_pos0=P)
+        open_gaps(dd, orc, kbar=kbar_o, pos=pos)
+        qn = dd["q"]
+    R, Cn = orc.scores(qn, kbar_o, pos, rows, w.n_kv_heads)
+    ref = orc.select(R, Cn, w.top_k)
+    cfg = cfg_of(w)
+    k = dev_bf16(d["k"])
+    kbar = ops.pool_kernels(cfg, k, d["kv_cap"], L)
+    idx = torch.empty((w.batch, w.n_kv_heads, n_q, w.top_k), dtype=torch.int32, device="cuda")
+    lib.infllmv2_topk_blocks(cfg, None, dev_bf16(qn), kbar, n_q, P, int(tree), d["kv_cap"], idx)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy().reshape(-1, w.top_k), ref, R, Cn
+
+
+@pytest.mark.parametrize("L,n_q,tree,hq,hkv,K", [(20000, 64, False, 8, 2, 16), (20000, 16, True, 8, 2, 16),
+                                                 (40000, 64, False, 4, 1, 16), (9000, 40, False, 16, 2, 8),
+                                                 (9000, 40, False, 16, 1, 5), (6000, 70, False, 2, 2, 12)])
+def test_fused_topk_chunk_matches_oracle(L, n_q, tree, hq, hkv, K):
+    """Fused scoring + selection for a chunk of queries late in a long context:
+    at most 512 candidates and K <= 16 take the per-token-group kernel, 40000
+    tokens (624 candidates) the general one."""
+    w = P0.scaled(name="fused_chunk", n_q_heads=hq, n_kv_heads=hkv, seq_len=L, top_k=K, n_plant=4,
+                  dense_threshold=0)
+    note(f"fused top-K L{L} n_q{n_q} tree{tree} Hq{hq}/Hkv{hkv} K{K}")
+    gidx, ref, _, _ = _fused_topk_chunk(w, L, n_q, tree, seed=13)
+    assert np.array_equal(gidx, ref)
+
+
+def test_fused_topk_exact_ties_take_lower_index():
+    """Blocks repeating with period 5 tie exactly (identical kernels): the K
+    selected are the lowest indices of the best class."""
+    L, n_q = 8192, 64
+    w = P0.scaled(name="fused_ties", n_q_heads=8, n_kv_heads=2, seq_len=L, top_k=16, n_plant=0,
+                  dense_threshold=0)
+    gidx, ref, R, Cn = _fused_topk_chunk(w, L, n_q, False, seed=17, periodic=5)
+    for r in range(len(Cn)):
+        top = np.unique(R[r, :Cn[r]])[::-1]
+        assert top[0] - top[1] > 1e-3, "classes too close for an exact comparison"
+    assert np.array_equal(gidx, ref)
+    assert (np.diff(gidx, axis=1) % 5 == 0).all(), "selection should be one tie class"
+
+
 # ---------------------------------------------------------------------------- decode / tree
 def run_decode(w, seed=0, tree=True):
     mask = None

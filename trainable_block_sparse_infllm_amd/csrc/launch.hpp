@@ -29,6 +29,13 @@ hipError_t launch_attn_rows(const Dims& d, int mode, const uint16_t* q, int n_q,
                             const uint16_t* v, int64_t kv_cap, int64_t kv_len, const int32_t* idx,
                             uint16_t* out, float* lse, hipStream_t s);
 
+// head_dim 128 fused scoring + top-K for prefill chunks (at most 512
+// candidate blocks); topk_prefill128_ok() says whether it takes the shape.
+bool topk_prefill128_ok(const Dims& d, int64_t cmax);
+hipError_t launch_topk_prefill128(const Dims& d, const uint16_t* q, const uint16_t* kbar, int n_q,
+                                  int64_t q_pos0, int is_tree, int64_t nblk, int64_t cmax,
+                                  int32_t* idx, hipStream_t s);
+
 // head_dim 128 prefill / dense attention over a per-tile block union staged
 // through an LDS ring. prefill128_stages() returns the ring depth for the
 // shape, or 0 if it does not fit (then launch_attn_rows is used).

@@ -1,114 +1,15 @@
 // Top-K block selection (MiniCPM4 technical-report summary, QbitAI repost,
 // section "Model architecture: InfLLM v2": only the most relevant context
 // blocks take part in attention; item 2: one block set per GQA group).
-//
-// Rule: with at most K candidates all are taken; otherwise the K highest
-// scores, compared as fp32, with the lower block index first on equal scores.
-// Rows are written ascending and padded with -1.
-//
-// One wavefront selects one row whose n <= 64*KPL candidates sit in registers
-// (candidate j in lane j % 64, slot j / 64). The K-th largest score key T is
-// found bit by bit from the most significant end, each step counting the keys
-// >= a trial value with ballots (after a prefilter that usually leaves one
-// candidate per lane); the row is then emitted in index order with
-// ballot/mbcnt compaction, taking every key > T and the first K - #(> T) keys
-// equal to T. All decisions are integer comparisons on order-preserving score
-// keys, so the choice is exact for the given scores.
+// The selection rule and the wavefront routine are in topk_select.hpp.
 //
 // Two producers feed it: a score tensor (decode, trees), or scores computed
 // in the same workgroup with MFMA and kept in LDS (prefill; never stored).
 #include "common.hpp"
 #include "launch.hpp"
+#include "topk_select.hpp"
 
 namespace infllmv2 {
-
-// Exact K-th largest key by a most-significant-bit-first search: T is the
-// largest value with #(keys >= T) >= K. One ballot per register slot per bit.
-template <int N>
-__device__ __forceinline__ uint32_t kth_largest(const uint32_t (&key)[N], int K) {
-  uint32_t T = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = T | (1u << bit);
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int r = 0; r < N; ++r) cnt += popc64(ballot64(key[r] >= cand));
-    if (cnt >= uint32_t(K)) T = cand;
-  }
-  return T;
-}
-
-// Emit, in ascending slot order (r*64 + lane), every key > T and the first
-// K - #(> T) keys equal to T; `idx_of` maps a slot to the block index written.
-template <int N, typename F>
-__device__ __forceinline__ void emit_topk(const uint32_t (&key)[N], uint32_t T, int K,
-                                          int32_t* __restrict__ out, F idx_of) {
-  const int l = lane_id();
-  uint32_t ngt = 0;
-#pragma unroll
-  for (int r = 0; r < N; ++r) ngt += popc64(ballot64(key[r] > T));
-  const uint32_t take_eq = uint32_t(K) - ngt;
-  uint32_t base = 0, eq_seen = 0;
-#pragma unroll
-  for (int r = 0; r < N; ++r) {
-    const bool eq = key[r] == T;
-    const uint64_t eqm = ballot64(eq);
-    const bool take = key[r] > T || (eq && eq_seen + mbcnt64(eqm) < take_eq);
-    const uint64_t tm = ballot64(take);
-    if (take) out[base + mbcnt64(tm)] = idx_of(r, l);
-    base += popc64(tm);
-    eq_seen += popc64(eqm);
-  }
-}
-
-// Top-K of one row held by one wavefront: candidate j sits in lane j % 64,
-// slot j / 64; keys of slots past n are 0 (below every real key). `scratch`
-// is 64 (key, index) pairs of LDS private to the wavefront.
-//
-// Prefilter: the K-th largest of the 64 per-lane maxima, T0, is a lower bound
-// of the K-th largest key (at least K lanes hold a key >= T0), so the answer
-// lies among the keys >= T0. When those fit one per lane (the usual case: a
-// few dozen), the exact search runs over them alone; otherwise over all keys.
-template <int KPL>
-__device__ __forceinline__ void wave_topk(const uint32_t (&key)[KPL], int n, int K,
-                                          int32_t* __restrict__ out, uint32_t* scratch) {
-  const int l = lane_id();
-  if (n <= K) {
-    for (int t = l; t < K; t += kWave) out[t] = t < n ? t : -1;
-    return;
-  }
-  if (K <= kWave) {
-    uint32_t mx[1] = {0u};
-#pragma unroll
-    for (int r = 0; r < KPL; ++r) mx[0] = max(mx[0], key[r]);
-    const uint32_t T0 = kth_largest<1>(mx, K);
-    uint32_t nc = 0;
-#pragma unroll
-    for (int r = 0; r < KPL; ++r) nc += popc64(ballot64(key[r] >= T0));
-    if (nc <= uint32_t(kWave)) {
-      uint32_t base = 0;
-#pragma unroll
-      for (int r = 0; r < KPL; ++r) {
-        const bool c = key[r] >= T0;
-        const uint64_t m = ballot64(c);
-        if (c) {
-          const uint32_t pos = base + mbcnt64(m);
-          scratch[2 * pos] = key[r];
-          scratch[2 * pos + 1] = uint32_t(r * kWave + l);
-        }
-        base += popc64(m);
-      }
-      __builtin_amdgcn_wave_barrier();
-      uint32_t ck[1] = {uint32_t(l) < nc ? scratch[2 * l] : 0u};
-      const int32_t cj = uint32_t(l) < nc ? int32_t(scratch[2 * l + 1]) : -1;
-      const uint32_t T = kth_largest<1>(ck, K);
-      emit_topk<1>(ck, T, K, out, [&](int, int) { return cj; });
-      __builtin_amdgcn_wave_barrier();
-      return;
-    }
-  }
-  const uint32_t T = kth_largest<KPL>(key, K);
-  emit_topk<KPL>(key, T, K, out, [](int r, int ln) { return r * kWave + ln; });
-}
 
 // ---------------------------------------------------------------- from scores
 template <int KPL>
@@ -276,6 +177,8 @@ hipError_t launch_topk_fused(const Dims& d, const uint16_t* q, const uint16_t* k
   const int64_t pos_last = is_tree ? q_pos0 : q_pos0 + n_q - 1;
   int64_t cmax = pos_last / kBlock;
   if (cmax > nblk) cmax = nblk;
+  if (topk_prefill128_ok(d, cmax))
+    return launch_topk_prefill128(d, q, kbar, n_q, q_pos0, is_tree, nblk, cmax, idx, s);
   const int kpl = pick_kpl(cmax);
   // Columns per workgroup: largest of 64/32/16 whose score tile fits 64 KB of LDS.
   int nt = 4;
