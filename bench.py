@@ -254,7 +254,7 @@ def bench_prefill(w, steps, warmup, torch, lib, ops, synth):
     q, k, v = dev(d["q"]), dev(d["k"]), dev(d["v"])
     T, kv_cap = w.seq_len, d["kv_cap"]
     del d
-    kbar = torch.zeros((w.batch, w.n_kv_heads, ops.nblk(kv_cap), 3, w.head_dim), dtype=torch.bfloat16,
+    kbar = torch.zeros(ops.kbar_shape(w.batch, w.n_kv_heads, kv_cap, w.head_dim), dtype=torch.bfloat16,
                        device="cuda")
     idx = torch.empty((w.batch, w.n_kv_heads, T, w.top_k), dtype=torch.int32, device="cuda")
     out = torch.empty((w.batch, w.n_q_heads, T, w.head_dim), dtype=torch.bfloat16, device="cuda")

@@ -36,7 +36,12 @@
  *     row-major, 16-byte aligned;
  *   - layouts: q   [B][Hq][n_q][D]         (heads g*G .. g*G+G-1 form group g)
  *              k,v [B][Hkv][kv_cap][D]     (rows >= kv_len are never read)
- *              kbar [B][Hkv][nblk][3][D]   nblk = ceil(kv_cap / 64)
+ *              kbar [B][Hkv][3][D/8][nblk][8]  nblk = ceil(kv_cap / 64): kernel m of
+ *                                          block j, elements 8p .. 8p+7, sit at
+ *                                          [b][g][m][p][j][0..7] (16-byte pieces of
+ *                                          consecutive blocks are adjacent, so a
+ *                                          load of one piece across blocks is
+ *                                          contiguous)
  *              scores [B][Hkv][n_q][nblk]  fp32, -inf past a row's candidates
  *              idx [B][Hkv][n_q][K]        int32
  *              out [B][Hq][n_q][D]         bf16
@@ -88,7 +93,8 @@ typedef struct infllmv2_cfg {
 } infllmv2_cfg;
 
 /* Semantic kernels of the complete blocks j in [first_block, kv_len/64):
- * kbar[b][g][j][m][:] = bf16(mean of k[b][g][64j+16m .. 64j+16m+31][:]), m = 0..2.
+ * kernel m of block j = bf16(mean of k[b][g][64j+16m .. 64j+16m+31][:]), m = 0..2,
+ * stored in the kbar layout above.
  * (QbitAI summary, "Model architecture: InfLLM v2", item 1: blocks are made of
  * fine-grained semantic kernels.) first_block lets a decode loop extend the
  * table when a block completes; blocks outside the range are not written. */
@@ -97,7 +103,7 @@ INFLLMV2_API int infllmv2_pool_kernels(const infllmv2_cfg* cfg, const void* k, i
 
 /* Block scores of every query row (QbitAI summary, "Model architecture:
  * InfLLM v2", items 1 and 2): scores[b][g][i][j] = sum over the heads h of
- * group g of max over m of q[b][h][i] . kbar[b][g][j][m], for j < floor(p_i/64);
+ * group g of max over m of q[b][h][i] . (kernel m of block j), for j < floor(p_i/64);
  * -inf for every other j < nblk. Positions: p_i = q_pos0 + i, or q_pos0 for
  * every row when is_tree != 0 (all draft nodes score against the prefix). */
 INFLLMV2_API int infllmv2_score_blocks(const infllmv2_cfg* cfg, const void* q, int32_t n_q, int64_t q_pos0,

@@ -31,6 +31,13 @@ def host_u16(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def kbar_rows(t: torch.Tensor) -> np.ndarray:
+    """Device kernel table [B][Hkv][3][D/8][nblk][8] -> the oracle's [B][Hkv][nblk][3][D] (bf16 bits)."""
+    a = host_u16(t)
+    B, Hkv, kpb, P, nb, e = a.shape
+    return np.ascontiguousarray(a.transpose(0, 1, 4, 2, 3, 5).reshape(B, Hkv, nb, kpb, P * e))
+
+
 def host_f64(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 

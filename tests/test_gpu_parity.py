@@ -14,7 +14,7 @@ import synth
 import trainable_block_sparse_infllm_amd as lib
 from trainable_block_sparse_infllm_amd import ops
 from gaps import open_gaps
-from gpu_util import (LSE_ABS, assert_close_rows, cfg_of, check_idx_rows, dev_bf16, dev_i32, dev_u64,
+from gpu_util import (LSE_ABS, assert_close_rows, cfg_of, check_idx_rows, dev_bf16, dev_i32, dev_u64, kbar_rows,
                       host_f64, host_u16, note)
 
 pytestmark = pytest.mark.gpu
@@ -72,7 +72,7 @@ TREE_CASES = {
 
 def _kbar_check(d, kbar_gpu, kbar_o):
     nfull = d["kv_len"] // 64
-    g = host_u16(kbar_gpu)
+    g = kbar_rows(kbar_gpu)
     assert np.array_equal(g[:, :, :nfull], kbar_o[:, :, :nfull]), "k̄ differs from the oracle"
 
 
@@ -332,7 +332,7 @@ def test_pool_incremental_blocks_match():
     kbar = ops.pool_kernels(cfg, k, d["kv_cap"], 1000)             # blocks 0..14
     lib.infllmv2_pool_kernels(cfg, k, d["kv_cap"], 3000, 15, kbar)   # extend to 46 blocks
     torch.cuda.synchronize()
-    assert np.array_equal(host_u16(kbar)[:, :, :46], kbar_o[:, :, :46])
+    assert np.array_equal(kbar_rows(kbar)[:, :, :46], kbar_o[:, :, :46])
 
 
 def test_decode_workspace_reused_across_shapes():

@@ -29,6 +29,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
 }
 
+// Offset (in elements) of the 16-byte piece p (elements 8p .. 8p+7) of kernel
+// m of block j in the k-bar table of group bg: [bg][m][D/8][nblk][8]. Pieces of
+// consecutive blocks are adjacent, so a wavefront reading one piece of 16 or
+// 32 consecutive blocks touches contiguous memory.
+template <int D>
+__device__ __forceinline__ int64_t kbar_off(int64_t bg, int m, int p, int64_t j, int64_t nblk) {
+  return ((bg * kKpb + m) * (D / 8) + p) * nblk * 8 + j * 8;
+}
+
 // Two floats -> packed bf16 pair (lo in the low half) with the hardware
 // round-to-nearest-even conversion (v_cvt_pk_bf16_f32).
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

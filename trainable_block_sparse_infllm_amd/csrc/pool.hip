@@ -8,7 +8,8 @@
 // fewer than 2^40, so the mean has a single value whatever the summation order
 // and the rounded kernel is reproducible bit for bit.
 //
-// HBM-bound: one read of K (64*D*2 bytes per block), 3*D*2 bytes written.
+// HBM-bound: one read of K (64*D*2 bytes per block), 3*D*2 bytes written
+// (16-byte pieces, in the piece-major k-bar layout).
 // One wavefront per block; lane l owns D/64 adjacent columns, so each row is a
 // single coalesced 2*D-byte wavefront load.
 #include "common.hpp"
@@ -29,7 +30,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ 
   const int64_t bg = item / nb;
   const int64_t j = first + item % nb;
   const uint16_t* src = k + (bg * kv_cap + j * kBlock) * D + CPL * l;
-  uint16_t* dst = kbar + (bg * nblk + j) * kKpb * D + CPL * l;
+  // lane l owns columns CPL*l ..: piece CPL*l/8, offset CPL*l%8 within it
+  const int piece = CPL * l / 8, within = CPL * l % 8;
 
   double s[4][CPL];
 #pragma unroll
@@ -58,9 +60,9 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ 
     if constexpr (CPL == 2) {
       const uint32_t lo = d2bf((s[m][0] + s[m + 1][0]) * 0.03125);
       const uint32_t hi = d2bf((s[m][1] + s[m + 1][1]) * 0.03125);
-      *reinterpret_cast<uint32_t*>(dst + m * D) = lo | (hi << 16);
+      *reinterpret_cast<uint32_t*>(kbar + kbar_off<D>(bg, m, piece, j, nblk) + within) = lo | (hi << 16);
     } else {
-      dst[m * D] = d2bf((s[m][0] + s[m + 1][0]) * 0.03125);
+      kbar[kbar_off<D>(bg, m, piece, j, nblk) + within] = d2bf((s[m][0] + s[m + 1][0]) * 0.03125);
     }
   }
 }

@@ -4,7 +4,7 @@
 // kernels; item 2, the query heads of one GQA group share the block choice, so
 // their relevances are summed).
 //
-//   R[b][g][i][j] = sum_{h in group g} max_{m<3} q[b][h][i] . kbar[b][g][j][m]
+//   R[b][g][i][j] = sum_{h in group g} max_{m<3} q[b][h][i] . (kernel m of block j)
 //
 // for j < floor(p_i / 64), -inf for every other j (p_i = q_pos0 + i, or q_pos0
 // for all tree nodes).
@@ -51,14 +51,16 @@ __global__ __launch_bounds__(64) void score_kernel(const uint16_t* __restrict__ 
 
   const int64_t jrow = j0 + r16;  // block row this lane feeds into the A operand
   const bool row_ok = jrow < nblk;
-  const uint16_t* kb = kbar + ((int64_t(bg) * nblk + (row_ok ? jrow : 0)) * kKpb) * D + kg * 8;
+  // A fragment row: block jrow; k-slots 8*kg .. of d step ks = piece 4*ks + kg
+  const int64_t jr = row_ok ? jrow : 0;
 
   f32x4 best[NT];
 #pragma unroll
   for (int m = 0; m < kKpb; ++m) {
     bf16x8 af[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) af[ks] = as_bf16x8(ldg16_if(row_ok, kb + m * D + ks * 32));
+    for (int ks = 0; ks < KS; ++ks)
+      af[ks] = as_bf16x8(ldg16_if(row_ok, kbar + kbar_off<D>(bg, m, 4 * ks + kg, jr, nblk)));
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};

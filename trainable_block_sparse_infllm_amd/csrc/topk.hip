@@ -89,13 +89,14 @@ __global__ __launch_bounds__(256) void topk_fused_kernel(const uint16_t* __restr
       const int64_t j0 = int64_t(ch) * 16;
       const int64_t jrow = j0 + r16;
       const bool row_ok = jrow < Cmax;
-      const uint16_t* kb = kbar + ((int64_t(bg) * nblk + (row_ok ? jrow : 0)) * kKpb) * D + kg * 8;
+      const int64_t jr = row_ok ? jrow : 0;     // A row: block jr; d step ks = piece 4*ks + kg
       f32x4 best[NT];
 #pragma unroll
       for (int m = 0; m < kKpb; ++m) {
         bf16x8 af[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) af[ks] = as_bf16x8(ldg16_if(row_ok, kb + m * D + ks * 32));
+        for (int ks = 0; ks < KS; ++ks)
+          af[ks] = as_bf16x8(ldg16_if(row_ok, kbar + kbar_off<D>(bg, m, 4 * ks + kg, jr, nblk)));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};

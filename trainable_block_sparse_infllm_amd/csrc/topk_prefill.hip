@@ -86,16 +86,17 @@ __global__ __launch_bounds__(256, 2) void topk_prefill_kernel(
       for (int ds = 0; ds < DS; ++ds) qa[st][ds] = as_bf16x8(ldg16_if(t < ntok, qrow + 16 * ds));
     }
     const int nchunk = int((Cmax + 31) / 32);
-    const uint16_t* kb_bg = kbar + int64_t(bg) * nblk * kKpb * kDK;
     // This wavefront's chunks are w, w + 4, ...; step s is (chunk w + 4*(s/3),
-    // kernel s%3). B operand of a step: block 32*chunk + r32, d = 16*ds + 8*hl ..
+    // kernel s%3). B operand of a step: block 32*chunk + r32, d = 16*ds + 8*hl ..,
+    // i.e. piece 2*ds + hl: 32 consecutive blocks of one piece are contiguous.
     const int nsteps = kKpb * ((nchunk - w + 3) / 4);
     auto load_step = [&](int s, bf16x8 (&dst)[DS]) {
       const int64_t blk = int64_t(w + 4 * (s / kKpb)) * 32 + r32;
       const bool ok = blk < Cmax;
-      const uint16_t* p = kb_bg + ((ok ? blk : 0) * kKpb + s % kKpb) * kDK + 8 * hl;
+      const int64_t jb = ok ? blk : 0;
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) dst[ds] = as_bf16x8(ldg16_if(ok, p + 16 * ds));
+      for (int ds = 0; ds < DS; ++ds)
+        dst[ds] = as_bf16x8(ldg16_if(ok, kbar + kbar_off<kDK>(bg, s % kKpb, 2 * ds + hl, jb, nblk)));
     };
     // Accumulator register r of lane l: tile row 32*st + 8*(r/4) + 4*hl + r%4,
     // block 32*chunk + r32. Max over the kernels; after the last, head sums
@@ -145,14 +146,17 @@ __global__ __launch_bounds__(256, 2) void topk_prefill_kernel(
       }
     };
 
-    // the next step's fragments load while one step computes
+    // The next step's fragments load while one step computes. The loads are
+    // issued unconditionally (a step past the end maps to blocks >= Cmax and
+    // reads zeros): behind a branch, the wait placed before the current
+    // step's MFMAs would also cover the prefetch.
     bf16x8 kfa[DS], kfb[DS];
-    if (nsteps > 0) load_step(0, kfa);
+    load_step(0, kfa);
     for (int s = 0; s < nsteps; s += 2) {
-      if (s + 1 < nsteps) load_step(s + 1, kfb);
+      load_step(s + 1, kfb);
       compute_step(s, kfa);
       if (s + 1 >= nsteps) break;
-      if (s + 2 < nsteps) load_step(s + 2, kfa);
+      load_step(s + 2, kfa);
       compute_step(s + 1, kfb);
     }
   }

@@ -36,6 +36,55 @@ __device__ __forceinline__ uint32_t kth_largest(const uint32_t (&key)[N], int K)
   return T;
 }
 
+// Value of lane l ^ J (J = 1, 2, ..., 32) without going through LDS: quad
+// permutes for 1 and 2, row shifts for 4 and 8, the gfx950 row swaps for 16
+// and 32 (permlane16_swap(x, x) leaves rows (0,0,2,2) / (1,1,3,3),
+// permlane32_swap(x, x) rows (0,1,0,1) / (2,3,2,3)).
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v, int l) {
+  if constexpr (J == 1) {
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+  } else if constexpr (J == 2) {
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+  } else if constexpr (J == 4 || J == 8) {
+    const uint32_t up = uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x100 + J, 0xF, 0xF, false));  // row_shl
+    const uint32_t dn = uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x110 + J, 0xF, 0xF, false));  // row_shr
+    return (l & J) ? dn : up;
+  } else if constexpr (J == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return ((l >> 4) & 1) ? r[0] : r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (l >= 32) ? r[0] : r[1];
+  }
+}
+
+// One bitonic stage: lanes l and l ^ J exchange so that segments of 2K lanes
+// (K = size of the merged run) end descending.
+template <int KS, int J>
+__device__ __forceinline__ uint32_t bitonic_step(uint32_t v, int l) {
+  const uint32_t p = xor_lane<J>(v, l);
+  const bool lower = (l & J) == 0;
+  const bool desc = (l & KS) == 0;
+  return lower == desc ? max(v, p) : min(v, p);
+}
+
+// K-th largest (with multiplicity, 1 <= K <= 64) of one key per lane: sort the
+// wavefront descending with a bitonic network and read lane K-1.
+__device__ __forceinline__ uint32_t kth_largest_lanes(uint32_t v, int K) {
+  const int l = lane_id();
+  v = bitonic_step<2, 1>(v, l);
+  v = bitonic_step<4, 2>(v, l);  v = bitonic_step<4, 1>(v, l);
+  v = bitonic_step<8, 4>(v, l);  v = bitonic_step<8, 2>(v, l);  v = bitonic_step<8, 1>(v, l);
+  v = bitonic_step<16, 8>(v, l); v = bitonic_step<16, 4>(v, l); v = bitonic_step<16, 2>(v, l);
+  v = bitonic_step<16, 1>(v, l);
+  v = bitonic_step<32, 16>(v, l); v = bitonic_step<32, 8>(v, l); v = bitonic_step<32, 4>(v, l);
+  v = bitonic_step<32, 2>(v, l);  v = bitonic_step<32, 1>(v, l);
+  v = bitonic_step<64, 32>(v, l); v = bitonic_step<64, 16>(v, l); v = bitonic_step<64, 8>(v, l);
+  v = bitonic_step<64, 4>(v, l);  v = bitonic_step<64, 2>(v, l);  v = bitonic_step<64, 1>(v, l);
+  return uint32_t(__builtin_amdgcn_readlane(int(v), K - 1));
+}
+
 // Emit, in ascending slot order (r*64 + lane), every key > T and the first
 // K - #(> T) keys equal to T; `idx_of` maps a slot to the block index written.
 template <int N, typename F>
@@ -79,7 +128,7 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[KPL], int n, int
     uint32_t mx[1] = {0u};
 #pragma unroll
     for (int r = 0; r < KPL; ++r) mx[0] = max(mx[0], key[r]);
-    const uint32_t T0 = kth_largest<1>(mx, K);
+    const uint32_t T0 = kth_largest_lanes(mx[0], K);
     uint32_t nc = 0;
 #pragma unroll
     for (int r = 0; r < KPL; ++r) nc += popc64(ballot64(key[r] >= T0));
@@ -99,7 +148,7 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[KPL], int n, int
       __builtin_amdgcn_wave_barrier();
       uint32_t ck[1] = {uint32_t(l) < nc ? scratch[2 * l] : 0u};
       const int32_t cj = uint32_t(l) < nc ? int32_t(scratch[2 * l + 1]) : -1;
-      const uint32_t T = kth_largest<1>(ck, K);
+      const uint32_t T = kth_largest_lanes(ck[0], K);
       emit_topk<1>(ck, T, K, out, [&](int, int) { return cj; });
       __builtin_amdgcn_wave_barrier();
       return;

@@ -33,10 +33,15 @@ class Workspace:
         return self.buf
 
 
+def kbar_shape(B: int, Hkv: int, kv_cap: int, D: int) -> tuple:
+    """Kernel table [B][Hkv][3][D/8][nblk][8]: 16-byte pieces of consecutive blocks adjacent."""
+    return (B, Hkv, 3, D // 8, nblk(kv_cap), 8)
+
+
 def pool_kernels(cfg, k, kv_cap, kv_len, first_block=0, kbar=None, stream=None):
     B, Hkv, _, D = k.shape
     if kbar is None:
-        kbar = torch.zeros((B, Hkv, nblk(kv_cap), 3, D), dtype=torch.bfloat16, device=k.device)
+        kbar = torch.zeros(kbar_shape(B, Hkv, kv_cap, D), dtype=torch.bfloat16, device=k.device)
     capi.infllmv2_pool_kernels(cfg, k, kv_cap, kv_len, first_block, kbar, stream)
     return kbar
 
