@@ -10,9 +10,11 @@
 //           p + 1 < dense_threshold;
 //   mode 1 (dense causal): keys 0..p;      mode 2 (dense): keys 0..kv_len-1.
 //
-// Work layout. A workgroup of NW wavefronts owns TQ <= 64 consecutive tokens
-// of one (b, g); each wavefront owns one sub-tile of 32 MFMA rows (32/G tokens
-// x G heads; one token's heads share a key set). The products run on the
+// Work layout. A workgroup of NW wavefronts (4; 2 for G = 1) owns TQ <= 64
+// consecutive tokens of one (b, g); each wavefront owns one sub-tile of 32
+// MFMA rows (32/G tokens x G heads; one token's heads share a key set). Two
+// workgroups share a CU, so the wavefronts on a SIMD are not tied by
+// barriers and one's MFMA work overlaps the other's softmax and waits. The products run on the
 // 32x32x16 bf16 MFMA, which on gfx950 sustains twice the rate of the 16x16x32
 // form. On the 32K workload 64 consecutive tokens need ~45 distinct blocks
 // between them while each needs 17, so the tile walks that union once and
@@ -64,10 +66,12 @@ __device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 
 template <int G>
 struct PrefillShape {
   static constexpr int TPS = 32 / G;
-  static constexpr int NW = TPS >= 8 ? 64 / TPS : 8;
+  static constexpr int NW = TPS >= 16 ? 64 / TPS : 4;
   static constexpr int TQ = NW * TPS;
   static constexpr int NT = 64 * NW;
   static constexpr int LPS = 32 / NW;
+  // wavefronts per SIMD the register budget must allow (two workgroups per CU)
+  static constexpr int MINW = G == 1 ? 1 : 2;
   static_assert(TQ <= 64, "token masks are 64-bit");
 };
 
@@ -173,7 +177,7 @@ __device__ __forceinline__ float halves_sum(float x) {
 }  // namespace
 
 template <int G>
-__global__ __launch_bounds__(PrefillShape<G>::NT) void prefill_attn_kernel(
+__global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void prefill_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ out, float* __restrict__ lse, int Hq,
     int Hkv, int n_q, int64_t kv_cap, int64_t kv_len, int K, int dense_thr, int mode,
@@ -491,9 +495,12 @@ int prefill128_stages(const Dims& d, int mode, int64_t kv_len) {
   const int64_t nb = (kv_len - 1) / kBlock + 1;
   if (nb > 256 * 32) return 0;
   const int64_t umax = prefill_umax(d, mode, nb);
+  // two workgroups per CU (80 KB of LDS each): their wavefronts share the
+  // SIMDs without sharing barriers, so one's MFMA work overlaps the other's
+  // softmax and memory waits
   for (int ns = 4; ns >= 2; --ns)
-    if (prefill_lds(ns, umax) <= 160 * 1024) return ns;
-  return 0;
+    if (prefill_lds(ns, umax) <= 80 * 1024) return ns;
+  return prefill_lds(2, umax) <= 160 * 1024 ? 2 : 0;
 }
 
 template <int G>
