@@ -127,14 +127,19 @@ __global__ __launch_bounds__(256) void decode_union_kernel(
 }
 
 // ------------------------------------------------------------------ split
-// V tile in LDS, row-major (64 keys x D), 16-byte pieces XOR-swizzled by key:
-// piece p of row r holds V[r][8*(p ^ sw(r)) .. +7] with sw(r) = 2*((r >> 2) & 3).
-// It is filled straight from HBM (global_load_lds, 1 KB per wavefront
-// instruction). A V^T fragment element V[key][d] is one 2-byte read; the four
-// 16-lane groups of a fragment read use keys 4 apart, so the swizzle sends
-// them to distinct pieces and the read is free of bank conflicts. For these
-// keys sw(key) = 2*kg, a per-lane constant, so every address is a base plus a
-// compile-time offset.
+// V tile in LDS, row-major (64 keys x D), 16-byte pieces XOR-swizzled by key
+// and filled straight from HBM (global_load_lds, 1 KB per wavefront
+// instruction); rows past kv_len read zeros.
+//   D = 128: piece p of row r holds V[r][8*(p ^ swz(r)) ..], swz(r) =
+//     ((r & 7) << 1) | ((r >> 3) & 1). V^T fragments come from transpose reads
+//     (ds_read_b64_tr_b16): each 16-lane group reads 4 consecutive rows x 2
+//     adjacent pieces, which the swizzle spreads over distinct banks.
+//   D = 64: piece p of row r holds V[r][8*(p ^ sw(r)) ..], sw(r) =
+//     2*((r >> 2) & 3); a V^T element is one 2-byte read, and the four 16-lane
+//     groups of a fragment read use keys 4 apart, which the swizzle sends to
+//     distinct pieces.
+__device__ __forceinline__ int vswz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
 template <int D>
 __device__ __forceinline__ void load_v_tile(const uint16_t* vbase, int64_t key0, int64_t kv_len,
                                             uint16_t* vt) {
@@ -146,15 +151,34 @@ __device__ __forceinline__ void load_v_tile(const uint16_t* vbase, int64_t key0,
     const int r = x * RPI + l / PPR;
     const int piece = l % PPR;
     const int64_t key = key0 + r;
-    const int sw = ((r >> 2) & 3) << 1;
+    const int sw = D == 128 ? vswz(r) : ((r >> 2) & 3) << 1;
     const void* src = key < kv_len ? static_cast<const void*>(vbase + key * D + ((piece ^ sw) << 3))
                                    : static_cast<const void*>(kZeroPiece);
     load_lds16(src, vt + x * RPI * D);
   }
 }
 
+typedef short dv4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) dv4i16 lds_dv4i16;
+typedef __attribute__((address_space(3))) char lds_dchar;
+
+// V^T fragment of the 16x16x32 product (D = 128): two transpose reads, keys
+// +0 and +16 of the fragment's row group. Each 16-lane group returns, to lane
+// j, element j%4 of the 8-byte chunks addressed by lanes j/4 + 4*i; lane k of
+// group kg points at V[32*k2 + 16*hh + 4*kg + k/4][16*dt + 4*(k%4)], so lane j
+// receives V^T(d = 16*dt + j, keys 32*k2 + 16*hh + 4*kg + i), the P^T key slots.
+__device__ __forceinline__ bf16x8 read_vt_tr(const uint16_t* vt, int off0, int off1) {
+  const lds_dchar* base = (const lds_dchar*)vt;
+  dv4i16 h[2];
+  h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_dv4i16*)(base + off0));
+  h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_dv4i16*)(base + off1));
+  bf16x8 r;
+  __builtin_memcpy(&r, h, sizeof r);
+  return r;
+}
+
 template <int D, int NSTD>
-__global__ __launch_bounds__(64, NSTD == 1 ? 2 : 1) void decode_split_kernel(
+__global__ __launch_bounds__(64, NSTD == 1 ? 3 : 1) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, const uint64_t* __restrict__ tree_mask,
     const int32_t* __restrict__ u_blk, const uint64_t* __restrict__ u_mask,
@@ -314,26 +338,45 @@ __global__ __launch_bounds__(64, NSTD == 1 ? 2 : 1) void decode_split_kernel(
       }
     }
     wait_vmem();                                   // the V tile has landed in LDS
-    const uint16_t* vlane = vt + 4 * kg * D + r16;  // key 4*kg, column r16 (swizzle applied per dt)
+    if constexpr (D == 128) {
+      // byte offset of lane (r16, kg)'s chunk for d tile 0, rows 4*kg + r16/4
+      const int v_row = 4 * kg + r16 / 4;
+      const int v_lane = v_row * (D * 2) + ((((r16 % 4) >> 1) ^ vswz(v_row)) << 4) + 8 * (r16 & 1);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const uint16_t* vcol = vlane + ((dt ^ kg) << 4);
+      for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        // key slots (kg, jj): key = 32*k2 + 16*(jj/4) + 4*kg + jj%4, matching pf's packing
-        uint32_t w4[4];
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int off = k2 * 32 * D * 2 + (v_lane ^ (dt << 5));
+          const bf16x8 vf = read_vt_tr(vt, off, off + 16 * D * 2);
 #pragma unroll
-        for (int hp = 0; hp < 4; ++hp) {
-          const int koff = 32 * k2 + 16 * (hp / 2) + 2 * (hp % 2);   // jj = 2*hp
-          const uint32_t lo = vcol[koff * D];
-          const uint32_t hi = vcol[(koff + 1) * D];
-          w4[hp] = lo | (hi << 16);
+          for (int s = 0; s < NSTD; ++s) {
+            if (!sub_on[s]) continue;
+            oacc[s][dt] = mfma16(vf, pf[s][k2], oacc[s][dt]);
+          }
         }
-        const bf16x8 vf = as_bf16x8(uint4{w4[0], w4[1], w4[2], w4[3]});
+      }
+    } else {
+      const uint16_t* vlane = vt + 4 * kg * D + r16;  // key 4*kg, column r16 (swizzle applied per dt)
 #pragma unroll
-        for (int s = 0; s < NSTD; ++s) {
-          if (!sub_on[s]) continue;
-          oacc[s][dt] = mfma16(vf, pf[s][k2], oacc[s][dt]);
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint16_t* vcol = vlane + ((dt ^ kg) << 4);
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          // key slots (kg, jj): key = 32*k2 + 16*(jj/4) + 4*kg + jj%4, matching pf's packing
+          uint32_t w4[4];
+#pragma unroll
+          for (int hp = 0; hp < 4; ++hp) {
+            const int koff = 32 * k2 + 16 * (hp / 2) + 2 * (hp % 2);   // jj = 2*hp
+            const uint32_t lo = vcol[koff * D];
+            const uint32_t hi = vcol[(koff + 1) * D];
+            w4[hp] = lo | (hi << 16);
+          }
+          const bf16x8 vf = as_bf16x8(uint4{w4[0], w4[1], w4[2], w4[3]});
+#pragma unroll
+          for (int s = 0; s < NSTD; ++s) {
+            if (!sub_on[s]) continue;
+            oacc[s][dt] = mfma16(vf, pf[s][k2], oacc[s][dt]);
+          }
         }
       }
     }
