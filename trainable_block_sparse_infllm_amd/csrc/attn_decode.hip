@@ -13,10 +13,13 @@
 //
 //   union (n_q > 1 only): per (b, g), the ascending list of blocks any row
 //     needs, each with a bitmask of the rows (tokens) that need it;
-//   split: one wavefront per (b, g, split of SB union entries). K fragments
-//     go from HBM straight into MFMA registers (A operand of S^T = K Q^T);
-//     V goes through LDS stored transposed (A operand of O^T = V^T P^T);
-//   combine: one wavefront per (b, h, row).
+//   split: one workgroup per (b, g, split of SB union entries), one wavefront
+//     per entry, so every entry's loads are in flight together. K fragments go
+//     from HBM straight into MFMA registers (A operand of S^T = K Q^T); V goes
+//     through LDS (A operand of O^T = V^T P^T). The wavefronts' partials merge
+//     in LDS; a workgroup covering all of a group's entries writes the output
+//     itself, otherwise one partial per split is stored;
+//   combine (more than one split): one wavefront per (b, h, row).
 #include <algorithm>
 
 #include "common.hpp"
@@ -26,8 +29,11 @@ namespace infllmv2 {
 
 namespace {
 
+constexpr int kMaxWaves = 9;    // one 16-row sub-tile per wavefront (<= 170 registers)
+constexpr int kMaxWaves2 = 4;   // two sub-tiles per wavefront
+
 struct DecodeLayout {
-  int64_t bgs, max_e, nsplit, rows;
+  int64_t bgs, max_e, nsplit, rows, sb;
   size_t off_union, off_mask, off_count, off_ml, off_o, total;
 };
 
@@ -43,9 +49,12 @@ DecodeLayout decode_layout(const Dims& d, int n_q, int64_t kv_len) {
     const int64_t local = last_blk - P / kBlock + 1;
     L.max_e = maybe_dense ? last_blk + 1 : std::min(last_blk + 1, int64_t(n_q) * d.K + local);
   }
-  const int64_t sb = std::max<int64_t>(1, (L.bgs * L.max_e + 4095) / 4096);
-  L.nsplit = (L.max_e + sb - 1) / sb;
+  // entries per split (= wavefronts per workgroup): about one workgroup per CU
+  // for the whole step, at most kMaxWaves (their V tiles share 160 KB of LDS)
   L.rows = int64_t(n_q) * d.G;
+  const int maxw = L.rows > 16 ? kMaxWaves2 : kMaxWaves;
+  L.sb = std::min<int64_t>(maxw, std::max<int64_t>(1, (L.bgs * L.max_e + 255) / 256));
+  L.nsplit = (L.max_e + L.sb - 1) / L.sb;
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   size_t off = 0;
   L.off_union = off;
@@ -178,17 +187,22 @@ __device__ __forceinline__ bf16x8 read_vt_tr(const uint16_t* vt, int off0, int o
 }
 
 template <int D, int NSTD>
-__global__ __launch_bounds__(64, NSTD == 1 ? 3 : 1) void decode_split_kernel(
+__global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, const uint64_t* __restrict__ tree_mask,
     const int32_t* __restrict__ u_blk, const uint64_t* __restrict__ u_mask,
     const int32_t* __restrict__ u_count, float* __restrict__ part_ml, float* __restrict__ part_o,
-    int Hq, int Hkv, int G, int n_q, int64_t kv_cap,
-    int64_t kv_len, int K, int dense_thr, int is_tree, int sb, int nsplit, int max_e, int rows,
-    float scale_log2) {
+    uint16_t* __restrict__ out, float* __restrict__ lse, int Hq, int Hkv, int G, int n_q,
+    int64_t kv_cap, int64_t kv_len, int K, int dense_thr, int is_tree, int sb, int nsplit,
+    int max_e, int rows, float scale_log2) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
-  __shared__ __align__(16) uint16_t vt[kBlock * D];
+  constexpr int WR = 16 * NSTD;                       // rows of a workgroup
+  extern __shared__ __align__(16) uint16_t dsm[];     // [waves][64*D]: V tile, then O partial
+  __shared__ float2 s_ml[kMaxWaves][WR];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int nwv = blockDim.x / kWave;
+  uint16_t* vt = dsm + w * kBlock * D;
   const int l = lane_id();
   const int r16 = l % 16, kg = l / 16;
   const int item = xcd_remap(blockIdx.x, gridDim.x);
@@ -240,7 +254,7 @@ __global__ __launch_bounds__(64, NSTD == 1 ? 3 : 1) void decode_split_kernel(
     for (int dt = 0; dt < DT; ++dt) oacc[s][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int u = u0; u < u1; ++u) {
+  for (int u = u0 + w; u < u1; u += nwv) {
     int64_t j;
     uint64_t nmask;
     if (n_q == 1) {
@@ -304,23 +318,22 @@ __global__ __launch_bounds__(64, NSTD == 1 ? 3 : 1) void decode_split_kernel(
           sacc[s][kt][i] = x;
           mb = fmaxf(mb, x);
         }
-      mb = fmaxf(mb, __shfl_xor(mb, 16));
-      mb = fmaxf(mb, __shfl_xor(mb, 32));
+      mb = rows4_max(mb);
       const float m_new = fmaxf(m_run[s], mb);
       const bool none = m_new == -INFINITY;
       const float alpha = none ? 1.f : exp2f(m_run[s] - m_new);
+      const float neg_m = none ? 0.f : -m_new;    // masked keys: exp2(-inf) = 0
       float ps = 0.f;
       float pv[4][4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float e = none ? 0.f : exp2f(sacc[s][kt][i] - m_new);
+          const float e = __builtin_amdgcn_exp2f(sacc[s][kt][i] + neg_m);
           pv[kt][i] = e;
           ps += e;
         }
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
+      ps = rows4_sum(ps);
       l_run[s] = l_run[s] * alpha + ps;
       m_run[s] = m_new;
 #pragma unroll
@@ -330,10 +343,10 @@ __global__ __launch_bounds__(64, NSTD == 1 ? 3 : 1) void decode_split_kernel(
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         uint4 uu;
-        uu.x = pack_bf16x2(pv[2 * k2][0], pv[2 * k2][1]);
-        uu.y = pack_bf16x2(pv[2 * k2][2], pv[2 * k2][3]);
-        uu.z = pack_bf16x2(pv[2 * k2 + 1][0], pv[2 * k2 + 1][1]);
-        uu.w = pack_bf16x2(pv[2 * k2 + 1][2], pv[2 * k2 + 1][3]);
+        uu.x = cvt_pk_bf16(pv[2 * k2][0], pv[2 * k2][1]);
+        uu.y = cvt_pk_bf16(pv[2 * k2][2], pv[2 * k2][3]);
+        uu.z = cvt_pk_bf16(pv[2 * k2 + 1][0], pv[2 * k2 + 1][1]);
+        uu.w = cvt_pk_bf16(pv[2 * k2 + 1][2], pv[2 * k2 + 1][3]);
         pf[s][k2] = as_bf16x8(uu);
       }
     }
@@ -382,21 +395,49 @@ __global__ __launch_bounds__(64, NSTD == 1 ? 3 : 1) void decode_split_kernel(
     }
   }
 
-  // partials: ml[bg][split][row] = (m, l); o[bg][split][row][d] (unnormalized)
+  // This wavefront's partial -> LDS: (m, l) per row, O (unnormalized, zeros
+  // for rows that saw no key) in the wavefront's V tile, [row][D] fp32.
+  wait_lds();
+  float* o_s = reinterpret_cast<float*>(vt);
 #pragma unroll
   for (int s = 0; s < NSTD; ++s) {
-    const int row = row0 + s * 16 + r16;
-    if (row >= rows) continue;
-    const int64_t pr = (int64_t(bg) * nsplit + split) * rows + row;
-    if (kg == 0) {
-      part_ml[pr * 2 + 0] = m_run[s];
-      part_ml[pr * 2 + 1] = l_run[s];
-    }
-    float* dst = part_o + pr * D;       // zeros when the row saw no key in this split
+    const int wr = s * 16 + r16;
+    if (kg == 0) s_ml[w][wr] = make_float2(m_run[s], l_run[s]);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<float4*>(dst + dt * 16 + kg * 4) =
+      *reinterpret_cast<float4*>(o_s + wr * D + dt * 16 + kg * 4) =
           make_float4(oacc[s][dt][0], oacc[s][dt][1], oacc[s][dt][2], oacc[s][dt][3]);
+  }
+  __syncthreads();
+  // Merge the wavefronts by log-sum-exp; thread t takes (row, column) pairs.
+  const bool final = nsplit == 1;
+  for (int e = threadIdx.x; e < WR * D; e += blockDim.x) {
+    const int wr = e / D, c = e % D;
+    const int row = row0 + wr;
+    if (row >= rows) continue;
+    float M = -INFINITY;
+    for (int x = 0; x < nwv; ++x) M = fmaxf(M, s_ml[x][wr].x);
+    float Lsum = 0.f, acc = 0.f;
+    for (int x = 0; x < nwv; ++x) {
+      const float2 ml = s_ml[x][wr];
+      const float wgt = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
+      Lsum += wgt * ml.y;
+      acc += wgt * reinterpret_cast<const float*>(dsm + x * kBlock * D)[wr * D + c];
+    }
+    if (final) {
+      const int node = row / G, hh = row % G;
+      const int64_t rid = (int64_t(b) * Hq + g * G + hh) * n_q + node;
+      out[rid * D + c] = f2bf(Lsum > 0.f ? acc / Lsum : 0.f);
+      if (lse && c == 0) lse[rid] = (M + log2f(Lsum)) * 0.69314718055994531f;
+    } else {
+      // partials: ml[bg][split][row] = (m, l); o[bg][split][row][d] (unnormalized)
+      const int64_t pr = (int64_t(bg) * nsplit + split) * rows + row;
+      part_o[pr * D + c] = acc;
+      if (c == 0) {
+        part_ml[pr * 2 + 0] = M;
+        part_ml[pr * 2 + 1] = Lsum;
+      }
+    }
   }
 }
 
@@ -404,7 +445,7 @@ __global__ __launch_bounds__(64, NSTD == 1 ? 3 : 1) void decode_split_kernel(
 // One wavefront per output row (b, h, i), in two round trips: lanes over splits
 // read every split's (m, l), then every lane issues the loads of its D/64
 // columns for all splits of the chunk before using any of them.
-template <int D>
+template <int D, int CH>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     const float* __restrict__ part_ml, const float* __restrict__ part_o,
     const int32_t* __restrict__ u_count, uint16_t* __restrict__ out, float* __restrict__ lse,
@@ -426,14 +467,15 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   float acc[CPL];
 #pragma unroll
   for (int x = 0; x < CPL; ++x) acc[x] = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += kWave) {
-    const int s = s0 + l;
+  // chunks of CH splits (CH = 8 when every row has at most 8, else 64)
+  for (int s0 = 0; s0 < ns; s0 += CH) {
+    const int s = s0 + (l % CH);
     const float* ml = part_ml + (pr0 + int64_t(s) * rows) * 2;
-    const float ms = ldf_or_neginf(s < ns, ml);
-    const float ls = ldf_or_zero(s < ns, ml + 1);
-    float o[kWave][CPL];                       // this lane's columns of every split in the chunk
+    const float ms = l < CH ? ldf_or_neginf(s < ns, ml) : -INFINITY;
+    const float ls = l < CH ? ldf_or_zero(s < ns, ml + 1) : 0.f;
+    float o[CH][CPL];                          // this lane's columns of every split in the chunk
 #pragma unroll
-    for (int t = 0; t < kWave; ++t) {
+    for (int t = 0; t < CH; ++t) {
       const bool ok = s0 + t < ns;
       const float* src = part_o + (pr0 + int64_t(s0 + t) * rows) * D + CPL * l;
 #pragma unroll
@@ -448,7 +490,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
     for (int x = 0; x < CPL; ++x) acc[x] *= a;
     M = m_new;
 #pragma unroll
-    for (int t = 0; t < kWave; ++t) {
+    for (int t = 0; t < CH; ++t) {
       const float wt = __shfl(wgt, t);
 #pragma unroll
       for (int x = 0; x < CPL; ++x) acc[x] += wt * o[t][x];
@@ -478,7 +520,7 @@ hipError_t launch_decode(const Dims& d, const uint16_t* q, int n_q, const uint16
   float* part_ml = reinterpret_cast<float*>(base + L.off_ml);
   float* part_o = reinterpret_cast<float*>(base + L.off_o);
   const int is_tree = tree_mask != nullptr;
-  const int sb = int((L.max_e + L.nsplit - 1) / L.nsplit);
+  const int sb = int(L.sb);
   if (n_q > 1) {
     const int nb = int((kv_len - 1) / kBlock) + 1;
     const size_t lds = size_t(nb) * 8;
@@ -498,27 +540,35 @@ hipError_t launch_decode(const Dims& d, const uint16_t* q, int n_q, const uint16
   const int n_e1 = int(L.max_e);
 #define SPLIT_CASE(DD, NN)                                                                        \
   if (d.D == DD && nstd == NN) {                                                                  \
-    decode_split_kernel<DD, NN><<<grid, 64, 0, s>>>(q, k, v, idx, tree_mask, u_blk, u_mask,       \
-                                                    u_count, part_ml, part_o, d.Hq, d.Hkv, d.G,  \
-                                                    n_q, kv_cap, kv_len, d.K, d.dense_thr,       \
-                                                    is_tree, sb, int(L.nsplit), int(L.max_e),    \
-                                                    int(L.rows), sl2);                           \
+    auto kern = decode_split_kernel<DD, NN>;                                                      \
+    static const hipError_t attr = hipFuncSetAttribute(                                           \
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,          \
+        (NN == 1 ? kMaxWaves : kMaxWaves2) * kBlock * DD * 2);                                    \
+    if (attr != hipSuccess) return attr;                                                          \
+    kern<<<grid, 64 * sb, size_t(sb) * kBlock * DD * 2, s>>>(                                     \
+        q, k, v, idx, tree_mask, u_blk, u_mask, u_count, part_ml, part_o, out, lse, d.Hq, d.Hkv,  \
+        d.G, n_q, kv_cap, kv_len, d.K, d.dense_thr, is_tree, sb, int(L.nsplit), int(L.max_e),     \
+        int(L.rows), sl2);                                                                        \
   } else
   SPLIT_CASE(128, 1) SPLIT_CASE(128, 2) SPLIT_CASE(64, 1) SPLIT_CASE(64, 2)
   { return hipErrorInvalidValue; }
 #undef SPLIT_CASE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (L.nsplit == 1) return hipSuccess;        // the split kernel wrote the output
   const int64_t nrows = int64_t(d.B) * d.Hq * n_q;
   const dim3 cgrid(unsigned((nrows + 3) / 4));
-  if (d.D == 128)
-    decode_combine_kernel<128><<<cgrid, 256, 0, s>>>(part_ml, part_o, u_count, out, lse, d.Hq,
-                                                     d.Hkv, d.G, n_q, int(L.nsplit), sb, n_e1,
-                                                     int(L.rows), nrows);
-  else
-    decode_combine_kernel<64><<<cgrid, 256, 0, s>>>(part_ml, part_o, u_count, out, lse, d.Hq,
-                                                    d.Hkv, d.G, n_q, int(L.nsplit), sb, n_e1,
-                                                    int(L.rows), nrows);
+#define COMBINE_CASE(DD, CC)                                                                      \
+  decode_combine_kernel<DD, CC><<<cgrid, 256, 0, s>>>(part_ml, part_o, u_count, out, lse, d.Hq,    \
+                                                      d.Hkv, d.G, n_q, int(L.nsplit), sb, n_e1,  \
+                                                      int(L.rows), nrows)
+  const bool few = L.nsplit <= 8;
+  if (d.D == 128) {
+    if (few) COMBINE_CASE(128, 8); else COMBINE_CASE(128, 64);
+  } else {
+    if (few) COMBINE_CASE(64, 8); else COMBINE_CASE(64, 64);
+  }
+#undef COMBINE_CASE
   return hipGetLastError();
 }
 
