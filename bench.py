@@ -3,8 +3,10 @@
 Headline (`value`): batched 128K decode throughput, tokens/s, for the
 decode_128k_b8 workload (8 sequences, 32 query / 8 KV heads, head_dim 128,
 131072-token caches, top-K 32 plus the own block): one step = block scoring
-over the whole k̄ table, top-K selection, and sparse attention (split + LSE
-combine) for the 8 new tokens, with k̄ already built. A second leg times the
+over the whole k̄ table (infllmv2_score_blocks), then top-K selection and
+sparse attention (split + LSE combine; infllmv2_sparse_attn_decode_scores,
+which selects inside the attention kernel) for the 8 new tokens, with k̄
+already built. A second leg times the
 32K causal sparse prefill (kernel pooling + fused score/top-K + attention) in
 TFLOP/s. Inputs are seeded synthetic tensors (synth) resident in HBM;
 decode steps rotate over independent copies of K, V and k̄ so that the
@@ -64,9 +66,12 @@ def prefill_flops(w) -> dict:
 ENTRY_KERNELS = {
     "score_blocks": (("score_kernel",), ("score.hip",)),
     "sparse_attn_decode": (("decode_split_kernel", "decode_combine_kernel", "decode_union_kernel"),
-                           ("attn_decode.hip",)),
+                           ("attn_decode.hip", "topk_select.hpp")),
+    "sparse_attn_decode_scores": (("decode_split_kernel", "decode_combine_kernel"),
+                                  ("attn_decode.hip", "topk_select.hpp")),
     "sparse_attn_prefill": (("prefill_attn_kernel",), ("attn_prefill.hip",)),
-    "topk_blocks_fused": (("topk_fused_kernel",), ("topk.hip",)),
+    "topk_blocks_fused": (("topk_prefill_kernel", "topk_fused_kernel"),
+                          ("topk.hip", "topk_prefill.hip", "topk_select.hpp")),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "trainable_block_sparse_infllm_amd", "csrc")
@@ -231,11 +236,12 @@ def bench_decode(w, steps, warmup, rotations, torch, lib, ops, synth):
     def step(s):
         # stream None: the binding uses torch's current stream (the capture stream inside a graph)
         k, v, kbar = sets[s % len(sets)]
+        # scores over the whole kernel table, then top-K selection and sparse attention in one
+        # entry point (the selection runs inside the attention kernel)
         return [
             lambda: lib.infllmv2_score_blocks(cfg, q, n_q, kv_len - 1, 0, kbar, kv_cap, scores, None),
-            lambda: lib.infllmv2_topk_blocks(cfg, scores, None, None, n_q, kv_len - 1, 0, kv_cap, idx, None),
-            lambda: lib.infllmv2_sparse_attn_decode(cfg, q, n_q, k, v, kv_cap, kv_len, idx, None, out, None,
-                                                    ws, nbytes, None),
+            lambda: lib.infllmv2_sparse_attn_decode_scores(cfg, q, k, v, kv_cap, kv_len, scores, idx, out, None,
+                                                           ws, nbytes, None),
         ]
     log(f"decode: timing {steps} eager steps after {warmup} warmup (per-stage events)")
     ms, stage_ms, _ = timed_loop(step, steps, warmup, torch)
@@ -336,13 +342,14 @@ def main():
     wd = synth.WORKLOADS["decode_128k_b8"]
     dec = bench_decode(wd, args.steps, args.warmup, args.rotations, torch, lib, ops, synth)
     tok_s = wd.batch / (dec["ms"] * 1e-3)
-    names = ["score_blocks", "topk_blocks", "sparse_attn_decode"]
+    names = ["score_blocks", "sparse_attn_decode_scores"]
     stage = dict(zip(names, dec["stage_ms"]))
     b = dec["bytes"]
     score_gbs = b["score"] / (stage["score_blocks"] * 1e-3) / 1e9
-    attn_gbs = b["attn"] / (stage["sparse_attn_decode"] * 1e-3) / 1e9
+    attn_gbs = b["attn"] / (stage["sparse_attn_decode_scores"] * 1e-3) / 1e9
     step_gbs = b["total"] / (dec["ms"] * 1e-3) / 1e9
-    dominant = "score_blocks" if stage["score_blocks"] >= stage["sparse_attn_decode"] else "sparse_attn_decode"
+    dominant = "score_blocks" if stage["score_blocks"] >= stage["sparse_attn_decode_scores"] \
+        else "sparse_attn_decode_scores"
     dom_gbs = score_gbs if dominant == "score_blocks" else attn_gbs
     dom_bytes = b["score"] if dominant == "score_blocks" else b["attn"]
     result = {

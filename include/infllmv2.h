@@ -152,6 +152,24 @@ INFLLMV2_API int infllmv2_sparse_attn_decode(const infllmv2_cfg* cfg, const void
                                 void* out, float* lse, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* A single-token decode step from block scores, in fewer launches (QbitAI
+ * summary, "Model architecture: InfLLM v2", item 2: one block set per GQA
+ * group, chosen by relevance): selects every group's top-K blocks from
+ * scores [B][Hkv][1][nblk] (as written by infllmv2_score_blocks with n_q = 1,
+ * q_pos0 = kv_len - 1), by the rule of infllmv2_topk_blocks, then attends
+ * them exactly as infllmv2_sparse_attn_decode with n_q = 1 and no tree mask.
+ * The selection runs inside the attention kernel (each split of a group
+ * repeats it) instead of in a kernel of its own.
+ *   idx_out: NULL, or [B][Hkv][1][K] int32 receiving the selected blocks.
+ *   Requires top_k <= 64 and at most 4096 candidate blocks ((kv_len-1)/64),
+ *   else INFLLMV2_UNSUPPORTED; workspace as for infllmv2_sparse_attn_decode
+ *   with n_q = 1. */
+INFLLMV2_API int infllmv2_sparse_attn_decode_scores(const infllmv2_cfg* cfg, const void* q,
+                                       const void* k_cache, const void* v_cache, int64_t kv_cap,
+                                       int64_t kv_len, const float* scores, int32_t* idx_out,
+                                       void* out, float* lse, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
 /* Dense attention of n_q queries at positions kv_len - n_q + i over the first
  * kv_len keys, causal (key <= position) or not: the short-context path
  * (QbitAI summary, "Model architecture: InfLLM v2": dense attention kept for

@@ -90,6 +90,11 @@ CASES = [
     ("infllmv2_sparse_attn_decode", {}, (A, 1, A, A, 64, 64, B, None, A, None, 0x100000, 16, None), -3, "workspace"),
     ("infllmv2_sparse_attn_decode", {}, (A, 65, A, A, 128, 128, B, None, A, None, 0x100000, 1 << 30, None), -1, "64 query rows"),
     ("infllmv2_sparse_attn_decode", {}, (A, 2, A, A, 128, 128, B, A + 4, A, None, 0x100000, 1 << 30, None), -1, "tree_mask"),
+    ("infllmv2_sparse_attn_decode_scores", {}, (A, A, A, 64, 64, None, None, B, None, 0x100000, 1 << 30, None), -1, "scores is NULL"),
+    ("infllmv2_sparse_attn_decode_scores", {}, (A, A, A, 64, 64, A + 2, None, B, None, 0x100000, 1 << 30, None), -1, "scores"),
+    ("infllmv2_sparse_attn_decode_scores", dict(top_k=65), (A, A, A, 64, 64, A, None, B, None, 0x100000, 1 << 30, None), -2, "top_k above 64"),
+    ("infllmv2_sparse_attn_decode_scores", {}, (A, A, A, 1 << 20, 1 << 20, A, None, B, None, 0x100000, 1 << 40, None), -2, "4096"),
+    ("infllmv2_sparse_attn_decode_scores", {}, (A, A, A, 64, 64, A, None, B, None, 0x100000, 16, None), -3, "workspace"),
     ("infllmv2_dense_attn", {}, (A, 1, A, A, 64, 0, 1, B, None, None), -1, "kv_len"),
     ("infllmv2_dense_attn", {}, (A, 1, A, None, 64, 64, 1, B, None, None), -1, "v is NULL"),
     ("infllmv2_dense_attn", dict(softmax_scale=float("nan")), (A, 1, A, A, 64, 64, 1, B, None, None), -1, "finite"),

@@ -276,6 +276,35 @@ def test_tree_end_to_end(case):
     run_decode(TREE_CASES[case])
 
 
+def _decode_scores_matches_split_path(w, seed=0):
+    """The fused entry (selection inside the attention kernel) reproduces the
+    separate top-K + attention entry points bit for bit."""
+    d, ref, res = run_decode(w, seed=seed)
+    cfg = cfg_of(w)
+    k, v = dev_bf16(d["k"]), dev_bf16(d["v"])
+    q = dev_bf16(d["q"])
+    out = torch.empty_like(res["out"])
+    lse = torch.empty_like(res["lse"])
+    idx = torch.full_like(res["idx"], -7)
+    nbytes = lib.infllmv2_decode_workspace_bytes(cfg, 1, d["kv_len"])
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    lib.infllmv2_sparse_attn_decode_scores(cfg, q, k, v, d["kv_cap"], d["kv_len"], res["scores"], idx, out, lse,
+                                           ws, nbytes)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, res["idx"]), "selected blocks differ"
+    assert torch.equal(out.view(torch.int16), res["out"].view(torch.int16)), "outputs differ"
+    assert torch.equal(lse, res["lse"]), "lse differs"
+
+
+@pytest.mark.parametrize("case", list(DECODE_CASES))
+def test_decode_from_scores_equals_split_path(case):
+    _decode_scores_matches_split_path(DECODE_CASES[case])
+
+
+def test_decode_from_scores_128k_batch8_full_size():
+    _decode_scores_matches_split_path(W["decode_128k_b8"])
+
+
 def test_multi_token_decode_without_tree():
     run_decode(TREE_CASES["p1000_n7_d64"].scaled(name="mt_rows", seq_len=1020), tree=False)
 

@@ -273,6 +273,36 @@ int infllmv2_sparse_attn_decode(const infllmv2_cfg* cfg, const void* q, int32_t 
   return INFLLMV2_OK;
 }
 
+int infllmv2_sparse_attn_decode_scores(const infllmv2_cfg* cfg, const void* q, const void* k_cache,
+                                       const void* v_cache, int64_t kv_cap, int64_t kv_len,
+                                       const float* scores, int32_t* idx_out, void* out,
+                                       float* lse, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  const char* fn = "infllmv2_sparse_attn_decode_scores";
+  Dims d;
+  TRY(check_cfg(fn, cfg, true, &d));
+  TRY(check_attn(fn, d, q, 1, k_cache, v_cache, kv_cap, kv_len, out, lse));
+  TRY(check_ptr(fn, scores, "scores", 4));
+  if (idx_out) TRY(check_ptr(fn, idx_out, "idx_out", 4));
+  if (d.K > 64) return fail(INFLLMV2_UNSUPPORTED, fn, "top_k above 64");
+  if ((kv_len - 1) / 64 > 4096) return fail(INFLLMV2_UNSUPPORTED, fn, "more than 4096 candidate blocks");
+  TRY(check_ptr(fn, workspace, "workspace", 256));
+  const size_t need = infllmv2::decode_workspace_bytes(d, 1, kv_len);
+  if (workspace_bytes < need) {
+    char msg[128];
+    std::snprintf(msg, sizeof msg, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    return fail(INFLLMV2_WORKSPACE_TOO_SMALL, fn, msg);
+  }
+  TRY(check_device(fn));
+  LAUNCH(fn, infllmv2::launch_decode(d, static_cast<const uint16_t*>(q), 1,
+                                     static_cast<const uint16_t*>(k_cache),
+                                     static_cast<const uint16_t*>(v_cache), kv_cap, kv_len, nullptr,
+                                     nullptr, static_cast<uint16_t*>(out), lse, workspace,
+                                     workspace_bytes, static_cast<hipStream_t>(stream), scores,
+                                     idx_out));
+  return INFLLMV2_OK;
+}
+
 int infllmv2_dense_attn(const infllmv2_cfg* cfg, const void* q, int32_t n_q, const void* k,
                         const void* v, int64_t kv_cap, int64_t kv_len, int32_t causal, void* out,
                         float* lse, void* stream) {

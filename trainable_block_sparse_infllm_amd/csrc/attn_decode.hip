@@ -20,10 +20,17 @@
 //     in LDS; a workgroup covering all of a group's entries writes the output
 //     itself, otherwise one partial per split is stored;
 //   combine (more than one split): one wavefront per (b, h, row).
+//
+// Single-token decode can also take the block scores instead of the block
+// list (SKPL > 0): wavefront 0 of every split workgroup selects the group's
+// top-K from the score row (the wavefront top-K of topk_select.hpp; the other
+// splits of the group repeat the same selection) and the entries follow. This
+// saves the separate selection kernel and its round trip.
 #include <algorithm>
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "topk_select.hpp"
 
 namespace infllmv2 {
 
@@ -186,7 +193,7 @@ __device__ __forceinline__ bf16x8 read_vt_tr(const uint16_t* vt, int off0, int o
   return r;
 }
 
-template <int D, int NSTD>
+template <int D, int NSTD, int SKPL>
 __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, const uint64_t* __restrict__ tree_mask,
@@ -194,7 +201,8 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
     const int32_t* __restrict__ u_count, float* __restrict__ part_ml, float* __restrict__ part_o,
     uint16_t* __restrict__ out, float* __restrict__ lse, int Hq, int Hkv, int G, int n_q,
     int64_t kv_cap, int64_t kv_len, int K, int dense_thr, int is_tree, int sb, int nsplit,
-    int max_e, int rows, float scale_log2) {
+    int max_e, int rows, float scale_log2, const float* __restrict__ scores, int64_t nblk,
+    int32_t* __restrict__ idx_out) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   constexpr int WR = 16 * NSTD;                       // rows of a workgroup
@@ -227,6 +235,30 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
   const int u0 = split * sb;
   const int u1 = min(u0 + sb, n_e);
 
+  // block list of a single-token row selected here from its scores
+  __shared__ int32_t s_sel[SKPL > 0 ? 64 : 1];
+  if constexpr (SKPL > 0) {
+    __shared__ uint32_t s_scr[2 * kWave];
+    if (w == 0) {                                 // (dense rows ignore it; idx_out still gets it)
+      const int C = int(min(own1, nblk));
+      const float* row = scores + int64_t(bg) * nblk;
+      float val[SKPL];
+#pragma unroll
+      for (int r = 0; r < SKPL; ++r) {
+        const int j = r * kWave + l;
+        val[r] = ldf_or_neginf(j < C, row + j);   // -inf keys rank below every score
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      uint32_t key[SKPL];
+#pragma unroll
+      for (int r = 0; r < SKPL; ++r) key[r] = ordered_key(val[r]);
+      wave_topk<SKPL>(key, C, K, s_sel, s_scr);
+      if (split == 0 && idx_out)
+        for (int t = l; t < K; t += kWave) idx_out[int64_t(bg) * K + t] = s_sel[t];
+    }
+    __syncthreads();
+  }
+
   // rows of this lane: sub-tile s, row r16 -> (node, head)
   int node_of[NSTD];
   uint64_t tmask[NSTD];
@@ -258,7 +290,7 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
     int64_t j;
     uint64_t nmask;
     if (n_q == 1) {
-      j = dense1 ? u : (u < K ? idx[int64_t(bg) * K + u] : own1);
+      j = dense1 ? u : (u < K ? (SKPL > 0 ? s_sel[u] : idx[int64_t(bg) * K + u]) : own1);
       if (!dense1 && u < K && (j < 0 || j >= own1)) continue;
       nmask = 1ull;
     } else {
@@ -510,7 +542,7 @@ size_t decode_workspace_bytes(const Dims& d, int n_q, int64_t kv_len) {
 hipError_t launch_decode(const Dims& d, const uint16_t* q, int n_q, const uint16_t* k,
                          const uint16_t* v, int64_t kv_cap, int64_t kv_len, const int32_t* idx,
                          const uint64_t* tree_mask, uint16_t* out, float* lse, void* ws,
-                         size_t ws_bytes, hipStream_t s) {
+                         size_t ws_bytes, hipStream_t s, const float* scores, int32_t* idx_out) {
   const DecodeLayout L = decode_layout(d, n_q, kv_len);
   if (ws_bytes < L.total) return hipErrorInvalidValue;
   char* base = static_cast<char*>(ws);
@@ -538,9 +570,16 @@ hipError_t launch_decode(const Dims& d, const uint16_t* q, int n_q, const uint16
   const dim3 grid(unsigned(L.bgs * L.nsplit), ygroups);
   const float sl2 = d.scale * 1.4426950408889634f;
   const int n_e1 = int(L.max_e);
-#define SPLIT_CASE(DD, NN)                                                                        \
-  if (d.D == DD && nstd == NN) {                                                                  \
-    auto kern = decode_split_kernel<DD, NN>;                                                      \
+  const int64_t nblk = (kv_cap + kBlock - 1) / kBlock;
+  int skpl = 0;                                   // keys per lane of the in-kernel selection
+  if (scores) {
+    const int64_t c = std::min((kv_len - 1) / kBlock, nblk);
+    skpl = 1;
+    while (int64_t(skpl) * kWave < c) skpl <<= 1;
+  }
+#define SPLIT_CASE(DD, NN, SK)                                                                    \
+  if (d.D == DD && nstd == NN && skpl == SK) {                                                    \
+    auto kern = decode_split_kernel<DD, NN, SK>;                                                  \
     static const hipError_t attr = hipFuncSetAttribute(                                           \
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,          \
         (NN == 1 ? kMaxWaves : kMaxWaves2) * kBlock * DD * 2);                                    \
@@ -548,10 +587,15 @@ hipError_t launch_decode(const Dims& d, const uint16_t* q, int n_q, const uint16
     kern<<<grid, 64 * sb, size_t(sb) * kBlock * DD * 2, s>>>(                                     \
         q, k, v, idx, tree_mask, u_blk, u_mask, u_count, part_ml, part_o, out, lse, d.Hq, d.Hkv,  \
         d.G, n_q, kv_cap, kv_len, d.K, d.dense_thr, is_tree, sb, int(L.nsplit), int(L.max_e),     \
-        int(L.rows), sl2);                                                                        \
+        int(L.rows), sl2, scores, nblk, idx_out);                                                 \
   } else
-  SPLIT_CASE(128, 1) SPLIT_CASE(128, 2) SPLIT_CASE(64, 1) SPLIT_CASE(64, 2)
+#define SPLIT_SEL(DD)                                                                             \
+  SPLIT_CASE(DD, 1, 1) SPLIT_CASE(DD, 1, 2) SPLIT_CASE(DD, 1, 4) SPLIT_CASE(DD, 1, 8)            \
+  SPLIT_CASE(DD, 1, 16) SPLIT_CASE(DD, 1, 32) SPLIT_CASE(DD, 1, 64)
+  SPLIT_CASE(128, 1, 0) SPLIT_CASE(128, 2, 0) SPLIT_CASE(64, 1, 0) SPLIT_CASE(64, 2, 0)
+  SPLIT_SEL(128) SPLIT_SEL(64)
   { return hipErrorInvalidValue; }
+#undef SPLIT_SEL
 #undef SPLIT_CASE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

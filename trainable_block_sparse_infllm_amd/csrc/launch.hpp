@@ -46,9 +46,12 @@ hipError_t launch_prefill128(const Dims& d, int mode, const uint16_t* q, int n_q
 
 size_t decode_workspace_bytes(const Dims& d, int n_q, int64_t kv_len);
 
+// scores != nullptr (single-token rows only): the block lists are selected in
+// the kernel from scores [B][Hkv][1][nblk] (written to idx_out when given).
 hipError_t launch_decode(const Dims& d, const uint16_t* q, int n_q, const uint16_t* k,
                          const uint16_t* v, int64_t kv_cap, int64_t kv_len, const int32_t* idx,
                          const uint64_t* tree_mask, uint16_t* out, float* lse, void* ws,
-                         size_t ws_bytes, hipStream_t s);
+                         size_t ws_bytes, hipStream_t s, const float* scores = nullptr,
+                         int32_t* idx_out = nullptr);
 
 }  // namespace infllmv2

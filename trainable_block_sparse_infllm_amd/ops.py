@@ -80,6 +80,26 @@ def decode(cfg, q, k_cache, v_cache, kbar, kv_len, *, tree_mask=None, ws: Worksp
     return dict(scores=scores, idx=idx, out=out, lse=lse)
 
 
+def decode_step(cfg, q, k_cache, v_cache, kbar, kv_len, *, ws: Workspace | None = None, with_lse=True,
+                stream=None):
+    """One single-token decode step: block scores, then selection and attention in one entry point."""
+    B, Hq, n_q, D = q.shape
+    if n_q != 1:
+        raise ValueError("decode_step takes one new token per sequence")
+    kv_cap = k_cache.shape[2]
+    scores = torch.empty((B, cfg.n_kv_heads, 1, nblk(kv_cap)), dtype=torch.float32, device=q.device)
+    capi.infllmv2_score_blocks(cfg, q, 1, kv_len - 1, 0, kbar, kv_cap, scores, stream)
+    idx = torch.empty((B, cfg.n_kv_heads, 1, cfg.top_k), dtype=torch.int32, device=q.device)
+    out = _bf16_like((B, Hq, 1, D), q)
+    lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=q.device) if with_lse else None
+    nbytes = capi.infllmv2_decode_workspace_bytes(cfg, 1, kv_len)
+    ws = ws or Workspace(q.device)
+    buf = ws.get(nbytes)
+    capi.infllmv2_sparse_attn_decode_scores(cfg, q, k_cache, v_cache, kv_cap, kv_len, scores, idx, out, lse,
+                                            buf, buf.numel(), stream)
+    return dict(scores=scores, idx=idx, out=out, lse=lse)
+
+
 def dense(cfg, q, k, v, kv_len, *, causal=True, with_lse=True, stream=None):
     B, Hq, n_q, D = q.shape
     out = _bf16_like((B, Hq, n_q, D), q)
