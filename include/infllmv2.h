@@ -36,12 +36,14 @@
  *     row-major, 16-byte aligned;
  *   - layouts: q   [B][Hq][n_q][D]         (heads g*G .. g*G+G-1 form group g)
  *              k,v [B][Hkv][kv_cap][D]     (rows >= kv_len are never read)
- *              kbar [B][Hkv][3][D/8][nblk][8]  nblk = ceil(kv_cap / 64): kernel m of
- *                                          block j, elements 8p .. 8p+7, sit at
- *                                          [b][g][m][p][j][0..7] (16-byte pieces of
- *                                          consecutive blocks are adjacent, so a
- *                                          load of one piece across blocks is
- *                                          contiguous)
+ *              kbar [B][Hkv][T][3][D/8][32][8]  nblk = ceil(kv_cap / 64),
+ *                                          T = ceil(nblk / 32): kernel m of block j,
+ *                                          elements 8p .. 8p+7, sit at
+ *                                          [b][g][j/32][m][p][j%32][0..7] (tiles of 32
+ *                                          blocks; in a tile the 32 copies of one
+ *                                          16-byte piece are adjacent). The buffer
+ *                                          holds whole tiles: entries of blocks
+ *                                          >= nblk are read but never affect a result
  *              scores [B][Hkv][n_q][nblk]  fp32, -inf past a row's candidates
  *              idx [B][Hkv][n_q][K]        int32
  *              out [B][Hq][n_q][D]         bf16

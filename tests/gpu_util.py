@@ -32,10 +32,11 @@ def host_u16(t: torch.Tensor) -> np.ndarray:
 
 
 def kbar_rows(t: torch.Tensor) -> np.ndarray:
-    """Device kernel table [B][Hkv][3][D/8][nblk][8] -> the oracle's [B][Hkv][nblk][3][D] (bf16 bits)."""
+    """Device kernel table [B][Hkv][ntile][3][D/8][32][8] -> the oracle's [B][Hkv][nblk][3][D]
+    (bf16 bits; nblk rounded up to whole tiles of 32 blocks)."""
     a = host_u16(t)
-    B, Hkv, kpb, P, nb, e = a.shape
-    return np.ascontiguousarray(a.transpose(0, 1, 4, 2, 3, 5).reshape(B, Hkv, nb, kpb, P * e))
+    B, Hkv, nt, kpb, P, tb, e = a.shape
+    return np.ascontiguousarray(a.transpose(0, 1, 2, 5, 3, 4, 6).reshape(B, Hkv, nt * tb, kpb, P * e))
 
 
 def host_f64(t: torch.Tensor) -> np.ndarray:

@@ -239,24 +239,45 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
   __shared__ int32_t s_sel[SKPL > 0 ? 64 : 1];
   if constexpr (SKPL > 0) {
     __shared__ uint32_t s_scr[2 * kWave];
-    if (w == 0) {                                 // (dense rows ignore it; idx_out still gets it)
-      const int C = int(min(own1, nblk));
-      const float* row = scores + int64_t(bg) * nblk;
-      float val[SKPL];
-#pragma unroll
-      for (int r = 0; r < SKPL; ++r) {
-        const int j = r * kWave + l;
-        val[r] = ldf_or_neginf(j < C, row + j);   // -inf keys rank below every score
+    const int C = int(min(own1, nblk));           // (dense rows ignore the list; idx_out gets it)
+    const float* row = scores + int64_t(bg) * nblk;
+    const bool vec = (nblk & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
+    bool many = false;
+    if constexpr (SKPL >= 8) many = nwv >= 8;
+    if constexpr (SKPL >= 8) {
+      if (many) {                                 // eight wavefronts share the selection
+        __shared__ WgTopkLds s_tk;
+        wg_topk8<SKPL>(row, nblk, vec, C, K, s_sel, s_scr, s_tk);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      uint32_t key[SKPL];
-#pragma unroll
-      for (int r = 0; r < SKPL; ++r) key[r] = ordered_key(val[r]);
-      wave_topk<SKPL>(key, C, K, s_sel, s_scr);
-      if (split == 0 && idx_out)
-        for (int t = l; t < K; t += kWave) idx_out[int64_t(bg) * K + t] = s_sel[t];
     }
-    __syncthreads();
+    if (!many && w == 0) {
+      // lane l holds candidates SKPL*l .. SKPL*l + SKPL-1 (lane order = index order)
+      const int jl = l * SKPL;
+      float val[SKPL];
+      bool done = false;
+      if constexpr (SKPL >= 4) {
+        if (vec) {
+#pragma unroll
+          for (int r = 0; r < SKPL; r += 4) {
+            const int j = jl + r;
+            const uint4 u = ldg16_or_neginf(j < nblk, row + (j < nblk ? j : 0));
+            val[r] = __uint_as_float(u.x);
+            val[r + 1] = __uint_as_float(u.y);
+            val[r + 2] = __uint_as_float(u.z);
+            val[r + 3] = __uint_as_float(u.w);
+          }
+          done = true;
+        }
+      }
+      if (!done) {
+#pragma unroll
+        for (int r = 0; r < SKPL; ++r) val[r] = ldf_or_neginf(jl + r < nblk, row + jl + r);
+      }
+      wave_topk_lc<SKPL>(val, C, K, s_sel, s_scr);
+    }
+    lds_barrier();
+    if (w == 0 && split == 0 && idx_out)
+      for (int t = l; t < K; t += kWave) idx_out[int64_t(bg) * K + t] = s_sel[t];
   }
 
   // rows of this lane: sub-tile s, row r16 -> (node, head)

@@ -30,12 +30,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // Offset (in elements) of the 16-byte piece p (elements 8p .. 8p+7) of kernel
-// m of block j in the k-bar table of group bg: [bg][m][D/8][nblk][8]. Pieces of
-// consecutive blocks are adjacent, so a wavefront reading one piece of 16 or
-// 32 consecutive blocks touches contiguous memory.
+// m of block j in the k-bar table of group bg:
+//   [bg][ceil(nblk/32)][3][D/8][32][8]
+// Blocks are grouped in tiles of 32; inside a tile the 32 blocks' copies of
+// one piece are adjacent. A wavefront reading pieces 2s and 2s+1 of one tile
+// (lanes 0-31 and 32-63, the k-slot halves of a 16-wide MFMA step) touches
+// one contiguous kilobyte, and a whole tile is 3*D*64 contiguous bytes.
 template <int D>
 __device__ __forceinline__ int64_t kbar_off(int64_t bg, int m, int p, int64_t j, int64_t nblk) {
-  return ((bg * kKpb + m) * (D / 8) + p) * nblk * 8 + j * 8;
+  const int64_t ntile = (nblk + 31) >> 5;
+  return (((bg * ntile + (j >> 5)) * kKpb + m) * (D / 8) + p) * 256 + (j & 31) * 8;
+}
+
+// 32x32x16 bf16 MFMA. Operand A: lane l holds row l%32, k-slots 8*(l/32) ..
+// +7; operand B: lane l holds column l%32, the same k-slots. Accumulator
+// register r of lane l: row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // Two floats -> packed bf16 pair (lo in the low half) with the hardware
@@ -89,6 +101,7 @@ __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast
 // tensors they stand in for: the load then stays a global load, not a flat one.)
 static __device__ __align__(16) uint32_t kZeroPiece[4] = {0u, 0u, 0u, 0u};
 static __device__ float kNegInf = -INFINITY;
+static __device__ __align__(16) float kNegInf4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 static __device__ float kZeroF = 0.f;
 
 typedef __attribute__((address_space(1))) const uint32_t g_u32;   // global-space views
@@ -104,6 +117,12 @@ __device__ __forceinline__ uint64_t opaque_addr(const void* p) {
 
 __device__ __forceinline__ uint4 ldg16_if(bool ok, const void* p) {
   const g_u32x4* z = (const g_u32x4*)opaque_addr(kZeroPiece);
+  const u32x4_t v = *(ok ? (const g_u32x4*)p : z);
+  return uint4{v.x, v.y, v.z, v.w};
+}
+
+__device__ __forceinline__ uint4 ldg16_or_neginf(bool ok, const void* p) {   // four fp32 -inf
+  const g_u32x4* z = (const g_u32x4*)opaque_addr(kNegInf4);
   const u32x4_t v = *(ok ? (const g_u32x4*)p : z);
   return uint4{v.x, v.y, v.z, v.w};
 }
@@ -134,6 +153,16 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 
 // s_waitcnt lgkmcnt(0): every LDS access of this wave has completed.
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier for LDS traffic only: the wavefront's LDS operations have
+// completed, then s_barrier. Unlike __syncthreads it does not wait for the
+// wavefront's outstanding global stores.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  wait_lds();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <int W>
 __device__ __forceinline__ float xor_max(float v) {
@@ -196,6 +225,7 @@ __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
 // among non-NaN values).
 __device__ __forceinline__ uint32_t ordered_key(float f) {
   uint32_t u = __float_as_uint(f);
+  u = u == 0x80000000u ? 0u : u;   // -0 and +0 are equal scores
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 

@@ -9,7 +9,7 @@
 // and the rounded kernel is reproducible bit for bit.
 //
 // HBM-bound: one read of K (64*D*2 bytes per block), 3*D*2 bytes written
-// (16-byte pieces, in the piece-major k-bar layout).
+// (16-byte pieces, in the tiled k-bar layout of kbar_off).
 // One wavefront per block; lane l owns D/64 adjacent columns, so each row is a
 // single coalesced 2*D-byte wavefront load.
 #include "common.hpp"

@@ -10,90 +10,112 @@
 // for all tree nodes).
 //
 // HBM-bound: every candidate's 3*D bf16 kernels are read once per (b, g) and
-// shared by all n_q*G query columns of the group. One wavefront scores 16
-// blocks with MFMA 16x16x32 (A = 16 kernel rows of one kernel slot m, B = the
-// group's query columns); the max over m is elementwise across the three
-// accumulator tiles and the head sum is a shuffle over G adjacent lanes.
+// shared by all n_q*G query rows of the group. One wavefront scores one tile
+// of 32 blocks (3*D*64 contiguous bytes of the k-bar table; each load
+// instruction reads one contiguous kilobyte) with the 32x32x16 MFMA: operand A
+// is 32 (node, head) rows of q, operand B the 32 blocks' kernels of one slot
+// m. The max over m is elementwise across the three accumulators; the rows of
+// one node sit in one lane's registers (G <= 4) or in a lane and its partner
+// 32 lanes away (G >= 8), so the head sum needs at most one cross-lane step,
+// and each node's 32 scores leave as one 128-byte store.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace infllmv2 {
 
-// NT: 16-column tiles of query columns (n_q * G <= 16 * NT).
-template <int D, int NT>
+// NR: 32-row tiles of (node, head) rows per wavefront; rows are node * G + head.
+template <int D, int G, int NR>
 __global__ __launch_bounds__(64) void score_kernel(const uint16_t* __restrict__ q,
                                                    const uint16_t* __restrict__ kbar,
                                                    float* __restrict__ scores, int Hq, int Hkv,
-                                                   int G, int n_q, int64_t q_pos0, int is_tree,
+                                                   int n_q, int64_t q_pos0, int is_tree,
                                                    int64_t nblk, int ntile) {
-  constexpr int KS = D / 32;
+  constexpr int DS = D / 16;
   const int l = lane_id();
-  const int r16 = l % 16, kg = l / 16;
+  const int r32 = l % 32, hl = l / 32;
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   const int tile = item % ntile;
   const int bg = item / ntile;
   const int b = bg / Hkv, g = bg % Hkv;
-  const int64_t j0 = int64_t(tile) * 16;
+  const int64_t j0 = int64_t(tile) * 32;
+  const int row0 = blockIdx.y * NR * 32;
+  const int node_hi = min(n_q - 1, (row0 + NR * 32 - 1) / G);
+  const int64_t cmax = min((is_tree ? q_pos0 : q_pos0 + node_hi) / kBlock, nblk);
 
-  // B operand: query columns c = col0 + nt*16 + r16 -> (node c / G, head c % G).
-  const int col0 = blockIdx.y * NT * 16;
-  bf16x8 qf[NT][KS];
+  f32x16 best[NR];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int c = col0 + nt * 16 + r16;
-    const int node = c / G, hh = c % G;
+  for (int nr = 0; nr < NR; ++nr)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint16_t* qrow = q + ((int64_t(b) * Hq + g * G + hh) * n_q + (node < n_q ? node : 0)) * D;
-      qf[nt][ks] = as_bf16x8(ldg16_if(node < n_q, qrow + ks * 32 + kg * 8));
+    for (int e = 0; e < 16; ++e) best[nr][e] = 0.f;
+
+  if (j0 < cmax) {
+    // B operand: block j0 + r32, d = 16*ds + 8*hl .. = piece 2*ds + hl. The
+    // table is padded to whole tiles, so every load is in bounds.
+    bf16x8 kf[kKpb][DS];
+#pragma unroll
+    for (int m = 0; m < kKpb; ++m)
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds)
+        kf[m][ds] = as_bf16x8(ldg16(kbar + kbar_off<D>(bg, m, 2 * ds + hl, j0 + r32, nblk)));
+    // A operand: row row0 + 32*nr + r32 -> (node, head), same k-slots.
+    bf16x8 qa[NR][DS];
+#pragma unroll
+    for (int nr = 0; nr < NR; ++nr) {
+      const int row = row0 + 32 * nr + r32;
+      const int node = row / G;
+      const bool ok = node < n_q;
+      const uint16_t* qrow =
+          q + ((int64_t(b) * Hq + g * G + row % G) * n_q + (ok ? node : 0)) * D + 8 * hl;
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) qa[nr][ds] = as_bf16x8(ldg16_if(ok, qrow + 16 * ds));
     }
-  }
-
-  const int64_t jrow = j0 + r16;  // block row this lane feeds into the A operand
-  const bool row_ok = jrow < nblk;
-  // A fragment row: block jrow; k-slots 8*kg .. of d step ks = piece 4*ks + kg
-  const int64_t jr = row_ok ? jrow : 0;
-
-  f32x4 best[NT];
 #pragma unroll
-  for (int m = 0; m < kKpb; ++m) {
-    bf16x8 af[KS];
+    for (int m = 0; m < kKpb; ++m)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      af[ks] = as_bf16x8(ldg16_if(row_ok, kbar + kbar_off<D>(bg, m, 4 * ks + kg, jr, nblk)));
+      for (int nr = 0; nr < NR; ++nr) {
+        f32x16 acc;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma16(af[ks], qf[nt][ks], acc);
-      if (m == 0) {
-        best[nt] = acc;
-      } else {
+        for (int ds = 0; ds < DS; ++ds) acc = mfma32(qa[nr][ds], kf[m][ds], acc);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) best[nt][i] = fmaxf(best[nt][i], acc[i]);
+        for (int e = 0; e < 16; ++e) best[nr][e] = m == 0 ? acc[e] : fmaxf(best[nr][e], acc[e]);
       }
-    }
   }
 
-  // Sum over the G heads of each node: G adjacent lanes (aligned groups).
+  // Register r of lane l holds row row0 + 32*nr + 8*(r/4) + 4*hl + r%4 and
+  // block j0 + r32.
+  const int64_t j = j0 + r32;
+  auto store = [&](int row, float v) {
+    const int node = row / G;
+    if (node >= n_q || j >= nblk) return;
+    const int64_t C = (is_tree ? q_pos0 : q_pos0 + node) / kBlock;
+    scores[(int64_t(bg) * n_q + node) * nblk + j] = j < C ? v : -INFINITY;
+  };
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
+  for (int nr = 0; nr < NR; ++nr) {
+    const int rbase = row0 + 32 * nr + 4 * hl;
+    if constexpr (G <= 4) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = best[nt][i];
-      for (int o = 1; o < G; o <<= 1) v += __shfl_xor(v, o);
-      best[nt][i] = v;
-    }
-    const int c = col0 + nt * 16 + r16;
-    const int node = c / G;
-    if (c % G == 0 && node < n_q) {
-      const int64_t pos = is_tree ? q_pos0 : q_pos0 + node;
-      const int64_t C = pos / kBlock;
-      float* dst = scores + ((int64_t(bg) * n_q + node) * nblk);
+      for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t j = j0 + kg * 4 + i;
-        if (j < nblk) dst[j] = j < C ? best[nt][i] : -INFINITY;
+        for (int u = 0; u < 4 / G; ++u) {
+          float v = 0.f;
+#pragma unroll
+          for (int h = 0; h < G; ++h) v += best[nr][4 * a + G * u + h];
+          store(rbase + 8 * a + G * u, v);
+        }
+    } else {
+      constexpr int NQ = G / 8;  // register quads per node in each lane half
+#pragma unroll
+      for (int a0 = 0; a0 < 4 / NQ; ++a0) {
+        float v = 0.f;
+#pragma unroll
+        for (int a = a0 * NQ; a < a0 * NQ + NQ; ++a)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v += best[nr][4 * a + i];
+        v += __shfl_xor(v, 32);
+        if (hl == 0) store(rbase + 8 * a0 * NQ, v);
       }
     }
   }
@@ -101,20 +123,20 @@ __global__ __launch_bounds__(64) void score_kernel(const uint16_t* __restrict__ 
 
 hipError_t launch_scores(const Dims& d, const uint16_t* q, int n_q, int64_t q_pos0, int is_tree,
                          const uint16_t* kbar, int64_t nblk, float* scores, hipStream_t s) {
-  const int cols = n_q * d.G;
-  const int NT = (cols + 15) / 16;
-  const int ntile = int((nblk + 15) / 16);
-  const unsigned ycols = unsigned((NT + 3) / 4);  // column groups of 64 when NT > 4
-  const dim3 grid(unsigned(int64_t(d.B) * d.Hkv * ntile), NT > 4 ? ycols : 1u);
-  const int NTk = NT > 4 ? 4 : NT;
-#define SCORE_CASE(DD, NN)                                                                       \
-  if (d.D == DD && NTk <= NN) {                                                                   \
-    score_kernel<DD, NN><<<grid, 64, 0, s>>>(q, kbar, scores, d.Hq, d.Hkv, d.G, n_q, q_pos0,    \
-                                             is_tree, nblk, ntile);                              \
+  const int rows = n_q * d.G;
+  const int NR = rows > 32 ? 2 : 1;
+  const int ntile = int((nblk + 31) / 32);
+  const dim3 grid(unsigned(int64_t(d.B) * d.Hkv * ntile), unsigned((rows + 32 * NR - 1) / (32 * NR)));
+#define SCORE_CASE(DD, GG, NN)                                                                   \
+  if (d.D == DD && d.G == GG && NR == NN) {                                                      \
+    score_kernel<DD, GG, NN><<<grid, 64, 0, s>>>(q, kbar, scores, d.Hq, d.Hkv, n_q, q_pos0,      \
+                                                 is_tree, nblk, ntile);                          \
     return hipGetLastError();                                                                    \
   }
-  SCORE_CASE(128, 1) SCORE_CASE(128, 2) SCORE_CASE(128, 4)
-  SCORE_CASE(64, 1) SCORE_CASE(64, 2) SCORE_CASE(64, 4)
+#define SCORE_G(DD, GG) SCORE_CASE(DD, GG, 1) SCORE_CASE(DD, GG, 2)
+  SCORE_G(128, 1) SCORE_G(128, 2) SCORE_G(128, 4) SCORE_G(128, 8) SCORE_G(128, 16)
+  SCORE_G(64, 1) SCORE_G(64, 2) SCORE_G(64, 4) SCORE_G(64, 8) SCORE_G(64, 16)
+#undef SCORE_G
 #undef SCORE_CASE
   return hipErrorInvalidValue;
 }

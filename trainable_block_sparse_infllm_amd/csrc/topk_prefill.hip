@@ -27,11 +27,6 @@ namespace infllmv2 {
 namespace {
 
 constexpr int kDK = 128;
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 __device__ __forceinline__ f32x16 max16(const f32x16& a, const f32x16& b) {
   f32x16 r;

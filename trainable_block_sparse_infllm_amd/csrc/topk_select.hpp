@@ -8,12 +8,12 @@
 // Rows are written ascending and padded with -1.
 //
 // One wavefront selects one row whose n <= 64*KPL candidates sit in registers
-// (candidate j in lane j % 64, slot j / 64). The K-th largest score key T is
-// found bit by bit from the most significant end, each step counting the keys
-// >= a trial value with ballots (after a prefilter that usually leaves one
-// candidate per lane); the row is then emitted in index order with
-// ballot/mbcnt compaction, taking every key > T and the first K - #(> T) keys
-// equal to T. All decisions are integer comparisons on order-preserving score
+// (wave_topk: candidate j in lane j % 64, slot j / 64; wave_topk_lc: candidate
+// j in lane j / KPL, slot j % KPL, so lane order is index order). A prefilter
+// usually leaves one candidate per lane; the K-th largest key T among them is
+// read off a bitonic sort (or, after heavy ties, found bit by bit from the
+// most significant end over all keys), and the row is emitted in index order,
+// taking every key > T and the first K - #(> T) keys equal to T. All decisions are integer comparisons on order-preserving score
 // keys, so the choice is exact for the given scores.
 #pragma once
 
@@ -156,6 +156,261 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[KPL], int n, int
   }
   const uint32_t T = kth_largest<KPL>(key, K);
   emit_topk<KPL>(key, T, K, out, [](int r, int ln) { return r * kWave + ln; });
+}
+
+// Inclusive prefix sum over the wavefront's lanes.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int l) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t t = uint32_t(__shfl_up(int(v), o));
+    if (l >= o) v += t;
+  }
+  return v;
+}
+
+// K-th largest (with multiplicity, 1 <= K <= 64) of one fp32 value per lane
+// (no NaNs): the same bitonic network on floats, so -0 and +0 compare equal.
+template <int KS, int J>
+__device__ __forceinline__ float bitonic_step_f(float v, int l) {
+  const float p = __uint_as_float(xor_lane<J>(__float_as_uint(v), l));
+  const bool lower = (l & J) == 0;
+  const bool desc = (l & KS) == 0;
+  return lower == desc ? fmaxf(v, p) : fminf(v, p);
+}
+
+__device__ __forceinline__ float kth_largest_lanes_f(float v, int K) {
+  const int l = lane_id();
+  v = bitonic_step_f<2, 1>(v, l);
+  v = bitonic_step_f<4, 2>(v, l);  v = bitonic_step_f<4, 1>(v, l);
+  v = bitonic_step_f<8, 4>(v, l);  v = bitonic_step_f<8, 2>(v, l);  v = bitonic_step_f<8, 1>(v, l);
+  v = bitonic_step_f<16, 8>(v, l); v = bitonic_step_f<16, 4>(v, l); v = bitonic_step_f<16, 2>(v, l);
+  v = bitonic_step_f<16, 1>(v, l);
+  v = bitonic_step_f<32, 16>(v, l); v = bitonic_step_f<32, 8>(v, l); v = bitonic_step_f<32, 4>(v, l);
+  v = bitonic_step_f<32, 2>(v, l);  v = bitonic_step_f<32, 1>(v, l);
+  v = bitonic_step_f<64, 32>(v, l); v = bitonic_step_f<64, 16>(v, l); v = bitonic_step_f<64, 8>(v, l);
+  v = bitonic_step_f<64, 4>(v, l);  v = bitonic_step_f<64, 2>(v, l);  v = bitonic_step_f<64, 1>(v, l);
+  return __uint_as_float(uint32_t(__builtin_amdgcn_readlane(int(__float_as_uint(v)), K - 1)));
+}
+
+// Top-K of one row of fp32 scores, lane-contiguous layout: candidate j in lane
+// j / KPL, slot j % KPL. Slots j >= n may hold anything (they are never
+// chosen); values must not be NaN. Same rule and output as wave_topk;
+// `scratch` is 64 (value, index) pairs of LDS private to the wavefront.
+//
+// Prefilter: T0 = K-th largest of the per-lane maxima. If no slot past n took
+// part, at least K candidates are >= T0, so the answer lies among the values
+// >= T0 (usually a few dozen). They are counted per lane and written, in index
+// order, at offsets from a prefix sum over lanes: one ballot-free pass over the
+// slots. The survivors then sit one per lane; those with j >= n are dropped,
+// and if K candidates remain, T is read off their bitonic sort. Otherwise
+// (more than 64 survivors after heavy ties, or slots past n that raised T0)
+// the exact search runs over all candidates.
+template <int KPL>
+__device__ __forceinline__ void wave_topk_lc(const float (&val)[KPL], int n, int K,
+                                             int32_t* __restrict__ out, uint32_t* scratch) {
+  const int l = lane_id();
+  if (n <= K) {
+    for (int t = l; t < K; t += kWave) out[t] = t < n ? t : -1;
+    return;
+  }
+  if (K <= kWave) {
+    float mx = val[0];
+#pragma unroll
+    for (int r = 1; r < KPL; ++r) mx = fmaxf(mx, val[r]);
+    const float T0 = kth_largest_lanes_f(mx, K);
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int r = 0; r < KPL; ++r) cnt += val[r] >= T0 ? 1u : 0u;
+    const uint32_t incl = wave_incl_scan(cnt, l);
+    const uint32_t total = uint32_t(__builtin_amdgcn_readlane(int(incl), kWave - 1));
+    if (total <= uint32_t(kWave)) {
+      uint32_t pos = incl - cnt;
+#pragma unroll
+      for (int r = 0; r < KPL; ++r) {
+        if (val[r] >= T0) {
+          scratch[2 * pos] = __float_as_uint(val[r]);
+          scratch[2 * pos + 1] = uint32_t(l * KPL + r);
+          ++pos;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      const int32_t cj = uint32_t(l) < total ? int32_t(scratch[2 * l + 1]) : -1;
+      const bool ok = cj >= 0 && cj < n;
+      const float cv = ok ? __uint_as_float(scratch[2 * l]) : -INFINITY;
+      __builtin_amdgcn_wave_barrier();
+      if (popc64(ballot64(ok)) >= uint32_t(K)) {
+        const float T = kth_largest_lanes_f(cv, K);
+        const uint32_t ngt = popc64(ballot64(ok && cv > T));
+        const uint64_t eqm = ballot64(ok && cv == T);
+        const bool take = ok && (cv > T || (cv == T && ngt + mbcnt64(eqm) < uint32_t(K)));
+        const uint64_t tm = ballot64(take);
+        if (take) out[mbcnt64(tm)] = cj;
+        return;
+      }
+    }
+  }
+  // Exact search over all candidates on order-preserving keys: every key > T,
+  // then the first K - #(> T) keys equal to T in index order (lower lanes
+  // first, then lower slots).
+  uint32_t key[KPL];
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) key[r] = l * KPL + r < n ? ordered_key(val[r]) : 0u;
+  const uint32_t T = kth_largest<KPL>(key, K);
+  uint32_t ngt = 0, neq = 0;
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) {
+    ngt += key[r] > T ? 1u : 0u;
+    neq += key[r] == T ? 1u : 0u;
+  }
+  const uint32_t ngt_all = uint32_t(__builtin_amdgcn_readlane(int(wave_incl_scan(ngt, l)), kWave - 1));
+  const uint32_t take_eq = uint32_t(K) - ngt_all;
+  const uint32_t eq_before = wave_incl_scan(neq, l) - neq;
+  const uint32_t eq_here = eq_before >= take_eq ? 0u : min(neq, take_eq - eq_before);
+  const uint32_t taken = ngt + eq_here;
+  uint32_t pos = wave_incl_scan(taken, l) - taken, eq_used = 0;
+#pragma unroll
+  for (int r = 0; r < KPL; ++r) {
+    const bool eq = key[r] == T;
+    if (key[r] > T || (eq && eq_used < eq_here)) out[pos++] = l * KPL + r;
+    eq_used += eq ? 1u : 0u;
+  }
+}
+
+// Inclusive prefix sum over the wavefront's lanes with DPP: row shifts build
+// the sums inside each 16-lane row, then the row broadcasts carry row totals.
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v) {
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x111, 0xF, 0xF, true));   // row_shr:1
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x112, 0xF, 0xF, true));   // row_shr:2
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x114, 0xF, 0xF, true));   // row_shr:4
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x118, 0xF, 0xF, true));   // row_shr:8
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return v;
+}
+
+// LDS of the workgroup selection below.
+struct WgTopkLds {
+  uint32_t gmax[kWave];     // maxima of the 64 candidate groups (keys)
+  uint32_t wtot[8];         // survivors per wavefront
+  uint32_t lk[kWave];       // survivors: key, candidate index (index order)
+  int32_t lj[kWave];
+};
+
+// Top-K of one row of fp32 scores by the 8 first wavefronts of a workgroup;
+// every wavefront of the workgroup must call it (it holds workgroup
+// barriers). Candidate j = (64*w + l)*S + s sits in wavefront w, lane l, slot
+// s, S = SKPL/8 (so a 64*SKPL-candidate row is spread over 8*64 lanes in index
+// order). Same rule, prefilter and fallback as wave_topk_lc: the groups are
+// the 64 runs of SKPL consecutive candidates (8 lanes of one wavefront), so
+// the bound T0 and the survivors are those of the one-wavefront version; the
+// slot work, the group maxima and the survivor counts are split 8 ways.
+// `row` holds the scores (j < nblk readable; slots past n may hold anything);
+// `vec`: rows are 16-byte aligned. Wavefront 0 writes out[0 .. K-1]; the
+// caller synchronizes the workgroup before reading it.
+template <int SKPL>
+__device__ __forceinline__ void wg_topk8(const float* __restrict__ row, int64_t nblk, bool vec,
+                                         int n, int K, int32_t* __restrict__ out,
+                                         uint32_t* scratch, WgTopkLds& sh) {
+  static_assert(SKPL >= 8, "eight wavefronts need at least one slot each");
+  constexpr int S = SKPL / 8;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int l = lane_id();
+  const bool part = w < 8;
+  const int j0 = (w * kWave + l) * S;
+  if (n <= K) {                          // every candidate is taken
+    if (w == 0)
+      for (int t = l; t < K; t += kWave) out[t] = t < n ? t : -1;
+    return;
+  }
+  uint32_t key[S];
+  if (part) {
+    float val[S];
+    bool done = false;
+    if constexpr (S >= 4) {
+      if (vec) {
+#pragma unroll
+        for (int s = 0; s < S; s += 4) {
+          const int j = j0 + s;
+          const uint4 u = ldg16_or_neginf(j < nblk, row + (j < nblk ? j : 0));
+          val[s] = __uint_as_float(u.x);
+          val[s + 1] = __uint_as_float(u.y);
+          val[s + 2] = __uint_as_float(u.z);
+          val[s + 3] = __uint_as_float(u.w);
+        }
+        done = true;
+      }
+    }
+    if (!done) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) val[s] = ldf_or_neginf(j0 + s < nblk, row + j0 + s);
+    }
+    uint32_t mx = 0u;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      key[s] = ordered_key(val[s]);
+      mx = max(mx, key[s]);
+    }
+    mx = max(mx, xor_lane<1>(mx, l));
+    mx = max(mx, xor_lane<2>(mx, l));
+    mx = max(mx, xor_lane<4>(mx, l));
+    if ((l & 7) == 0) sh.gmax[w * 8 + l / 8] = mx;
+  }
+  lds_barrier();
+  uint32_t mask = 0u, excl = 0u;
+  if (part && K <= kWave) {
+    const uint32_t T0 = kth_largest_lanes(sh.gmax[l], K);
+#pragma unroll
+    for (int s = 0; s < S; ++s) mask |= (key[s] >= T0 ? 1u : 0u) << s;
+    const uint32_t cnt = __popc(mask);
+    const uint32_t incl = wave_incl_scan_dpp(cnt);
+    excl = incl - cnt;
+    if (l == kWave - 1) sh.wtot[w] = incl;
+  }
+  lds_barrier();
+  uint32_t total = ~0u;
+  if (part && K <= kWave) {
+    uint32_t base = 0u;
+    total = 0u;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const uint32_t t = sh.wtot[v];
+      base += v < w ? t : 0u;
+      total += t;
+    }
+    if (total <= uint32_t(kWave)) {
+      uint32_t pos = base + excl;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        if ((mask >> s) & 1u) {
+          sh.lk[pos] = key[s];
+          sh.lj[pos] = j0 + s;
+          ++pos;
+        }
+      }
+    }
+  }
+  lds_barrier();
+  if (w != 0) return;
+  if (total <= uint32_t(kWave)) {
+    const int32_t cj = uint32_t(l) < total ? sh.lj[l] : -1;
+    const bool ok = cj >= 0 && cj < n;
+    const uint32_t ck = ok ? sh.lk[l] : 0u;
+    if (popc64(ballot64(ok)) >= uint32_t(K)) {
+      const uint32_t T = kth_largest_lanes(ck, K);
+      const uint32_t ngt = popc64(ballot64(ok && ck > T));
+      const uint64_t eqm = ballot64(ok && ck == T);
+      const bool take = ok && (ck > T || (ck == T && ngt + mbcnt64(eqm) < uint32_t(K)));
+      const uint64_t tm = ballot64(take);
+      if (take) out[mbcnt64(tm)] = cj;
+      return;
+    }
+  }
+  // Heavy ties, or slots past n that raised T0: wavefront 0 takes the whole
+  // row (lane-contiguous) and runs the one-wavefront selection.
+  float all[SKPL];
+#pragma unroll
+  for (int r = 0; r < SKPL; ++r) all[r] = ldf_or_neginf(l * SKPL + r < nblk, row + l * SKPL + r);
+  wave_topk_lc<SKPL>(all, n, K, out, scratch);
 }
 
 }  // namespace infllmv2

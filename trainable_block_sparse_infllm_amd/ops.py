@@ -34,8 +34,9 @@ class Workspace:
 
 
 def kbar_shape(B: int, Hkv: int, kv_cap: int, D: int) -> tuple:
-    """Kernel table [B][Hkv][3][D/8][nblk][8]: 16-byte pieces of consecutive blocks adjacent."""
-    return (B, Hkv, 3, D // 8, nblk(kv_cap), 8)
+    """Kernel table [B][Hkv][ceil(nblk/32)][3][D/8][32][8]: tiles of 32 blocks, and inside
+    a tile the 32 blocks' copies of each 16-byte piece adjacent."""
+    return (B, Hkv, (nblk(kv_cap) + 31) // 32, 3, D // 8, 32, 8)
 
 
 def pool_kernels(cfg, k, kv_cap, kv_len, first_block=0, kbar=None, stream=None):
