@@ -305,6 +305,39 @@ def test_decode_from_scores_128k_batch8_full_size():
     _decode_scores_matches_split_path(W["decode_128k_b8"])
 
 
+@pytest.mark.parametrize("B,Hkv,kv_len,kv_cap", [(8, 8, 131072, 131072),      # eight-wavefront selection
+                                                (2, 4, 65636, 65636),          # one-wavefront selection
+                                                (1, 8, 64 * 1026 + 5, 64 * 1027)])  # rows not 16-byte aligned
+def test_decode_selection_from_scores_exact(B, Hkv, kv_len, kv_cap):
+    """Selection inside the decode kernel equals the oracle's rule on hand-made
+    fp32 scores: quantized values (many exact ties), -0 and +0 mixed (equal as
+    fp32), one row of all-equal scores (the exact fallback), and garbage past
+    the candidates (ignored)."""
+    rng = np.random.default_rng(11)
+    K, D, G = 32, 128, 4
+    nblk = ops.nblk(kv_cap)
+    C = (kv_len - 1) // 64
+    R = (np.round(rng.standard_normal((B * Hkv, nblk)) * 4) / 4).astype(np.float32)
+    zeros = R == 0
+    R[zeros] = np.where(rng.random(np.count_nonzero(zeros)) < 0.5, np.float32(-0.0), np.float32(0.0))
+    R[0, :] = 0.5
+    ref = orc.select(np.where(np.arange(nblk) < C, R, -np.inf).astype(np.float64), np.full(B * Hkv, C), K)
+    R[:, C:] = 1e30
+    cfg = lib.make_cfg(B, Hkv * G, Hkv, D, top_k=K)
+    note(f"decode selection: B{B} Hkv{Hkv} kv_len {kv_len} nblk {nblk}")
+    q = torch.randn((B, Hkv * G, 1, D), device="cuda").to(torch.bfloat16)
+    k = torch.randn((B, Hkv, kv_cap, D), device="cuda").to(torch.bfloat16)
+    v = torch.randn((B, Hkv, kv_cap, D), device="cuda").to(torch.bfloat16)
+    scores = torch.from_numpy(R).cuda()
+    idx = torch.full((B, Hkv, 1, K), -7, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    nbytes = lib.infllmv2_decode_workspace_bytes(cfg, 1, kv_len)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    lib.infllmv2_sparse_attn_decode_scores(cfg, q, k, v, kv_cap, kv_len, scores, idx, out, None, ws, nbytes)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy().reshape(-1, K), ref)
+
+
 def test_multi_token_decode_without_tree():
     run_decode(TREE_CASES["p1000_n7_d64"].scaled(name="mt_rows", seq_len=1020), tree=False)
 
