@@ -75,18 +75,25 @@ struct PrefillShape {
 // loads chunks w, w + NW, ... Lane l's 16 bytes land in slot l % 16 of row
 // 4c + l / 16, so it fetches the global piece stored in that slot. Rows past
 // kv_len repeat row kv_len - 1 (finite data; their scores are masked).
+//
+// A full block reads from a block base that is the same for the whole
+// wavefront plus a per-lane 32-bit byte offset, so the loads take the
+// scalar-base form without 64-bit address arithmetic per lane. The lane part
+// of chunk c depends on c % 4 only: row 4*(c%16) + l/16 has swizzle
+// ((4*(c%2) + l/16) << 1) | ((c/2) % 2); `lane_off[c % 4]` holds it.
 template <int NW>
 __device__ __forceinline__ void issue_stage(char* stage, const uint16_t* kbase,
                                            const uint16_t* vbase, int64_t key0, int64_t kv_len,
-                                           int w, int l) {
+                                           int w, int l, const uint32_t (&lane_off)[4]) {
   constexpr int LPS = 32 / NW;
   if (key0 + kBlock <= kv_len) {
+    const char* kb = reinterpret_cast<const char*>(kbase + key0 * kD);
+    const char* vb = reinterpret_cast<const char*>(vbase + key0 * kD);
 #pragma unroll
     for (int x = 0; x < LPS; ++x) {
       const int c = x * NW + w;
-      const int row = 4 * (c % 16) + l / 16;
-      const uint16_t* src = (c < 16 ? kbase : vbase) + key0 * kD;
-      load_lds16(src + row * kD + ((l % 16) ^ swz(row)) * 8, stage + c * 1024);
+      const char* src = (c < 16 ? kb : vb) + (c % 16) * 1024;
+      load_lds16(src + lane_off[c % 4], stage + c * 1024);
     }
   } else {
 #pragma unroll
@@ -158,16 +165,12 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Max / sum over lanes l and l ^ 32 (the two halves of a 32-row MFMA column).
+// Max over lanes l and l ^ 32 (the two halves of a 32-row MFMA column).
 __device__ __forceinline__ float halves_max(float x) {
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-__device__ __forceinline__ float halves_sum(float x) {
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
 
 }  // namespace
 
@@ -191,6 +194,7 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(u_blk + umax);                 // [256]
   int32_t* wbase = reinterpret_cast<int32_t*>(bitmap + 256);                    // [256]
   int32_t* wtot = wbase + 256;                                                  // [NW]
+  int32_t* jsel = wtot + 16;                                                    // [TQ * K]
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -243,9 +247,15 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
     __syncthreads();
     for (int e = tid; e < ntok * K; e += NT) {
       const int t = e / K;
-      if (t < dend) continue;
-      const int j = idx[(int64_t(bg) * n_q + tok0 + t) * K + e % K];
-      if (j >= 0 && j < (base + t) / kBlock) atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+      int j = -1;
+      if (t >= dend) {
+        j = idx[(int64_t(bg) * n_q + tok0 + t) * K + e % K];
+        if (j >= 0 && j < (base + t) / kBlock)
+          atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+        else
+          j = -1;
+      }
+      jsel[e] = j;
     }
     __syncthreads();
     // exclusive prefix of the words' popcounts (thread t owns words t*WPT ..),
@@ -290,9 +300,8 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
     __syncthreads();
     for (int e = tid; e < ntok * K; e += NT) {
       const int t = e / K;
-      if (t < dend) continue;
-      const int j = idx[(int64_t(bg) * n_q + tok0 + t) * K + e % K];
-      if (j >= 0 && j < (base + t) / kBlock) {
+      const int j = jsel[e];
+      if (j >= 0) {
         const int u = wbase[j >> 5] + __popc(bitmap[j >> 5] & ((1u << (j & 31)) - 1u));
         if (u < umax) atomicOr(reinterpret_cast<unsigned long long*>(&u_mask[u]), 1ull << t);
       }
@@ -303,17 +312,39 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
   auto blk_of = [&](int u) -> int64_t {
     return tile_dense ? int64_t(u) : int64_t(__builtin_amdgcn_readfirstlane(lds_read(u_blk + u)));
   };
+  // Raw LDS reads of an entry's block / token mask, issued one iteration
+  // ahead so that their latency overlaps the stage wait; made uniform at use.
+  auto blk_raw = [&](int u) -> int32_t { return tile_dense ? u : lds_read(u_blk + u); };
+  auto mask_raw = [&](int u) -> uint64_t {
+    return tile_dense ? range_mask(u) : lds_read(u_mask + u);
+  };
 
   // ---------------------------------------------------------------- ring prologue
+  uint32_t lane_off[4];
+#pragma unroll
+  for (int c4 = 0; c4 < 4; ++c4) {
+    const int row = 4 * c4 + l / 16;            // row % 16 of chunk c = row of chunk c % 4
+    lane_off[c4] = uint32_t((l / 16) * (kD * 2) + (((l % 16) ^ swz(row)) << 4));
+  }
   for (int p = 0; p < nstage - 1 && p < U; ++p)
-    issue_stage<NW>(ring + p * kStageBytes, kbase, vbase, blk_of(p) * kBlock, kv_len, w, l);
+    issue_stage<NW>(ring + p * kStageBytes, kbase, vbase, blk_of(p) * kBlock, kv_len, w, l, lane_off);
 
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  // Row sums of P come from the MFMA as well: O^T's product with an all-ones
+  // A operand puts every row's sum of the bf16 P in each accumulator register
+  // (register 0 is read). It takes four MFMAs per block off the VALU, which
+  // bounds this loop.
+  f32x16 lacc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) lacc[e] = 0.f;
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = __bf16(1.0f);
+  float m_run = -INFINITY;
   const int64_t row_p = base + w * TPS + r32 / G;      // this lane's row position
   const int64_t p_first = base + w * TPS;              // the wavefront's first token
 
@@ -336,32 +367,56 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
   // ---------------------------------------------------------------- 2/3. ring + compute
   int cur = 0;                                    // ring slot of entry u
   int nxt = nstage - 1;                           // ring slot of entry u + nstage - 1
+  int32_t blk_nx = U > 0 ? blk_raw(0) : 0;         // entry u's block and mask
+  uint64_t mask_nx = U > 0 ? mask_raw(0) : 0ull;
   for (int u = 0; u < U; ++u) {
+    const int32_t blk_cur = blk_nx;
+    const uint64_t mask_cur = mask_nx;
+    const int32_t blk_iss = u + nstage - 1 < U ? blk_raw(u + nstage - 1) : 0;
+    if (u + 1 < U) {
+      blk_nx = blk_raw(u + 1);
+      mask_nx = mask_raw(u + 1);
+    }
     wait_stages_pending<LPS>(min(nstage - 2, U - 1 - u));
     wait_lds();
     ring_barrier();                               // entry u landed for every wave; slot nxt is free
     if (u + nstage - 1 < U)
-      issue_stage<NW>(ring + nxt * kStageBytes, kbase, vbase, blk_of(u + nstage - 1) * kBlock,
-                      kv_len, w, l);
+      issue_stage<NW>(ring + nxt * kStageBytes, kbase, vbase,
+                      int64_t(__builtin_amdgcn_readfirstlane(blk_iss)) * kBlock, kv_len, w, l,
+                      lane_off);
     const char* kt_b = ring + cur * kStageBytes;
     const lds_char* vt_b = (const lds_char*)(ring + cur * kStageBytes + kTileBytes);
     cur = cur + 1 == nstage ? 0 : cur + 1;
     nxt = nxt + 1 == nstage ? 0 : nxt + 1;
-    const int64_t key0 = blk_of(u) * kBlock;
-    const uint64_t tmask = tile_dense ? range_mask(key0 / kBlock) : uniform_u64(lds_read(u_mask + u));
+    const int64_t key0 = int64_t(__builtin_amdgcn_readfirstlane(blk_cur)) * kBlock;
+    const uint64_t tmask = uniform_u64(mask_cur);
     const uint32_t bits = uint32_t(tmask >> (w * TPS)) & uint32_t((1ull << TPS) - 1ull);
     if (bits == 0) continue;                      // no token of this wavefront needs the block
 
     // S^T = K Q^T: two 32-key tiles. Accumulator register r of lane l holds
     // key 32*kt + 8*(r/4) + 4*hl + r%4 of row r32.
     f32x16 sacc[2];
+    {
+      bf16x8 kf[2][DS];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[kt][e] = 0.f;
+        for (int ds = 0; ds < DS; ++ds) kf[kt][ds] = lds_read_k(kt_b + kt * 8192, k_lane ^ (ds << 5));
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds)
-        sacc[kt] = mfma32(lds_read_k(kt_b + kt * 8192, k_lane ^ (ds << 5)), qf[ds], sacc[kt]);
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[kt][e] = 0.f;
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) sacc[kt] = mfma32(kf[kt][ds], qf[ds], sacc[kt]);
+      }
+      // K fragment reads run four ahead of the MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
 
     // Masked online softmax in the exp2 domain. A row whose token does not
@@ -392,7 +447,7 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
       const float m_new = mb * scale_log2;
       const float alpha = grow ? exp2f(m_run - m_new) : 1.f;   // 0 on a row's first block
       if (grow) m_run = m_new;
-      l_run *= alpha;
+      lacc[0] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -400,7 +455,6 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
     }
     // exp2 argument <= kRescale; results below 2^-126 flush to zero
     const float bias = !row_on ? -INFINITY : (m_run == -INFINITY ? 0.f : -m_run);
-    float ps = 0.f;
     // P^T as the B operand of k-step ks (keys 16*ks ..): k-slot jj of lane
     // half hl holds key 16*ks + 8*(jj/4) + 4*hl + jj%4, i.e. accumulator
     // registers 8*(ks%2) .. 8*(ks%2)+7 of sacc[ks/2].
@@ -411,7 +465,6 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         pv[jj] = __builtin_amdgcn_exp2f(fmaf(sacc[ks / 2][8 * (ks % 2) + jj], scale_log2, bias));
-        ps += pv[jj];
       }
       uint4 uu;
       uu.x = cvt_pk_bf16(pv[0], pv[1]);
@@ -420,23 +473,39 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
       uu.w = cvt_pk_bf16(pv[6], pv[7]);
       pf[ks] = as_bf16x8(uu);
     }
-    l_run += halves_sum(ps);
 
     // O^T += V^T P^T. In a transpose read each 16-lane group returns, to lane
     // j, element j%4 of the 8-byte chunks addressed by lanes j/4 + 4*i
     // (i = 0..3); with lane k pointing at V[kb + k/4][d0 + 4*(k%4)], lane j
     // receives V^T entries (d0 + j, keys kb .. kb+3), matching P^T's k-slots.
+    {
+      bf16x8 vfr[DT][4];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 vf = lds_read_vt(vt_b + ks * 4096, v_lane[0] ^ (dt << 6), v_lane[1] ^ (dt << 6));
-        oacc[dt] = mfma32(vf, pf[ks], oacc[dt]);
+        for (int ks = 0; ks < 4; ++ks)
+          vfr[dt][ks] = lds_read_vt(vt_b + ks * 4096, v_lane[0] ^ (dt << 6), v_lane[1] ^ (dt << 6));
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) lacc = mfma32(ones, pf[ks], lacc);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) oacc[dt] = mfma32(vfr[dt][ks], pf[ks], oacc[dt]);
+      // transpose reads run ahead of the MFMAs that use them
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
   }
 
   // ---------------------------------------------------------------- epilogue
   // oacc[dt] register r of lane l: d = 32*dt + 8*(r/4) + 4*hl + r%4 of row r32.
+  const float l_run = lacc[0];
   if (my_t < n_q) {
     const int h = g * G + r32 % G;
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
@@ -479,8 +548,8 @@ int64_t prefill_umax(const Dims& d, int mode, int64_t nb) {
   return std::min(nb, std::max(sparse, mixed));
 }
 
-size_t prefill_lds(int nstage, int64_t umax) {
-  return size_t(nstage) * kStageBytes + size_t(umax) * 12 + 512 * 4 + 64;
+size_t prefill_lds(int nstage, int64_t umax, int tq, int K) {
+  return size_t(nstage) * kStageBytes + size_t(umax) * 12 + 512 * 4 + 64 + size_t(tq) * K * 4;
 }
 
 }  // namespace
@@ -494,8 +563,8 @@ int prefill128_stages(const Dims& d, int mode, int64_t kv_len) {
   // SIMDs without sharing barriers, so one's MFMA work overlaps the other's
   // softmax and memory waits
   for (int ns = 4; ns >= 2; --ns)
-    if (prefill_lds(ns, umax) <= 80 * 1024) return ns;
-  return prefill_lds(2, umax) <= 160 * 1024 ? 2 : 0;
+    if (prefill_lds(ns, umax, prefill_tq(d.G), d.K) <= 80 * 1024) return ns;
+  return prefill_lds(2, umax, prefill_tq(d.G), d.K) <= 160 * 1024 ? 2 : 0;
 }
 
 template <int G>
@@ -515,7 +584,7 @@ static hipError_t launch_prefill_t(const Dims& d, int mode, const uint16_t* q, i
                                                      160 * 1024);
   if (attr != hipSuccess) return attr;
   const dim3 grid(unsigned(int64_t(d.B) * d.Hkv * ntile));
-  kern<<<grid, Sh::NT, prefill_lds(nstage, umax), s>>>(
+  kern<<<grid, Sh::NT, prefill_lds(nstage, umax, Sh::TQ, d.K), s>>>(
       q, k, v, idx, out, lse, d.Hq, d.Hkv, n_q, kv_cap, kv_len, d.K, d.dense_thr, mode,
       d.scale * 1.4426950408889634f, ntile, int(umax), nstage);
   return hipGetLastError();
