@@ -161,7 +161,9 @@ INFLLMV2_API int infllmv2_sparse_attn_decode(const infllmv2_cfg* cfg, const void
  * q_pos0 = kv_len - 1), by the rule of infllmv2_topk_blocks, then attends
  * them exactly as infllmv2_sparse_attn_decode with n_q = 1 and no tree mask.
  * The selection runs inside the attention kernel (each split of a group
- * repeats it) instead of in a kernel of its own.
+ * repeats it) instead of in a kernel of its own. Only entries j < (kv_len-1)/64
+ * of a score row are candidates; the rest of the row may hold any value
+ * (it is never chosen). Scores must not be NaN.
  *   idx_out: NULL, or [B][Hkv][1][K] int32 receiving the selected blocks.
  *   Requires top_k <= 64 and at most 4096 candidate blocks ((kv_len-1)/64),
  *   else INFLLMV2_UNSUPPORTED; workspace as for infllmv2_sparse_attn_decode
