@@ -73,52 +73,32 @@ struct PrefillShape {
 // Keys key0 .. key0+63 of K and V -> one LDS stage. The stage is 32 chunks of
 // 1 KB (chunk c < 16: K rows 4c..4c+3, else V rows 4(c-16)..); wavefront w
 // loads chunks w, w + NW, ... Lane l's 16 bytes land in slot l % 16 of row
-// 4c + l / 16, so it fetches the global piece stored in that slot. Rows past
-// kv_len repeat row kv_len - 1 (finite data; their scores are masked).
+// 4c + l / 16, so it fetches the global piece stored in that slot.
 //
-// A full block reads from a block base that is the same for the whole
-// wavefront plus a per-lane 32-bit byte offset, so the loads take the
-// scalar-base form without 64-bit address arithmetic per lane. The lane part
-// of chunk c depends on c % 4 only: row 4*(c%16) + l/16 has swizzle
-// ((4*(c%2) + l/16) << 1) | ((c/2) % 2); `lane_off[c % 4]` holds it.
-template <int NW>
-__device__ __forceinline__ void issue_stage(char* stage, const uint16_t* kbase,
-                                           const uint16_t* vbase, int64_t key0, int64_t kv_len,
-                                           int w, int l, const uint32_t (&lane_off)[4]) {
-  constexpr int LPS = 32 / NW;
-  if (key0 + kBlock <= kv_len) {
-    const char* kb = reinterpret_cast<const char*>(kbase + key0 * kD);
-    const char* vb = reinterpret_cast<const char*>(vbase + key0 * kD);
-#pragma unroll
-    for (int x = 0; x < LPS; ++x) {
-      const int c = x * NW + w;
-      const char* src = (c < 16 ? kb : vb) + (c % 16) * 1024;
-      load_lds16(src + lane_off[c % 4], stage + c * 1024);
-    }
-  } else {
-#pragma unroll
-    for (int x = 0; x < LPS; ++x) {
-      const int c = x * NW + w;
-      const int row = 4 * (c % 16) + l / 16;
-      const int64_t key = min(key0 + row, kv_len - 1);
-      const uint16_t* src = c < 16 ? kbase : vbase;
-      load_lds16(src + key * kD + ((l % 16) ^ swz(row)) * 8, stage + c * 1024);
-    }
-  }
+// The loads are buffer loads straight into LDS: the resource holds the
+// (b, g) base and bounds the rows at kv_len (rows past it read zeros: finite,
+// and their scores are masked; nothing past the tensor is touched), and a
+// load costs one 32-bit add (scalar block offset + per-lane offset). The lane
+// part of chunk c depends on c % 4 only: row 4*(c%16) + l/16 has swizzle
+// ((4*(c%2) + l/16) << 1) | ((c/2) % 2).
+__device__ __forceinline__ uint32_t stage_lane_off(int c4, int l) {
+  const int row = 4 * c4 + l / 16;
+  return uint32_t((l / 16) * (kD * 2) + (((l % 16) ^ swz(row)) << 4));
 }
 
-// s_waitcnt vmcnt(n), n = LPS * stages: stages complete in issue order, so an
-// entry has landed once only the stages issued after it are pending.
-template <int LPS>
-__device__ __forceinline__ void wait_stages_pending(int stages) {
-  // vmcnt field: bits 3:0 and 15:14; expcnt and lgkmcnt left at their maximum
-#define INFLLMV2_VMCNT(n) (0x0F70 | ((n) & 15) | ((((n) >> 4) & 3) << 14))
-  switch (stages) {
-    case 0: __builtin_amdgcn_s_waitcnt(INFLLMV2_VMCNT(0)); break;
-    case 1: __builtin_amdgcn_s_waitcnt(INFLLMV2_VMCNT(LPS)); break;
-    default: __builtin_amdgcn_s_waitcnt(INFLLMV2_VMCNT(2 * LPS)); break;
+template <int NW>
+__device__ __forceinline__ void issue_stage(char* stage, __amdgpu_buffer_rsrc_t rk,
+                                           __amdgpu_buffer_rsrc_t rv, int64_t key0, int w, int l) {
+  constexpr int LPS = 32 / NW;
+  const uint32_t blk_off = uint32_t(key0) * uint32_t(kD * 2);
+#pragma unroll
+  for (int x = 0; x < LPS; ++x) {
+    const int c = x * NW + w;
+    // the whole offset goes in the VGPR operand, which the range check covers
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c < 16 ? rk : rv, (las_void*)(stage + c * 1024), 16,
+                                             stage_lane_off(c % 4, l) + blk_off + (c % 16) * 1024,
+                                             0, 0, 0);
   }
-#undef INFLLMV2_VMCNT
 }
 
 // Bits lo .. hi-1 of a token mask, clamped to tokens 0 .. n-1 (n <= 64).
@@ -179,7 +159,7 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ out, float* __restrict__ lse, int Hq,
     int Hkv, int n_q, int64_t kv_cap, int64_t kv_len, int K, int dense_thr, int mode,
-    float scale_log2, int ntile, int umax, int nstage) {
+    float scale_log2, int ntile, int umax) {
   using Sh = PrefillShape<G>;
   constexpr int TPS = Sh::TPS, NW = Sh::NW, TQ = Sh::TQ, NT = Sh::NT, LPS = Sh::LPS;
   constexpr int WPT = (256 + NT - 1) / NT;   // bitmap words per thread
@@ -188,8 +168,8 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
   constexpr float kRescale = 8.f;            // log2 headroom before the running max is moved
 
   extern __shared__ __align__(16) char smem[];
-  char* ring = smem;                                                            // [nstage]
-  uint64_t* u_mask = reinterpret_cast<uint64_t*>(smem + nstage * kStageBytes);  // [umax]
+  char* ring = smem;                                                            // [2 stages]
+  uint64_t* u_mask = reinterpret_cast<uint64_t*>(smem + 2 * kStageBytes);      // [umax]
   int32_t* u_blk = reinterpret_cast<int32_t*>(u_mask + umax);                   // [umax]
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(u_blk + umax);                 // [256]
   int32_t* wbase = reinterpret_cast<int32_t*>(bitmap + 256);                    // [256]
@@ -320,14 +300,12 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
   };
 
   // ---------------------------------------------------------------- ring prologue
-  uint32_t lane_off[4];
-#pragma unroll
-  for (int c4 = 0; c4 < 4; ++c4) {
-    const int row = 4 * c4 + l / 16;            // row % 16 of chunk c = row of chunk c % 4
-    lane_off[c4] = uint32_t((l / 16) * (kD * 2) + (((l % 16) ^ swz(row)) << 4));
-  }
-  for (int p = 0; p < nstage - 1 && p < U; ++p)
-    issue_stage<NW>(ring + p * kStageBytes, kbase, vbase, blk_of(p) * kBlock, kv_len, w, l, lane_off);
+  const uint32_t nrec = uint32_t(kv_len) * uint32_t(kD * 2);   // bytes of rows < kv_len
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(kbase), 0, int(nrec), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(vbase), 0, int(nrec), 0x00020000);
+  if (U > 0) issue_stage<NW>(ring, rk, rv, blk_of(0) * kBlock, w, l);
 
   f32x16 oacc[DT];
 #pragma unroll
@@ -365,29 +343,27 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
   }
 
   // ---------------------------------------------------------------- 2/3. ring + compute
-  int cur = 0;                                    // ring slot of entry u
-  int nxt = nstage - 1;                           // ring slot of entry u + nstage - 1
+  // Two ring slots: entry u sits in slot u % 2; entry u + 1 is issued into
+  // the other slot once every wavefront has passed the barrier of entry u
+  // (so nobody still reads entry u - 1 there).
   int32_t blk_nx = U > 0 ? blk_raw(0) : 0;         // entry u's block and mask
   uint64_t mask_nx = U > 0 ? mask_raw(0) : 0ull;
   for (int u = 0; u < U; ++u) {
     const int32_t blk_cur = blk_nx;
     const uint64_t mask_cur = mask_nx;
-    const int32_t blk_iss = u + nstage - 1 < U ? blk_raw(u + nstage - 1) : 0;
     if (u + 1 < U) {
       blk_nx = blk_raw(u + 1);
       mask_nx = mask_raw(u + 1);
     }
-    wait_stages_pending<LPS>(min(nstage - 2, U - 1 - u));
+    wait_vmem();                                  // this wave's loads of entry u landed
     wait_lds();
-    ring_barrier();                               // entry u landed for every wave; slot nxt is free
-    if (u + nstage - 1 < U)
-      issue_stage<NW>(ring + nxt * kStageBytes, kbase, vbase,
-                      int64_t(__builtin_amdgcn_readfirstlane(blk_iss)) * kBlock, kv_len, w, l,
-                      lane_off);
-    const char* kt_b = ring + cur * kStageBytes;
-    const lds_char* vt_b = (const lds_char*)(ring + cur * kStageBytes + kTileBytes);
-    cur = cur + 1 == nstage ? 0 : cur + 1;
-    nxt = nxt + 1 == nstage ? 0 : nxt + 1;
+    ring_barrier();                               // ... and every wave's; the other slot is free
+    char* const slot = ring + (u & 1) * kStageBytes;
+    if (u + 1 < U)
+      issue_stage<NW>(ring + ((u + 1) & 1) * kStageBytes, rk, rv,
+                      int64_t(__builtin_amdgcn_readfirstlane(blk_nx)) * kBlock, w, l);
+    const char* kt_b = slot;
+    const lds_char* vt_b = (const lds_char*)(slot + kTileBytes);
     const int64_t key0 = int64_t(__builtin_amdgcn_readfirstlane(blk_cur)) * kBlock;
     const uint64_t tmask = uniform_u64(mask_cur);
     const uint32_t bits = uint32_t(tmask >> (w * TPS)) & uint32_t((1ull << TPS) - 1ull);
@@ -548,8 +524,8 @@ int64_t prefill_umax(const Dims& d, int mode, int64_t nb) {
   return std::min(nb, std::max(sparse, mixed));
 }
 
-size_t prefill_lds(int nstage, int64_t umax, int tq, int K) {
-  return size_t(nstage) * kStageBytes + size_t(umax) * 12 + 512 * 4 + 64 + size_t(tq) * K * 4;
+size_t prefill_lds(int64_t umax, int tq, int K) {
+  return size_t(2) * kStageBytes + size_t(umax) * 12 + 512 * 4 + 64 + size_t(tq) * K * 4;
 }
 
 }  // namespace
@@ -558,13 +534,12 @@ int prefill128_stages(const Dims& d, int mode, int64_t kv_len) {
   if (d.D != 128) return 0;
   const int64_t nb = (kv_len - 1) / kBlock + 1;
   if (nb > 256 * 32) return 0;
+  if (kv_len > int64_t(INT32_MAX) / (kD * 2)) return 0;   // 32-bit buffer offsets
+  // a two-stage ring; two workgroups per CU (80 KB of LDS each) when the
+  // union list fits, so the wavefronts sharing a SIMD are not tied by one
+  // barrier and one's MFMA work overlaps the other's softmax and waits
   const int64_t umax = prefill_umax(d, mode, nb);
-  // two workgroups per CU (80 KB of LDS each): their wavefronts share the
-  // SIMDs without sharing barriers, so one's MFMA work overlaps the other's
-  // softmax and memory waits
-  for (int ns = 4; ns >= 2; --ns)
-    if (prefill_lds(ns, umax, prefill_tq(d.G), d.K) <= 80 * 1024) return ns;
-  return prefill_lds(2, umax, prefill_tq(d.G), d.K) <= 160 * 1024 ? 2 : 0;
+  return prefill_lds(umax, prefill_tq(d.G), d.K) <= 160 * 1024 ? 2 : 0;
 }
 
 template <int G>
@@ -575,8 +550,7 @@ static hipError_t launch_prefill_t(const Dims& d, int mode, const uint16_t* q, i
   using Sh = PrefillShape<G>;
   const int ntile = (n_q + Sh::TQ - 1) / Sh::TQ;
   const int64_t nb = (kv_len - 1) / kBlock + 1;
-  const int nstage = prefill128_stages(d, mode, kv_len);
-  if (nstage == 0) return hipErrorInvalidValue;
+  if (prefill128_stages(d, mode, kv_len) == 0) return hipErrorInvalidValue;
   const int64_t umax = prefill_umax(d, mode, nb);
   auto kern = prefill_attn_kernel<G>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -584,9 +558,9 @@ static hipError_t launch_prefill_t(const Dims& d, int mode, const uint16_t* q, i
                                                      160 * 1024);
   if (attr != hipSuccess) return attr;
   const dim3 grid(unsigned(int64_t(d.B) * d.Hkv * ntile));
-  kern<<<grid, Sh::NT, prefill_lds(nstage, umax, Sh::TQ, d.K), s>>>(
+  kern<<<grid, Sh::NT, prefill_lds(umax, Sh::TQ, d.K), s>>>(
       q, k, v, idx, out, lse, d.Hq, d.Hkv, n_q, kv_cap, kv_len, d.K, d.dense_thr, mode,
-      d.scale * 1.4426950408889634f, ntile, int(umax), nstage);
+      d.scale * 1.4426950408889634f, ntile, int(umax));
   return hipGetLastError();
 }
 
