@@ -38,6 +38,7 @@
 // LDS tiles are row-major 64 x 128 bf16 whose 16-byte pieces are XOR-swizzled
 // per row by swz(r) = ((r & 7) << 1) | ((r >> 3) & 1).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -348,7 +349,20 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
   // (so nobody still reads entry u - 1 there).
   int32_t blk_nx = U > 0 ? blk_raw(0) : 0;         // entry u's block and mask
   uint64_t mask_nx = U > 0 ? mask_raw(0) : 0ull;
-  for (int u = 0; u < U; ++u) {
+  // Per-lane parts of the fragment addresses; the ring slot, tile and k-step
+  // parts are compile-time offsets (the loop below is unrolled by the two
+  // ring slots), so every fragment read is a ds_read with an immediate offset.
+  int kaddr[DS], vaddr[2][DT];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) kaddr[ds] = k_lane ^ (ds << 5);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    vaddr[0][dt] = v_lane[0] ^ (dt << 6);
+    vaddr[1][dt] = v_lane[1] ^ (dt << 6);
+  }
+
+  auto step = [&](int u, auto slot_c) __attribute__((always_inline)) {
+    constexpr int SLOT = decltype(slot_c)::value;   // == u % 2
     const int32_t blk_cur = blk_nx;
     const uint64_t mask_cur = mask_nx;
     if (u + 1 < U) {
@@ -358,16 +372,15 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
     wait_vmem();                                  // this wave's loads of entry u landed
     wait_lds();
     ring_barrier();                               // ... and every wave's; the other slot is free
-    char* const slot = ring + (u & 1) * kStageBytes;
     if (u + 1 < U)
-      issue_stage<NW>(ring + ((u + 1) & 1) * kStageBytes, rk, rv,
+      issue_stage<NW>(ring + (1 - SLOT) * kStageBytes, rk, rv,
                       int64_t(__builtin_amdgcn_readfirstlane(blk_nx)) * kBlock, w, l);
-    const char* kt_b = slot;
-    const lds_char* vt_b = (const lds_char*)(slot + kTileBytes);
+    const char* kt_b = ring + SLOT * kStageBytes;
+    const lds_char* vt_b = (const lds_char*)(ring + SLOT * kStageBytes + kTileBytes);
     const int64_t key0 = int64_t(__builtin_amdgcn_readfirstlane(blk_cur)) * kBlock;
     const uint64_t tmask = uniform_u64(mask_cur);
     const uint32_t bits = uint32_t(tmask >> (w * TPS)) & uint32_t((1ull << TPS) - 1ull);
-    if (bits == 0) continue;                      // no token of this wavefront needs the block
+    if (bits == 0) return;                        // no token of this wavefront needs the block
 
     // S^T = K Q^T: two 32-key tiles. Accumulator register r of lane l holds
     // key 32*kt + 8*(r/4) + 4*hl + r%4 of row r32.
@@ -377,7 +390,7 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int ds = 0; ds < DS; ++ds) kf[kt][ds] = lds_read_k(kt_b + kt * 8192, k_lane ^ (ds << 5));
+        for (int ds = 0; ds < DS; ++ds) kf[kt][ds] = lds_read_k(kt_b + kt * 8192, kaddr[ds]);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -460,7 +473,7 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          vfr[dt][ks] = lds_read_vt(vt_b + ks * 4096, v_lane[0] ^ (dt << 6), v_lane[1] ^ (dt << 6));
+          vfr[dt][ks] = lds_read_vt(vt_b + ks * 4096, vaddr[0][dt], vaddr[1][dt]);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) lacc = mfma32(ones, pf[ks], lacc);
 #pragma unroll
@@ -477,6 +490,10 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
+  };
+  for (int u = 0; u < U; u += 2) {
+    step(u, std::integral_constant<int, 0>());
+    if (u + 1 < U) step(u + 1, std::integral_constant<int, 1>());
   }
 
   // ---------------------------------------------------------------- epilogue
