@@ -68,6 +68,9 @@ def lib():
         L.orc_attend.restype = i32
         L.orc_attend.argtypes = [i32, i32, i32, i32, i32, i32, P, i32, P, P, P, i64, i64,
                                  P, i32, i32, P, dbl, i32, P, P, P, P]
+        L.orc_attend_backward.restype = i32
+        L.orc_attend_backward.argtypes = [i32, i32, i32, i32, i32, i32, P, i32, P, P, P, i64, i64,
+                                          P, i32, i32, P, dbl, P, P, P, P]
         _lib = L
     return _lib
 
@@ -181,6 +184,37 @@ def attend(mode: int, q, k, v, pos, kv_len: int, rows, n_kv_heads: int, *, idx=N
     if rc:
         raise ValueError("orc_attend rejected its arguments")
     return out, lse, nk
+
+
+def attend_backward(mode: int, q, k, v, pos, kv_len: int, n_kv_heads: int, dout, *, idx=None,
+                    K: int = 0, dense_threshold: int = 0, tree_mask=None, scale: float | None = None,
+                    bs: int = 64):
+    """Gradients of sum(dout * o) over every row (b, h, i) of `q`, with the key sets of
+    `attend`: returns dq [B][Hq][n_q][D], dk and dv [B][Hkv][kv_cap][D], all fp64."""
+    q = _c(q, np.uint16)
+    k = _c(k, np.uint16)
+    v = _c(v, np.uint16)
+    dout = _c(dout, np.uint16)
+    B, Hq, n_q, D = q.shape
+    cap = k.shape[2]
+    pos = _c(pos, np.int64)
+    if idx is not None:
+        idx = _c(idx, np.int32)
+        K = idx.shape[-1]
+    if tree_mask is not None:
+        tree_mask = _c(tree_mask, np.uint64)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = np.empty((B, Hq, n_q, D), dtype=np.float64)
+    dk = np.empty((B, n_kv_heads, cap, D), dtype=np.float64)
+    dv = np.empty((B, n_kv_heads, cap, D), dtype=np.float64)
+    rc = lib().orc_attend_backward(mode, B, Hq, n_kv_heads, D, bs, _ptr(q), n_q, _ptr(pos), _ptr(k),
+                                   _ptr(v), cap, kv_len, _ptr(idx), K, dense_threshold,
+                                   _ptr(tree_mask), float(scale), _ptr(dout), _ptr(dq), _ptr(dk),
+                                   _ptr(dv))
+    if rc:
+        raise ValueError("orc_attend_backward rejected its arguments")
+    return dq, dk, dv
 
 
 # ------------------------------------------------------------ whole path

@@ -343,3 +343,88 @@ int orc_attend(int mode, int B, int Hq, int Hkv, int D, int bs,
   }
   return bad ? -1 : 0;
 }
+
+/* ------------------------------------------------------- 6. backward
+ * Gradients of L = sum over rows of dO . o (the rows' attention outputs of
+ * orc_attend, same key sets) with respect to q, k and v, in fp64. Per row,
+ * with P_t the softmax weights over its keys:
+ *   dP_t = dO . v_t;  D = sum_t P_t dP_t;  dS_t = P_t (dP_t - D);
+ *   dq = scale sum_t dS_t k_t;  dk_t += scale dS_t q;  dv_t += P_t dO.
+ * (The softmax Jacobian is diag(P) - P P^T, so dL/ds_t = P_t (dP_t - D).)
+ * Every row (b, h, i) of the call contributes (all heads, all n_q rows).
+ * dout [B][Hq][n_q][D] bf16; dq [B][Hq][n_q][D], dk and dv [B][Hkv][kv_cap][D]
+ * fp64, fully written (zeros where no row attends). */
+int orc_attend_backward(int mode, int B, int Hq, int Hkv, int D, int bs,
+                        const uint16_t* q, int n_q, const int64_t* pos,
+                        const uint16_t* k, const uint16_t* v, int64_t kv_cap, int64_t kv_len,
+                        const int32_t* idx, int K, int dense_threshold,
+                        const uint64_t* tree_mask, double scale, const uint16_t* dout,
+                        double* dq, double* dk, double* dv) {
+  if (Hq % Hkv || kv_len > kv_cap) return -1;
+  const int G = Hq / Hkv;
+  memset(dq, 0, sizeof(double) * (size_t)B * Hq * n_q * D);
+  memset(dk, 0, sizeof(double) * (size_t)B * Hkv * kv_cap * D);
+  memset(dv, 0, sizeof(double) * (size_t)B * Hkv * kv_cap * D);
+  int bad = 0;
+  /* one (b, g) per task: its rows write only its dk, dv slices */
+  #pragma omp parallel
+  {
+    int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)(kv_len + 64));
+    double* s = (double*)malloc(sizeof(double) * (size_t)(kv_len + 64));
+    double* dp = (double*)malloc(sizeof(double) * (size_t)(kv_len + 64));
+    #pragma omp for schedule(dynamic)
+    for (int bg = 0; bg < B * Hkv; ++bg) {
+      const int b = bg / Hkv, g = bg % Hkv;
+      for (int hh = 0; hh < G; ++hh) {
+        const int h = g * G + hh;
+        for (int i = 0; i < n_q; ++i) {
+          const int32_t* sel = idx ? &idx[(((int64_t)b * Hkv + g) * n_q + i) * K] : NULL;
+          const uint64_t msk = tree_mask ? tree_mask[(int64_t)b * n_q + i] : 0ull;
+          const int64_t n = orc_keyset(mode, bs, pos[i], kv_len, sel, K, dense_threshold, msk, keys);
+          if (n <= 0) { bad = 1; continue; }
+          const uint16_t* qv = &q[(((int64_t)b * Hq + h) * n_q + i) * D];
+          const uint16_t* gv = &dout[(((int64_t)b * Hq + h) * n_q + i) * D];
+          double mx = -INFINITY;
+          for (int64_t t = 0; t < n; ++t) {
+            const uint16_t* kr = &k[((int64_t)bg * kv_cap + keys[t]) * D];
+            const uint16_t* vr = &v[((int64_t)bg * kv_cap + keys[t]) * D];
+            double dot = 0.0, dd = 0.0;
+            for (int e = 0; e < D; ++e) {
+              dot += bf(&qv[e]) * bf(&kr[e]);
+              dd += bf(&gv[e]) * bf(&vr[e]);
+            }
+            s[t] = scale * dot;
+            dp[t] = dd;
+            if (s[t] > mx) mx = s[t];
+          }
+          double l = 0.0;
+          for (int64_t t = 0; t < n; ++t) {
+            s[t] = exp(s[t] - mx);          /* unnormalized P */
+            l += s[t];
+          }
+          double Dsum = 0.0;
+          for (int64_t t = 0; t < n; ++t) {
+            s[t] /= l;                      /* P_t */
+            Dsum += s[t] * dp[t];
+          }
+          double* dqr = &dq[(((int64_t)b * Hq + h) * n_q + i) * D];
+          for (int64_t t = 0; t < n; ++t) {
+            const double ds = s[t] * (dp[t] - Dsum);
+            const uint16_t* kr = &k[((int64_t)bg * kv_cap + keys[t]) * D];
+            double* dkr = &dk[((int64_t)bg * kv_cap + keys[t]) * D];
+            double* dvr = &dv[((int64_t)bg * kv_cap + keys[t]) * D];
+            for (int e = 0; e < D; ++e) {
+              dqr[e] += scale * ds * bf(&kr[e]);
+              dkr[e] += scale * ds * bf(&qv[e]);
+              dvr[e] += s[t] * bf(&gv[e]);
+            }
+          }
+        }
+      }
+    }
+    free(keys);
+    free(s);
+    free(dp);
+  }
+  return bad ? -1 : 0;
+}
