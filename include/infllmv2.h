@@ -174,6 +174,36 @@ INFLLMV2_API int infllmv2_sparse_attn_decode_scores(const infllmv2_cfg* cfg, con
                                        void* out, float* lse, void* workspace,
                                        size_t workspace_bytes, void* stream);
 
+/* Bytes of workspace infllmv2_sparse_attn_prefill_backward needs for these
+ * shapes (0 if the configuration is invalid). */
+INFLLMV2_API size_t infllmv2_prefill_backward_workspace_bytes(const infllmv2_cfg* cfg, int32_t n_q,
+                                                 int64_t kv_len);
+
+/* Backward of infllmv2_sparse_attn_prefill: the gradients that make the
+ * sparse attention trainable (QbitAI summary, "Model architecture: InfLLM
+ * v2": native, trainable sparse attention; the block choice is a discrete
+ * selection and passes no gradient). For upstream gradients dout of the
+ * forward output out, with the forward's own key sets (idx, the own block up
+ * to each row's position, dense rows below dense_threshold):
+ *   dS_t = P_t (dout . v_t - dout . out),  P_t = exp(scale q.k_t - lse),
+ *   dq = scale sum_t dS_t k_t,  dk_t = scale sum over rows dS_t q,
+ *   dv_t = sum over rows P_t dout.
+ *   q, out, dout [B][Hq][n_q][D] bf16; idx as for the forward; lse [B][Hq][n_q]
+ *   fp32 as written by the forward (required);
+ *   dq [B][Hq][n_q][D] fp32 (fully written); dk, dv [B][Hkv][kv_cap][D] fp32:
+ *   rows < kv_len are written (zeros for keys no row attends), rows past
+ *   kv_len are left untouched.
+ *   The dk, dv sums of keys attended by more than 256 tokens are split over
+ *   workgroups and added atomically, so their last bits may differ between
+ *   runs. Requires head_dim 128 (else INFLLMV2_UNSUPPORTED); workspace of at
+ *   least infllmv2_prefill_backward_workspace_bytes(), no initial contents. */
+INFLLMV2_API int infllmv2_sparse_attn_prefill_backward(const infllmv2_cfg* cfg, const void* q,
+                                          int32_t n_q, const void* k, const void* v,
+                                          int64_t kv_cap, int64_t kv_len, const int32_t* idx,
+                                          const void* out, const float* lse, const void* dout,
+                                          float* dq, float* dk, float* dv, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
 /* Dense attention of n_q queries at positions kv_len - n_q + i over the first
  * kv_len keys, causal (key <= position) or not: the short-context path
  * (QbitAI summary, "Model architecture: InfLLM v2": dense attention kept for

@@ -95,6 +95,12 @@ CASES = [
     ("infllmv2_sparse_attn_decode_scores", dict(top_k=65), (A, A, A, 64, 64, A, None, B, None, 0x100000, 1 << 30, None), -2, "top_k above 64"),
     ("infllmv2_sparse_attn_decode_scores", {}, (A, A, A, 1 << 20, 1 << 20, A, None, B, None, 0x100000, 1 << 40, None), -2, "4096"),
     ("infllmv2_sparse_attn_decode_scores", {}, (A, A, A, 64, 64, A, None, B, None, 0x100000, 16, None), -3, "workspace"),
+    ("infllmv2_sparse_attn_prefill_backward", {}, (A, 64, A, A, 64, 64, B, A, None, A, A, A, A, 0x100000, 1 << 30, None), -1, "lse is NULL"),
+    ("infllmv2_sparse_attn_prefill_backward", {}, (A, 64, A, A, 64, 64, B, A, B, None, A, A, A, 0x100000, 1 << 30, None), -1, "dout is NULL"),
+    ("infllmv2_sparse_attn_prefill_backward", {}, (A, 64, A, A, 64, 64, B, A, B, A, A + 4, A, A, 0x100000, 1 << 30, None), -1, "dq"),
+    ("infllmv2_sparse_attn_prefill_backward", dict(head_dim=64), (A, 64, A, A, 64, 64, B, A, B, A, A, A, A, 0x100000, 1 << 30, None), -2, "head_dim 128"),
+    ("infllmv2_sparse_attn_prefill_backward", {}, (A, 64, A, A, 64, 64, B, A, B, A, A, A, A, 0x100000, 16, None), -3, "workspace"),
+    ("infllmv2_sparse_attn_prefill_backward", {}, (A, 65, A, A, 64, 64, B, A, B, A, A, A, A, 0x100000, 1 << 30, None), -1, "n_q"),
     ("infllmv2_dense_attn", {}, (A, 1, A, A, 64, 0, 1, B, None, None), -1, "kv_len"),
     ("infllmv2_dense_attn", {}, (A, 1, A, None, 64, 64, 1, B, None, None), -1, "v is NULL"),
     ("infllmv2_dense_attn", dict(softmax_scale=float("nan")), (A, 1, A, A, 64, 64, 1, B, None, None), -1, "finite"),
@@ -125,6 +131,10 @@ def test_workspace_bytes(t):
     assert n1 > 0 and n16 > n1
     assert t.infllmv2_decode_workspace_bytes(cfg, 0, 10) == 0
     assert t.infllmv2_decode_workspace_bytes(cfg, 5, 3) == 0
+    cfg = cfg_ok(t, top_k=16)
+    b1 = t.infllmv2_prefill_backward_workspace_bytes(cfg, 32768, 32768)
+    assert b1 > 0 and t.infllmv2_prefill_backward_workspace_bytes(cfg, 1024, 1024) < b1
+    assert t.infllmv2_prefill_backward_workspace_bytes(cfg, 0, 10) == 0
 
 
 def test_binding_raises_with_status(t):

@@ -133,3 +133,33 @@ def test_backward_sum_rule_and_zero_query(orc):
     dq1, dk1, dv1 = orc.attend_backward(orc.MODE_CAUSAL, d["q"][:, :, :1], d["k"], d["v"],
                                         orc.positions("prefill", 1, 0), 1, w.n_kv_heads, dout[:, :, :1])
     assert np.abs(dq1).max() == 0.0 and np.abs(dk1).max() == 0.0
+
+
+def test_backward_tolerance_covers_bf16_arithmetic(orc):
+    """The GPU backward rounds dS to bf16 before its products and forms
+    Delta = dO . O from the bf16 forward output. Replaying exactly those two
+    roundings in fp64 on sampled rows must stay well inside the GPU test's
+    bounds for dq (mean-abs <= 1e-2 mean|dq|, max-abs <= 2e-2 max|dq|)."""
+    w = tiny("bwd_tol", n_q_heads=8, n_kv_heads=2, head_dim=128, seq_len=1100, top_k=4,
+             dense_threshold=300, n_plant=2)
+    d, idx, dout = _case(orc, w, 0)
+    T, G = w.seq_len, 4
+    f = lambda a: synth.bf16_to_f32(a).astype(np.float64)
+    bf = lambda x: synth.bf16_to_f32(synth.to_bf16_bits(x.astype(np.float32)).reshape(x.shape)).astype(np.float64)
+    q, k, v, g = f(d["q"]), f(d["k"]), f(d["v"]), f(dout)
+    sc = 1 / math.sqrt(128)
+    ex, ap = [], []
+    for h in range(8):
+        for i in range(0, T, 11):
+            keys = orc.keyset(orc.MODE_SPARSE, i, T, idx[0, h // G, i], w.top_k, w.dense_threshold)
+            kk, vv = k[0, h // G, keys], v[0, h // G, keys]
+            s = sc * kk @ q[0, h, i]
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            dp = vv @ g[0, h, i]
+            ex.append(sc * (p * (dp - p @ dp)) @ kk)
+            ap.append(sc * bf(p * (dp - bf(p @ vv) @ g[0, h, i])) @ kk)
+    ex, ap = np.array(ex), np.array(ap)
+    err = np.abs(ap - ex)
+    assert err.mean() <= 0.6e-2 * np.abs(ex).mean()
+    assert err.max() <= 1e-2 * np.abs(ex).max()

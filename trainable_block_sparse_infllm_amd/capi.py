@@ -19,6 +19,7 @@ EXPORTS = [
     "infllmv2_pool_kernels", "infllmv2_score_blocks", "infllmv2_topk_blocks",
     "infllmv2_sparse_attn_prefill", "infllmv2_decode_workspace_bytes",
     "infllmv2_sparse_attn_decode", "infllmv2_sparse_attn_decode_scores", "infllmv2_dense_attn",
+    "infllmv2_prefill_backward_workspace_bytes", "infllmv2_sparse_attn_prefill_backward",
     "infllmv2_strerror",
     "infllmv2_last_error",
 ]
@@ -66,6 +67,9 @@ def lib():
             "infllmv2_sparse_attn_decode": (i32, [cfg, P, i32, P, P, i64, i64, P, P, P, P, P, sz, P]),
             "infllmv2_sparse_attn_decode_scores": (i32, [cfg, P, P, P, i64, i64, P, P, P, P, P, sz, P]),
             "infllmv2_dense_attn": (i32, [cfg, P, i32, P, P, i64, i64, i32, P, P, P]),
+            "infllmv2_prefill_backward_workspace_bytes": (sz, [cfg, i32, i64]),
+            "infllmv2_sparse_attn_prefill_backward": (i32, [cfg, P, i32, P, P, i64, i64, P, P, P, P,
+                                                            P, P, P, P, sz, P]),
             "infllmv2_strerror": (C.c_char_p, [i32]),
             "infllmv2_last_error": (C.c_char_p, []),
         }
@@ -142,6 +146,17 @@ def infllmv2_sparse_attn_decode_scores(cfg, q, k_cache, v_cache, kv_cap, kv_len,
 def infllmv2_dense_attn(cfg, q, n_q, k, v, kv_cap, kv_len, causal, out, lse=None, stream=None):
     _check(lib().infllmv2_dense_attn(C.byref(cfg), _p(q), n_q, _p(k), _p(v), kv_cap, kv_len, int(causal),
                                      _p(out), _p(lse), _s(stream)))
+
+
+def infllmv2_prefill_backward_workspace_bytes(cfg, n_q, kv_len) -> int:
+    return int(lib().infllmv2_prefill_backward_workspace_bytes(C.byref(cfg), n_q, kv_len))
+
+
+def infllmv2_sparse_attn_prefill_backward(cfg, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, dout, dq, dk,
+                                          dv, workspace, workspace_bytes, stream=None):
+    _check(lib().infllmv2_sparse_attn_prefill_backward(
+        C.byref(cfg), _p(q), n_q, _p(k), _p(v), kv_cap, kv_len, _p(idx), _p(out), _p(lse), _p(dout),
+        _p(dq), _p(dk), _p(dv), _p(workspace), workspace_bytes, _s(stream)))
 
 
 def infllmv2_strerror(status: int) -> str:

@@ -236,6 +236,48 @@ int infllmv2_sparse_attn_prefill(const infllmv2_cfg* cfg, const void* q, int32_t
   return INFLLMV2_OK;
 }
 
+size_t infllmv2_prefill_backward_workspace_bytes(const infllmv2_cfg* cfg, int32_t n_q,
+                                                int64_t kv_len) {
+  Dims d;
+  if (check_cfg("infllmv2_prefill_backward_workspace_bytes", cfg, true, &d) != INFLLMV2_OK) return 0;
+  if (n_q < 1 || kv_len < n_q) return 0;
+  return infllmv2::prefill_backward_workspace_bytes(d, n_q, kv_len);
+}
+
+int infllmv2_sparse_attn_prefill_backward(const infllmv2_cfg* cfg, const void* q, int32_t n_q,
+                                          const void* k, const void* v, int64_t kv_cap,
+                                          int64_t kv_len, const int32_t* idx, const void* out,
+                                          const float* lse, const void* dout, float* dq, float* dk,
+                                          float* dv, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  const char* fn = "infllmv2_sparse_attn_prefill_backward";
+  Dims d;
+  TRY(check_cfg(fn, cfg, true, &d));
+  TRY(check_attn(fn, d, q, n_q, k, v, kv_cap, kv_len, out, lse));
+  TRY(check_ptr(fn, idx, "idx", 4));
+  TRY(check_ptr(fn, lse, "lse", 4));
+  TRY(check_ptr(fn, dout, "dout", 16));
+  TRY(check_ptr(fn, dq, "dq", 16));
+  TRY(check_ptr(fn, dk, "dk", 16));
+  TRY(check_ptr(fn, dv, "dv", 16));
+  if (!infllmv2::prefill_backward_ok(d, kv_len))
+    return fail(INFLLMV2_UNSUPPORTED, fn, "backward needs head_dim 128 and a tile that fits LDS");
+  TRY(check_ptr(fn, workspace, "workspace", 256));
+  const size_t need = infllmv2::prefill_backward_workspace_bytes(d, n_q, kv_len);
+  if (workspace_bytes < need) {
+    char msg[128];
+    std::snprintf(msg, sizeof msg, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    return fail(INFLLMV2_WORKSPACE_TOO_SMALL, fn, msg);
+  }
+  TRY(check_device(fn));
+  LAUNCH(fn, infllmv2::launch_prefill_backward(
+                 d, static_cast<const uint16_t*>(q), n_q, static_cast<const uint16_t*>(k),
+                 static_cast<const uint16_t*>(v), kv_cap, kv_len, idx,
+                 static_cast<const uint16_t*>(out), lse, static_cast<const uint16_t*>(dout), dq, dk,
+                 dv, workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+  return INFLLMV2_OK;
+}
+
 size_t infllmv2_decode_workspace_bytes(const infllmv2_cfg* cfg, int32_t n_q, int64_t kv_len) {
   Dims d;
   if (check_cfg("infllmv2_decode_workspace_bytes", cfg, true, &d) != INFLLMV2_OK) return 0;

@@ -1,0 +1,699 @@
+// Backward of the sparse prefill attention, head_dim 128: the gradients that
+// make the block-sparse attention trainable (MiniCPM4 technical-report
+// summary, QbitAI repost, section "Model architecture: InfLLM v2": the sparse
+// attention is native and trainable; the block choice itself is a discrete
+// selection and carries no gradient).
+//
+// For a row with weights P over its attended keys (the forward's key sets:
+// selected blocks, the own block up to the row's position, or the dense
+// prefix below the threshold), upstream gradient dO and forward output O:
+//   dP_t = dO . v_t;  Delta = dO . O;  dS_t = P_t (dP_t - Delta);
+//   dq = scale sum_t dS_t k_t;  dk_t += scale dS_t q;  dv_t += P_t dO.
+// P_t = exp(scale q.k_t - lse) is recomputed from the forward's lse.
+//
+// Kernels:
+//   prep  -- Delta and lse in log2 units per row;
+//   dq    -- query-centric, the forward's tiling: a workgroup walks the union
+//            of its tile's blocks through the LDS ring and keeps dQ^T in MFMA
+//            accumulators (S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T with
+//            K^T from transpose reads of the K tile);
+//   index -- for every key block, the list of query tokens that attend it
+//            (counts, prefix sums, fill) and its split into segments;
+//   dkv   -- key-centric: a workgroup owns one segment of one block's list;
+//            K and V of the block stay in LDS, chunks of 64 query rows (Q and
+//            dO) stream through a two-stage LDS ring, and dK^T, dV^T stay in
+//            MFMA accumulators (S = Q K^T, dP = dO V^T, dV^T += dO^T P,
+//            dK^T += Q^T dS with Q^T and dO^T from transpose reads). A block
+//            split into several segments adds its partial sums atomically.
+#include <algorithm>
+
+#include "common.hpp"
+#include "launch.hpp"
+#include "prefill_tile.hpp"
+
+namespace infllmv2 {
+
+using namespace tile;
+
+namespace {
+
+constexpr int kSegTokens = 256;     // query tokens per dK/dV segment
+constexpr int kChunkRows = 64;      // query rows per dK/dV chunk (two 32-row halves)
+
+struct BwdLayout {
+  int64_t rows, bgs, nblk, emax, smax;
+  size_t off_lse2, off_delta, off_cnt, off_cur, off_off, off_nseg, off_list, off_seg, total;
+};
+
+BwdLayout bwd_layout(const Dims& d, int n_q, int64_t kv_len) {
+  BwdLayout L{};
+  L.rows = int64_t(d.B) * d.Hq * n_q;
+  L.bgs = int64_t(d.B) * d.Hkv;
+  L.nblk = (kv_len - 1) / kBlock + 1;
+  // blocks one token attends: K selected + its own; a dense row (p + 1 <
+  // threshold) every block up to its own
+  const int64_t dense_blocks = d.dense_thr > 0 ? (int64_t(d.dense_thr) - 2) / kBlock + 1 : 0;
+  L.emax = int64_t(n_q) * std::max<int64_t>(d.K + 1, dense_blocks);
+  L.smax = (L.emax + kSegTokens - 1) / kSegTokens + L.nblk;
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  size_t o = 0;
+  L.off_lse2 = o;  o = al(o + size_t(L.rows) * 4);
+  L.off_delta = o; o = al(o + size_t(L.rows) * 4);
+  L.off_cnt = o;   o = al(o + size_t(L.bgs * L.nblk) * 4);
+  L.off_cur = o;   o = al(o + size_t(L.bgs * L.nblk) * 4);
+  L.off_off = o;   o = al(o + size_t(L.bgs * L.nblk) * 4);
+  L.off_nseg = o;  o = al(o + size_t(L.bgs) * 4);
+  L.off_list = o;  o = al(o + size_t(L.bgs * L.emax) * 4);
+  L.off_seg = o;   o = al(o + size_t(L.bgs * L.smax) * 16);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ zero
+// Plain fill (no memset node, so the sequence can be captured in a graph).
+__global__ __launch_bounds__(256) void bwd_zero_kernel(uint4* __restrict__ p, int64_t n16) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += int64_t(gridDim.x) * 256)
+    p[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+// dk, dv rows < kv_len of every (b, g) -> 0 (rows past kv_len are not touched).
+__global__ __launch_bounds__(256) void bwd_zero_rows_kernel(float* __restrict__ dk,
+                                                            float* __restrict__ dv, int64_t kv_cap,
+                                                            int64_t kv_len, int64_t bgs) {
+  const int64_t per = kv_len * kD / 4;                  // float4 per (b, g)
+  const int64_t n = bgs * per;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+    const int64_t bg = i / per, r = i % per;
+    const int64_t o = bg * kv_cap * kD / 4 + r;
+    reinterpret_cast<float4*>(dk)[o] = make_float4(0.f, 0.f, 0.f, 0.f);
+    reinterpret_cast<float4*>(dv)[o] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// ------------------------------------------------------------------ prep
+// Delta = dO . O (both bf16, fp32 sum) and lse in log2 units, per row; 16
+// lanes per row, 8 columns each.
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ out,
+                                                       const uint16_t* __restrict__ dout,
+                                                       const float* __restrict__ lse,
+                                                       float* __restrict__ lse2,
+                                                       float* __restrict__ delta, int64_t rows) {
+  const int64_t r = int64_t(blockIdx.x) * 16 + threadIdx.x / 16;
+  const int c = threadIdx.x % 16;
+  float s = 0.f;
+  if (r < rows) {
+    const uint4 a = ldg16(out + r * kD + 8 * c);
+    const uint4 b = ldg16(dout + r * kD + 8 * c);
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s += bf2f(uint16_t(aw[i] & 0xFFFFu)) * bf2f(uint16_t(bw[i] & 0xFFFFu));
+      s += bf2f(uint16_t(aw[i] >> 16)) * bf2f(uint16_t(bw[i] >> 16));
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
+  if (r < rows && c == 0) {
+    delta[r] = s;
+    lse2[r] = lse[r] * 1.4426950408889634f;
+  }
+}
+
+// ------------------------------------------------------------------ dq
+template <int G>
+__global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ idx, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse2, const float* __restrict__ delta, float* __restrict__ dq,
+    int Hq, int Hkv, int n_q, int64_t kv_cap, int64_t kv_len, int K, int dense_thr,
+    float scale_log2, float scale, int ntile, int umax) {
+  using Sh = PrefillShape<G>;
+  constexpr int TPS = Sh::TPS, NW = Sh::NW, TQ = Sh::TQ, NT = Sh::NT;
+  constexpr int DS = kD / 16;
+  constexpr int DT = kD / 32;
+  constexpr int mode = 0;
+
+  extern __shared__ __align__(16) char smem[];
+  char* ring = smem;
+  uint64_t* u_mask = reinterpret_cast<uint64_t*>(smem + 2 * kStageBytes);
+  int32_t* u_blk = reinterpret_cast<int32_t*>(u_mask + umax);
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(u_blk + umax);
+  int32_t* wbase = reinterpret_cast<int32_t*>(bitmap + 256);
+  int32_t* wtot = wbase + 256;
+  int32_t* jsel = wtot + 16;
+
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int l = lane_id();
+  const int r32 = l % 32, hl = l / 32;
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = item % ntile;
+  const int bg = item / ntile;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int tok0 = tile * TQ;
+  const int ntok = min(TQ, n_q - tok0);
+  const int64_t base = kv_len - n_q + tok0;
+  const int64_t own_lo = base / kBlock;
+  const int64_t own_hi = (base + ntok - 1) / kBlock;
+  const int64_t dend = dense_thr > 0 ? dense_thr - 1 - base : 0;
+  const bool tile_dense = dend >= ntok;
+  const uint16_t* kbase = k + int64_t(bg) * kv_cap * kD;
+  const uint16_t* vbase = v + int64_t(bg) * kv_cap * kD;
+
+  // This lane's row: token tok0 + w*TPS + r32/G, head g*G + r32%G. Q^T and
+  // dO^T fragments (B operands, k-slots 8*hl .. of each 16-wide d step).
+  const int my_t = tok0 + w * TPS + r32 / G;
+  const int h = g * G + r32 % G;
+  const int64_t rid = (int64_t(b) * Hq + h) * n_q + (my_t < n_q ? my_t : 0);
+  bf16x8 qf[DS], df[DS];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) {
+    qf[ds] = as_bf16x8(ldg16_if(my_t < n_q, q + rid * kD + ds * 16 + hl * 8));
+    df[ds] = as_bf16x8(ldg16_if(my_t < n_q, dout + rid * kD + ds * 16 + hl * 8));
+  }
+  const float row_lse2 = my_t < n_q ? lse2[rid] : 0.f;
+  const float row_delta = my_t < n_q ? delta[rid] : 0.f;
+
+  int U;
+  if (tile_dense)
+    U = int(own_hi) + 1;
+  else
+    U = build_union<NT, NW>(idx, bg, n_q, tok0, ntok, base, own_lo, own_hi, dend, K, umax, mode,
+                            u_mask, u_blk, bitmap, wbase, wtot, jsel);
+  U = __builtin_amdgcn_readfirstlane(U);
+  auto blk_of = [&](int u) -> int {
+    return tile_dense ? u : __builtin_amdgcn_readfirstlane(lds_read(u_blk + u));
+  };
+  auto mask_of = [&](int u) -> uint64_t {
+    return tile_dense ? range_mask(u, mode, base, dend, ntok) : uniform_u64(lds_read(u_mask + u));
+  };
+
+  const uint32_t nrec = uint32_t(kv_len) * uint32_t(kD * 2);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(kbase), 0, int(nrec), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(vbase), 0, int(nrec), 0x00020000);
+  if (U > 0) issue_stage<NW>(ring, rk, rv, int64_t(blk_of(0)) * kBlock, w, l);
+
+  f32x16 dqacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dqacc[dt][e] = 0.f;
+  const int row_p = int(base) + w * TPS + r32 / G;
+  const int p_first = int(base) + w * TPS;
+  // fragment lane offsets (the forward's): K / V row fragment (kt, ds) at
+  // 8192*kt + (k_lane ^ (ds << 5)); transpose fragment (dt, ks) at
+  // 4096*ks + (t_lane[q] ^ (dt << 6)), q = 0, 1
+  const int k_lane = r32 * (kD * 2) + ((hl ^ swz(r32)) << 4);
+  int t_lane[2];
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq) {
+    const int j = l % 16;
+    const int row = 8 * qq + 4 * hl + j / 4;
+    const int piece = 2 * ((l / 16) % 2) + (j % 4) / 2;
+    t_lane[qq] = row * (kD * 2) + ((piece ^ swz(row)) << 4) + 8 * (j & 1);
+  }
+
+  for (int u = 0; u < U; ++u) {
+    wait_vmem();
+    wait_lds();
+    ring_barrier();                               // entry u landed; the other slot is free
+    char* const slot = ring + (u & 1) * kStageBytes;
+    if (u + 1 < U)
+      issue_stage<NW>(ring + ((u + 1) & 1) * kStageBytes, rk, rv, int64_t(blk_of(u + 1)) * kBlock,
+                      w, l);
+    const int key0 = blk_of(u) * kBlock;
+    const uint32_t bits = uint32_t(mask_of(u) >> (w * TPS)) & uint32_t((1ull << TPS) - 1ull);
+    if (bits == 0) continue;
+    const char* kt_b = slot;
+    const char* vt_b = slot + kTileBytes;
+
+    // S^T = K Q^T and dP^T = V dO^T: register r of lane l holds key
+    // 32*kt + 8*(r/4) + 4*hl + r%4 of row r32.
+    f32x16 sacc[2], pacc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        sacc[kt][e] = 0.f;
+        pacc[kt][e] = 0.f;
+      }
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        sacc[kt] = mfma32(lds_read_k(kt_b + kt * 8192, k_lane ^ (ds << 5)), qf[ds], sacc[kt]);
+        pacc[kt] = mfma32(lds_read_k(vt_b + kt * 8192, k_lane ^ (ds << 5)), df[ds], pacc[kt]);
+      }
+    }
+    // P^T from the forward's lse; dS^T = P^T (dP^T - Delta). Rows that do not
+    // attend the block, and keys past a row's position, get P = 0.
+    const bool row_on = (bits >> (r32 / G)) & 1u;
+    const int lim = key0 + kBlock - 1 > p_first ? row_p - key0 : 63;
+    bf16x8 sf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float ds_[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int e = 8 * (ks % 2) + jj;
+        const int key = 32 * (ks / 2) + 8 * (e / 4) + 4 * hl + e % 4;
+        const float p = (row_on && key <= lim)
+                            ? __builtin_amdgcn_exp2f(fmaf(sacc[ks / 2][e], scale_log2, -row_lse2))
+                            : 0.f;
+        ds_[jj] = p * (pacc[ks / 2][e] - row_delta);
+      }
+      uint4 uu;
+      uu.x = cvt_pk_bf16(ds_[0], ds_[1]);
+      uu.y = cvt_pk_bf16(ds_[2], ds_[3]);
+      uu.z = cvt_pk_bf16(ds_[4], ds_[5]);
+      uu.w = cvt_pk_bf16(ds_[6], ds_[7]);
+      sf[ks] = as_bf16x8(uu);
+    }
+    // dQ^T += K^T dS^T: K^T fragments by transpose reads of the K tile.
+    const lds_char* kt_l = (const lds_char*)kt_b;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        dqacc[dt] = mfma32(lds_read_vt(kt_l + ks * 4096, t_lane[0] ^ (dt << 6), t_lane[1] ^ (dt << 6)),
+                           sf[ks], dqacc[dt]);
+  }
+
+  // dqacc[dt] register r of lane l: d = 32*dt + 8*(r/4) + 4*hl + r%4 of row r32.
+  if (my_t < n_q) {
+    float* dst = dq + rid * kD;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        *reinterpret_cast<float4*>(dst + 32 * dt + 8 * rb + 4 * hl) =
+            make_float4(dqacc[dt][4 * rb] * scale, dqacc[dt][4 * rb + 1] * scale,
+                        dqacc[dt][4 * rb + 2] * scale, dqacc[dt][4 * rb + 3] * scale);
+  }
+}
+
+// ------------------------------------------------------------------ index
+// Blocks attended by token t (position p = P0 + t): every block <= own for a
+// dense row, else its selected blocks below own, plus own.
+template <typename F>
+__device__ __forceinline__ void for_each_block(const int32_t* __restrict__ idx_row, int K,
+                                               int64_t p, int dense_thr, F f) {
+  const int own = int(p / kBlock);
+  if (dense_thr > 0 && p + 1 < dense_thr) {
+    for (int j = 0; j <= own; ++j) f(j);
+    return;
+  }
+  for (int x = 0; x < K; ++x) {
+    const int j = idx_row[x];
+    if (j >= 0 && j < own) f(j);
+  }
+  f(own);
+}
+
+__global__ __launch_bounds__(256) void bwd_count_kernel(const int32_t* __restrict__ idx,
+                                                        int32_t* __restrict__ cnt, int Hkv, int n_q,
+                                                        int64_t kv_len, int K, int dense_thr,
+                                                        int64_t nblk, int ttiles) {
+  const int bg = blockIdx.x / ttiles;
+  const int t = (blockIdx.x % ttiles) * 256 + threadIdx.x;
+  if (t >= n_q) return;
+  const int64_t p = kv_len - n_q + t;
+  int32_t* c = cnt + int64_t(bg) * nblk;
+  for_each_block(idx + (int64_t(bg) * n_q + t) * K, K, p, dense_thr,
+                 [&](int j) { atomicAdd(&c[j], 1); });
+}
+
+__global__ __launch_bounds__(256) void bwd_fill_kernel(const int32_t* __restrict__ idx,
+                                                       const int32_t* __restrict__ off,
+                                                       int32_t* __restrict__ cur,
+                                                       int32_t* __restrict__ list, int Hkv, int n_q,
+                                                       int64_t kv_len, int K, int dense_thr,
+                                                       int64_t nblk, int64_t emax, int ttiles) {
+  const int bg = blockIdx.x / ttiles;
+  const int t = (blockIdx.x % ttiles) * 256 + threadIdx.x;
+  if (t >= n_q) return;
+  const int64_t p = kv_len - n_q + t;
+  const int32_t* o = off + int64_t(bg) * nblk;
+  int32_t* c = cur + int64_t(bg) * nblk;
+  int32_t* ls = list + int64_t(bg) * emax;
+  for_each_block(idx + (int64_t(bg) * n_q + t) * K, K, p, dense_thr,
+                 [&](int j) { ls[o[j] + atomicAdd(&c[j], 1)] = t; });
+}
+
+// One workgroup per (b, g): exclusive prefix of the per-block counts (list
+// offsets) and the segment table: block j's list is cut into segments of at
+// most kSegTokens tokens, each entry (j, start, length, split flag).
+__global__ __launch_bounds__(256) void bwd_scan_kernel(const int32_t* __restrict__ cnt,
+                                                       int32_t* __restrict__ off,
+                                                       int4* __restrict__ seg,
+                                                       int32_t* __restrict__ nseg, int64_t nblk,
+                                                       int64_t smax) {
+  __shared__ int s_a[256], s_b[256];
+  const int bg = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int per = int((nblk + 255) / 256);
+  const int lo = min<int64_t>(nblk, int64_t(tid) * per), hi = min<int64_t>(nblk, lo + per);
+  const int32_t* c = cnt + int64_t(bg) * nblk;
+  int ca = 0, cs = 0;
+  for (int j = lo; j < hi; ++j) {
+    ca += c[j];
+    cs += (c[j] + kSegTokens - 1) / kSegTokens;
+  }
+  s_a[tid] = ca;
+  s_b[tid] = cs;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {             // inclusive scans
+    const int xa = tid >= o ? s_a[tid - o] : 0;
+    const int xb = tid >= o ? s_b[tid - o] : 0;
+    __syncthreads();
+    s_a[tid] += xa;
+    s_b[tid] += xb;
+    __syncthreads();
+  }
+  int pa = s_a[tid] - ca, ps = s_b[tid] - cs;
+  int4* sg = seg + int64_t(bg) * smax;
+  for (int j = lo; j < hi; ++j) {
+    off[int64_t(bg) * nblk + j] = pa;
+    const int n = c[j];
+    const int ns = (n + kSegTokens - 1) / kSegTokens;
+    for (int x = 0; x < ns; ++x)
+      sg[ps + x] = make_int4(j, pa + x * kSegTokens, min(kSegTokens, n - x * kSegTokens), ns > 1);
+    pa += n;
+    ps += ns;
+  }
+  if (tid == 255) nseg[bg] = s_b[255];
+}
+
+// ------------------------------------------------------------------ dkv
+// LDS: K and V tiles of the block (swizzled like the ring stages), two
+// stages of Q and dO tiles (64 rows each), the segment's tokens and per-row
+// (lse2, Delta).
+constexpr int kDkvQTile = kChunkRows * kD * 2;          // 16 KB
+constexpr int kDkvStage = 2 * kDkvQTile;                // Q then dO
+constexpr int kDkvLds = kStageBytes + 2 * kDkvStage + kSegTokens * 4 + kSegTokens * 16 * 8 + 64;
+
+// Rows 0..63 of a chunk -> one stage: 16 chunks of 1 KB per tensor (rows
+// 4c..4c+3), lane l's 16 bytes land in slot l % 16 of row 4c + l/16 and it
+// fetches the global piece stored there; rows past the segment repeat its
+// last row (finite; their P and dS are zero).
+__device__ __forceinline__ void issue_qd_stage(char* stage, const uint16_t* q, const uint16_t* dout,
+                                               const int32_t* s_tok, int len, int row0, int64_t qb,
+                                               int G, int n_q, int w, int l) {
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    const int c = x * 4 + w;                        // 0..31: tensor c / 16, row group c % 16
+    const int row = 4 * (c % 16) + l / 16;
+    int rr = row0 + row;                            // (token slot, head) of the segment
+    const int tslot = min(rr / G, len - 1);
+    const int hh = rr % G;
+    const int64_t rid = (qb + hh) * n_q + s_tok[tslot];
+    const uint16_t* src = (c < 16 ? q : dout) + rid * kD + (((l % 16) ^ swz(row)) << 3);
+    load_lds16(src, stage + c * 1024);
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse2,
+    const float* __restrict__ delta, const int32_t* __restrict__ list,
+    const int4* __restrict__ seg, const int32_t* __restrict__ nseg, float* __restrict__ dk,
+    float* __restrict__ dv, int Hq, int Hkv, int n_q, int64_t kv_cap, int64_t kv_len,
+    int64_t emax, int64_t smax, float scale_log2, float scale) {
+  constexpr int DS = kD / 16;
+  constexpr int DT = kD / 32;
+  extern __shared__ __align__(16) char smem[];
+  char* kv_t = smem;                                  // K tile, V tile
+  char* ring = smem + kStageBytes;                    // 2 stages x (Q tile, dO tile)
+  int32_t* s_tok = reinterpret_cast<int32_t*>(ring + 2 * kDkvStage);
+  float2* s_row = reinterpret_cast<float2*>(s_tok + kSegTokens);   // [kSegTokens*G] (lse2, Delta)
+
+  const int bg = blockIdx.x / int(smax);
+  const int sidx = blockIdx.x % int(smax);
+  if (sidx >= nseg[bg]) return;
+  const int4 sg = seg[int64_t(bg) * smax + sidx];
+  const int j = sg.x, start = sg.y, len = sg.z;
+  const bool split = sg.w != 0;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int l = lane_id();
+  const int r32 = l % 32, hl = l / 32;
+  const int kt = w & 1;             // keys 32*kt .. of the block
+  const int rh = w >> 1;            // rows 32*rh .. of each chunk
+  const int key0 = j * kBlock;
+  const int64_t P0 = kv_len - n_q;
+  const int64_t qb = int64_t(b) * Hq + int64_t(g) * G;      // first head row of the group
+
+  // the segment's tokens and per-row (lse2, Delta)
+  for (int i = threadIdx.x; i < len; i += 256) s_tok[i] = list[int64_t(bg) * emax + start + i];
+  __syncthreads();
+  for (int i = threadIdx.x; i < len * G; i += 256) {
+    const int64_t rid = (qb + i % G) * n_q + s_tok[i / G];
+    s_row[i] = make_float2(lse2[rid], delta[rid]);
+  }
+  // K and V of the block -> LDS (swizzled), rows past kv_len read as zeros
+  {
+    const uint16_t* kb = k + (int64_t(bg) * kv_cap) * kD;
+    const uint16_t* vb = v + (int64_t(bg) * kv_cap) * kD;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int c = x * 4 + w;
+      const int row = 4 * (c % 16) + l / 16;
+      const int64_t key = key0 + row;
+      const void* src = key < kv_len
+                            ? static_cast<const void*>((c < 16 ? kb : vb) + key * kD +
+                                                       (((l % 16) ^ swz(row)) << 3))
+                            : static_cast<const void*>(kZeroPiece);
+      load_lds16(src, kv_t + c * 1024);
+    }
+  }
+  const int nch = (len * G + kChunkRows - 1) / kChunkRows;
+  issue_qd_stage(ring, q, dout, s_tok, len, 0, qb, G, n_q, w, l);
+
+  f32x16 dkacc[DT], dvacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      dkacc[dt][e] = 0.f;
+      dvacc[dt][e] = 0.f;
+    }
+  // A fragments of S = Q K^T and dP = dO V^T: row 32*rh + r32, piece 2*ds + hl
+  // (offset r_lane ^ (ds << 5) within the half); B fragments: K / V row of key
+  // 32*kt + r32 (same addressing on the K / V tiles). Transpose fragments
+  // (dt, ks) of the Q / dO half: 4096*ks + (t_lane[q] ^ (dt << 6)).
+  const int r_lane = r32 * (kD * 2) + ((hl ^ swz(r32)) << 4);
+  int t_lane[2];
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq) {
+    const int jj = l % 16;
+    const int row = 8 * qq + 4 * hl + jj / 4;
+    const int piece = 2 * ((l / 16) % 2) + (jj % 4) / 2;
+    t_lane[qq] = row * (kD * 2) + ((piece ^ swz(row)) << 4) + 8 * (jj & 1);
+  }
+
+  for (int c = 0; c < nch; ++c) {
+    wait_vmem();
+    wait_lds();
+    ring_barrier();                                 // chunk c (and K, V) landed; other slot free
+    char* const st = ring + (c & 1) * kDkvStage;
+    if (c + 1 < nch)
+      issue_qd_stage(ring + ((c + 1) & 1) * kDkvStage, q, dout, s_tok, len, (c + 1) * kChunkRows,
+                     qb, G, n_q, w, l);
+    const char* qh = st + rh * (32 * kD * 2);               // this wave's 32 rows of Q
+    const char* dh = st + kDkvQTile + rh * (32 * kD * 2);   // and of dO
+    const char* kk = kv_t + kt * 8192;
+    const char* vv = kv_t + kTileBytes + kt * 8192;
+    f32x16 sacc, pacc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      sacc[e] = 0.f;
+      pacc[e] = 0.f;
+    }
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      sacc = mfma32(lds_read_k(qh, r_lane ^ (ds << 5)), lds_read_k(kk, r_lane ^ (ds << 5)), sacc);
+      pacc = mfma32(lds_read_k(dh, r_lane ^ (ds << 5)), lds_read_k(vv, r_lane ^ (ds << 5)), pacc);
+    }
+    // register e of lane l: row 32*rh + 8*(e/4) + 4*hl + e%4 of the chunk,
+    // key 32*kt + r32 of the block
+    const int key = key0 + 32 * kt + r32;
+    bf16x8 pf[2], sf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      float pv[8], dv_[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int e = 8 * ks + jj;
+        const int rr = c * kChunkRows + 32 * rh + 8 * (e / 4) + 4 * hl + e % 4;   // segment row
+        const bool ok = rr < len * G && key <= P0 + s_tok[min(rr / G, len - 1)];
+        const float2 ld = s_row[min(rr, len * G - 1)];
+        const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[e], scale_log2, -ld.x)) : 0.f;
+        pv[jj] = p;
+        dv_[jj] = p * (pacc[e] - ld.y);
+      }
+      uint4 a, d;
+      a.x = cvt_pk_bf16(pv[0], pv[1]);   a.y = cvt_pk_bf16(pv[2], pv[3]);
+      a.z = cvt_pk_bf16(pv[4], pv[5]);   a.w = cvt_pk_bf16(pv[6], pv[7]);
+      d.x = cvt_pk_bf16(dv_[0], dv_[1]); d.y = cvt_pk_bf16(dv_[2], dv_[3]);
+      d.z = cvt_pk_bf16(dv_[4], dv_[5]); d.w = cvt_pk_bf16(dv_[6], dv_[7]);
+      pf[ks] = as_bf16x8(a);
+      sf[ks] = as_bf16x8(d);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS (rows of this half as the k dimension)
+    const lds_char* ql = (const lds_char*)qh;
+    const lds_char* dl = (const lds_char*)dh;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        dvacc[dt] = mfma32(lds_read_vt(dl + ks * 4096, t_lane[0] ^ (dt << 6), t_lane[1] ^ (dt << 6)),
+                           pf[ks], dvacc[dt]);
+        dkacc[dt] = mfma32(lds_read_vt(ql + ks * 4096, t_lane[0] ^ (dt << 6), t_lane[1] ^ (dt << 6)),
+                           sf[ks], dkacc[dt]);
+      }
+  }
+
+  // The two row halves' partial sums meet in LDS (the ring is free now):
+  // waves rh = 1 store, waves rh = 0 add and write out.
+  wait_vmem();
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(ring) + kt * (2 * DT * 16 * kWave);
+  if (rh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        red[(dt * 16 + e) * kWave + l] = dkacc[dt][e];
+        red[((DT + dt) * 16 + e) * kWave + l] = dvacc[dt][e];
+      }
+  }
+  __syncthreads();
+  if (rh == 0) {
+    // register e of lane l: d = 32*dt + 8*(e/4) + 4*hl + e%4, key 32*kt + r32
+    const int64_t keyg = key0 + 32 * kt + r32;
+    if (keyg < kv_len) {
+      float* dkr = dk + (int64_t(bg) * kv_cap + keyg) * kD;
+      float* dvr = dv + (int64_t(bg) * kv_cap + keyg) * kD;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          float a4[4], v4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = 4 * rb + i;
+            a4[i] = (dkacc[dt][e] + red[(dt * 16 + e) * kWave + l]) * scale;
+            v4[i] = dvacc[dt][e] + red[((DT + dt) * 16 + e) * kWave + l];
+          }
+          const int d0 = 32 * dt + 8 * rb + 4 * hl;
+          if (split) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              atomicAdd(dkr + d0 + i, a4[i]);
+              atomicAdd(dvr + d0 + i, v4[i]);
+            }
+          } else {
+            *reinterpret_cast<float4*>(dkr + d0) = make_float4(a4[0], a4[1], a4[2], a4[3]);
+            *reinterpret_cast<float4*>(dvr + d0) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+          }
+        }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launch
+size_t prefill_backward_workspace_bytes(const Dims& d, int n_q, int64_t kv_len) {
+  return bwd_layout(d, n_q, kv_len).total;
+}
+
+bool prefill_backward_ok(const Dims& d, int64_t kv_len) {
+  return d.D == kD && prefill128_stages(d, 0, kv_len) > 0;
+}
+
+template <int G>
+static hipError_t launch_bwd_t(const Dims& d, const uint16_t* q, int n_q, const uint16_t* k,
+                               const uint16_t* v, int64_t kv_cap, int64_t kv_len,
+                               const int32_t* idx, const uint16_t* out, const float* lse,
+                               const uint16_t* dout, float* dq, float* dk, float* dv, void* ws,
+                               hipStream_t s) {
+  const BwdLayout L = bwd_layout(d, n_q, kv_len);
+  char* w8 = static_cast<char*>(ws);
+  float* lse2 = reinterpret_cast<float*>(w8 + L.off_lse2);
+  float* delta = reinterpret_cast<float*>(w8 + L.off_delta);
+  int32_t* cnt = reinterpret_cast<int32_t*>(w8 + L.off_cnt);
+  int32_t* cur = reinterpret_cast<int32_t*>(w8 + L.off_cur);
+  int32_t* off = reinterpret_cast<int32_t*>(w8 + L.off_off);
+  int32_t* nseg = reinterpret_cast<int32_t*>(w8 + L.off_nseg);
+  int32_t* list = reinterpret_cast<int32_t*>(w8 + L.off_list);
+  int4* seg = reinterpret_cast<int4*>(w8 + L.off_seg);
+  const float sl2 = d.scale * 1.4426950408889634f;
+  hipError_t e;
+
+  // counters (cnt and cur are adjacent) and dk, dv rows < kv_len -> 0
+  const int64_t n16 = int64_t(L.off_off - L.off_cnt) / 16;
+  bwd_zero_kernel<<<dim3(unsigned(std::min<int64_t>(1024, (n16 + 255) / 256))), 256, 0, s>>>(
+      reinterpret_cast<uint4*>(cnt), n16);
+  bwd_zero_rows_kernel<<<dim3(2048), 256, 0, s>>>(dk, dv, kv_cap, kv_len, L.bgs);
+  bwd_prep_kernel<<<dim3(unsigned((L.rows + 15) / 16)), 256, 0, s>>>(out, dout, lse, lse2, delta,
+                                                                     L.rows);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  // dq: the forward's tiling
+  {
+    using Sh = PrefillShape<G>;
+    const int ntile = (n_q + Sh::TQ - 1) / Sh::TQ;
+    const int64_t umax = prefill_umax(d, 0, L.nblk);
+    auto kern = bwd_dq_kernel<G>;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       160 * 1024);
+    if (attr != hipSuccess) return attr;
+    kern<<<dim3(unsigned(L.bgs * ntile)), Sh::NT, prefill_lds(umax, Sh::TQ, d.K), s>>>(
+        q, k, v, idx, dout, lse2, delta, dq, d.Hq, d.Hkv, n_q, kv_cap, kv_len, d.K, d.dense_thr,
+        sl2, d.scale, ntile, int(umax));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+
+  // inverse index
+  const int ttiles = (n_q + 255) / 256;
+  bwd_count_kernel<<<dim3(unsigned(L.bgs * ttiles)), 256, 0, s>>>(idx, cnt, d.Hkv, n_q, kv_len,
+                                                                  d.K, d.dense_thr, L.nblk, ttiles);
+  bwd_scan_kernel<<<dim3(unsigned(L.bgs)), 256, 0, s>>>(cnt, off, seg, nseg, L.nblk, L.smax);
+  bwd_fill_kernel<<<dim3(unsigned(L.bgs * ttiles)), 256, 0, s>>>(
+      idx, off, cur, list, d.Hkv, n_q, kv_len, d.K, d.dense_thr, L.nblk, L.emax, ttiles);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  // dk, dv
+  {
+    auto kern = bwd_dkv_kernel<G>;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       160 * 1024);
+    if (attr != hipSuccess) return attr;
+    kern<<<dim3(unsigned(L.bgs * L.smax)), 256, kDkvLds, s>>>(
+        q, k, v, dout, lse2, delta, list, seg, nseg, dk, dv, d.Hq, d.Hkv, n_q, kv_cap, kv_len,
+        L.emax, L.smax, sl2, d.scale);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_backward(const Dims& d, const uint16_t* q, int n_q, const uint16_t* k,
+                                   const uint16_t* v, int64_t kv_cap, int64_t kv_len,
+                                   const int32_t* idx, const uint16_t* out, const float* lse,
+                                   const uint16_t* dout, float* dq, float* dk, float* dv, void* ws,
+                                   size_t ws_bytes, hipStream_t s) {
+  if (ws_bytes < bwd_layout(d, n_q, kv_len).total) return hipErrorInvalidValue;
+  switch (d.G) {
+#define BWD_CASE(GG)                                                                              \
+  case GG:                                                                                        \
+    return launch_bwd_t<GG>(d, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, dout, dq, dk, dv, ws, \
+                            s);
+    BWD_CASE(1) BWD_CASE(2) BWD_CASE(4) BWD_CASE(8) BWD_CASE(16)
+#undef BWD_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace infllmv2

@@ -54,4 +54,13 @@ hipError_t launch_decode(const Dims& d, const uint16_t* q, int n_q, const uint16
                          size_t ws_bytes, hipStream_t s, const float* scores = nullptr,
                          int32_t* idx_out = nullptr);
 
+// Backward of the head_dim-128 sparse prefill (mode 0): dq, dk, dv (fp32).
+bool prefill_backward_ok(const Dims& d, int64_t kv_len);
+size_t prefill_backward_workspace_bytes(const Dims& d, int n_q, int64_t kv_len);
+hipError_t launch_prefill_backward(const Dims& d, const uint16_t* q, int n_q, const uint16_t* k,
+                                   const uint16_t* v, int64_t kv_cap, int64_t kv_len,
+                                   const int32_t* idx, const uint16_t* out, const float* lse,
+                                   const uint16_t* dout, float* dq, float* dk, float* dv, void* ws,
+                                   size_t ws_bytes, hipStream_t s);
+
 }  // namespace infllmv2

@@ -60,6 +60,22 @@ def sparse_prefill(cfg, q, k, v, *, with_lse=True, stream=None):
     return dict(kbar=kbar, idx=idx, out=out, lse=lse)
 
 
+def sparse_prefill_backward(cfg, q, k, v, idx, out, lse, dout, *, kv_len=None, stream=None):
+    """Gradients of the sparse prefill: returns dq [B][Hq][n_q][D], dk and dv
+    [B][Hkv][kv_cap][D] (fp32; dk, dv rows past kv_len are zero here)."""
+    B, Hq, n_q, D = q.shape
+    kv_cap = k.shape[2]
+    kv_len = n_q if kv_len is None else kv_len
+    dq = torch.empty((B, Hq, n_q, D), dtype=torch.float32, device=q.device)
+    dk = torch.zeros((B, cfg.n_kv_heads, kv_cap, D), dtype=torch.float32, device=q.device)
+    dv = torch.zeros_like(dk)
+    nbytes = capi.infllmv2_prefill_backward_workspace_bytes(cfg, n_q, kv_len)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    capi.infllmv2_sparse_attn_prefill_backward(cfg, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, dout,
+                                               dq, dk, dv, ws, nbytes, stream)
+    return dict(dq=dq, dk=dk, dv=dv)
+
+
 def decode(cfg, q, k_cache, v_cache, kbar, kv_len, *, tree_mask=None, ws: Workspace | None = None,
            with_lse=True, stream=None):
     """n_q new tokens (tree nodes when tree_mask is given): scores -> top-K -> split attention."""
