@@ -8,7 +8,8 @@ sparse attention (split + LSE combine; infllmv2_sparse_attn_decode_scores,
 which selects inside the attention kernel) for the 8 new tokens, with k̄
 already built. A second leg times the
 32K causal sparse prefill (kernel pooling + fused score/top-K + attention) in
-TFLOP/s. Inputs are seeded synthetic tensors (synth) resident in HBM;
+TFLOP/s, and a third its backward (dq, dk, dv from the forward's selection,
+output and log-sum-exp for one upstream gradient) in TFLOP/s. Inputs are seeded synthetic tensors (synth) resident in HBM;
 decode steps rotate over independent copies of K, V and k̄ so that the
 256 MB last-level cache cannot serve a step from the previous one.
 
@@ -61,6 +62,13 @@ def prefill_flops(w) -> dict:
     return dict(attn=attn, score=score, total=attn + score)
 
 
+def backward_flops(w) -> float:
+    """Algorithmic flops of the sparse prefill backward: per (query head, attended key) pair the
+    score recompute q.k, dP = dO.v, and the three gradient products dV += P dO, dK += dS q,
+    dQ += dS k, each 2*D flops (10*D per pair, 2.5 times the forward attention)."""
+    return 2.5 * prefill_flops(w)["attn"]
+
+
 # ------------------------------------------------------------------ measured HBM traffic
 # Kernels launched by each timed entry point, and the sources their code comes from.
 ENTRY_KERNELS = {
@@ -72,6 +80,10 @@ ENTRY_KERNELS = {
     "sparse_attn_prefill": (("prefill_attn_kernel",), ("attn_prefill.hip",)),
     "topk_blocks_fused": (("topk_prefill_kernel", "topk_fused_kernel"),
                           ("topk.hip", "topk_prefill.hip", "topk_select.hpp")),
+    "sparse_attn_prefill_backward": (("bwd_zero_kernel", "bwd_zero_rows_kernel", "bwd_prep_kernel",
+                                      "bwd_dq_kernel", "bwd_count_kernel", "bwd_fill_kernel",
+                                      "bwd_scan_kernel", "bwd_dkv_kernel"),
+                                     ("attn_backward.hip", "prefill_tile.hpp")),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "trainable_block_sparse_infllm_amd", "csrc")
@@ -275,6 +287,40 @@ def bench_prefill(w, steps, warmup, torch, lib, ops, synth):
     return dict(ms=ms, stage_ms=stage_ms, flops=prefill_flops(w))
 
 
+def bench_prefill_backward(w, steps, warmup, torch, lib, ops, synth):
+    """Gradients of the sparse prefill (dq, dk, dv) for one upstream gradient dO, from the forward's
+    own selection, output and log-sum-exp, as one training step's attention backward."""
+    log(f"backward: generating {w.name} inputs and running the forward once (untimed)")
+    d = synth.generate(w, seed=0, threads=16)
+    cfg = lib.make_cfg(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, top_k=w.top_k,
+                       dense_threshold=w.dense_threshold)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    q, k, v = dev(d["q"]), dev(d["k"]), dev(d["v"])
+    T, kv_cap = w.seq_len, d["kv_cap"]
+    del d
+    B, Hq, Hkv, D = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
+    kbar = torch.zeros(ops.kbar_shape(B, Hkv, kv_cap, D), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((B, Hkv, T, w.top_k), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, Hq, T, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
+    lib.infllmv2_pool_kernels(cfg, k, kv_cap, T, 0, kbar, None)
+    lib.infllmv2_topk_blocks(cfg, None, q, kbar, T, 0, 0, kv_cap, idx, None)
+    lib.infllmv2_sparse_attn_prefill(cfg, q, T, k, v, kv_cap, T, idx, out, lse, None)
+    gen = torch.Generator(device="cuda").manual_seed(1)
+    dout = torch.randn((B, Hq, T, D), generator=gen, device="cuda").to(torch.bfloat16)
+    dq = torch.empty((B, Hq, T, D), dtype=torch.float32, device="cuda")
+    dk = torch.zeros((B, Hkv, kv_cap, D), dtype=torch.float32, device="cuda")
+    dv = torch.zeros_like(dk)
+    nbytes = lib.infllmv2_prefill_backward_workspace_bytes(cfg, T, T)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+    def step(s):
+        return [lambda: lib.infllmv2_sparse_attn_prefill_backward(cfg, q, T, k, v, kv_cap, T, idx, out, lse,
+                                                                  dout, dq, dk, dv, ws, nbytes, None)]
+    log(f"backward: timing {steps} steps after {warmup} warmup")
+    ms, _, _ = timed_loop(step, steps, warmup, torch)
+    return dict(ms=ms, flops=backward_flops(w), workspace_bytes=nbytes)
+
+
 # ------------------------------------------------------------------ CPU baseline (oracle)
 def cpu_baseline_decode(w, budget_s, synth):
     import oracle as orc
@@ -305,6 +351,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     ap.add_argument("--summarize-trace", metavar="DB",
@@ -394,6 +441,19 @@ def main():
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic("sparse_attn_prefill")},
+        }
+    if not args.no_prefill and not args.no_backward:
+        wp = synth.WORKLOADS["prefill_32k"]
+        bw = bench_prefill_backward(wp, max(3, args.steps // 5), max(1, args.warmup // 5), torch, lib, ops,
+                                    synth)
+        btf = bw["flops"] / (bw["ms"] * 1e-3) / 1e12
+        result["prefill_backward"] = {
+            "workload": wp.name, "ms_per_step": round(bw["ms"], 4), "algorithmic_gflop": round(bw["flops"] / 1e9, 2),
+            "workspace_bytes": bw["workspace_bytes"],
+            "roofline": {"bound": "mfma", "kernel": "sparse_attn_prefill_backward", "achieved": round(btf, 2),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(btf / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic("sparse_attn_prefill_backward")},
         }
     if args.copy_calibration:
         n = 1 << 30

@@ -193,9 +193,11 @@ INFLLMV2_API size_t infllmv2_prefill_backward_workspace_bytes(const infllmv2_cfg
  *   dq [B][Hq][n_q][D] fp32 (fully written); dk, dv [B][Hkv][kv_cap][D] fp32:
  *   rows < kv_len are written (zeros for keys no row attends), rows past
  *   kv_len are left untouched.
- *   The dk, dv sums of keys attended by more than 256 tokens are split over
- *   workgroups and added atomically, so their last bits may differ between
- *   runs. Requires head_dim 128 (else INFLLMV2_UNSUPPORTED); workspace of at
+ *   The dk, dv sums of a key block attended by more than 4096 query rows
+ *   (tokens x heads of the group) are split over workgroups and added with
+ *   fp32 atomics, so their last bits may differ between runs; dk and dv must
+ *   therefore be ordinary device memory (hipMalloc), not host or fine-grained
+ *   memory. Requires head_dim 128 (else INFLLMV2_UNSUPPORTED); workspace of at
  *   least infllmv2_prefill_backward_workspace_bytes(), no initial contents. */
 INFLLMV2_API int infllmv2_sparse_attn_prefill_backward(const infllmv2_cfg* cfg, const void* q,
                                           int32_t n_q, const void* k, const void* v,

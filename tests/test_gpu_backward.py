@@ -82,10 +82,42 @@ def test_prefill_backward_matches_oracle(case):
     run_backward(CASES[case])
 
 
-def test_prefill_backward_heavy_keys_split_atomically():
-    # every token attends the same few blocks (K covers all candidates early,
-    # and the planted blocks later): the lists of the first blocks exceed one
-    # 256-token segment, so their dk, dv are summed over several workgroups
-    w = W0.scaled(name="bwd_heavy", n_q_heads=8, n_kv_heads=2, head_dim=128, seq_len=1600, top_k=8,
-                  dense_threshold=0, n_plant=8)
-    run_backward(w)
+def _rows_per_block(idx, T, K, G, dense_threshold):
+    """Query rows (token x head of the group) attending each key block, from the selection."""
+    nblk = (T - 1) // 64 + 1
+    cnt = np.zeros((idx.shape[0], idx.shape[1], nblk), np.int64)
+    for b in range(idx.shape[0]):
+        for g in range(idx.shape[1]):
+            for t in range(T):
+                own = t // 64
+                if dense_threshold > 0 and t + 1 < dense_threshold:
+                    cnt[b, g, :own + 1] += 1
+                    continue
+                sel = [j for j in idx[b, g, t] if 0 <= j < own]
+                cnt[b, g, sel] += 1
+                cnt[b, g, own] += 1
+    return cnt * G
+
+
+HEAVY = {
+    # K = 16 covers every candidate for the first 1088 tokens, so block 0 is
+    # attended by more than 1024 tokens = 4096 rows of a 4-head group
+    "g4": W0.scaled(name="bwd_heavy_g4", n_q_heads=8, n_kv_heads=2, head_dim=128, seq_len=1600, top_k=16,
+                    dense_threshold=0, n_plant=8),
+    # 16 heads per group: 256 tokens already fill one segment
+    "g16": W0.scaled(name="bwd_heavy_g16", n_q_heads=16, n_kv_heads=1, head_dim=128, seq_len=1300, top_k=8,
+                     dense_threshold=0, n_plant=4),
+}
+
+
+@pytest.mark.parametrize("case", list(HEAVY))
+def test_prefill_backward_heavy_keys_split_atomically(case):
+    # blocks attended by more than one segment's 4096 query rows have their
+    # dk, dv summed over several workgroups with fp32 atomics
+    w = HEAVY[case]
+    g = run_backward(w)
+    cfg = cfg_of(w)
+    d = synth.generate(w, seed=0)
+    fw = ops.sparse_prefill(cfg, dev_bf16(d["q"]), dev_bf16(d["k"]), dev_bf16(d["v"]))
+    rows = _rows_per_block(fw["idx"].cpu().numpy(), w.seq_len, w.top_k, w.group, w.dense_threshold)
+    assert rows.max() > 4096, f"no block needs a split (max rows {rows.max()})"

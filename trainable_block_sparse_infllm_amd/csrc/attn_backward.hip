@@ -18,13 +18,18 @@
 //            accumulators (S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T with
 //            K^T from transpose reads of the K tile);
 //   index -- for every key block, the list of query tokens that attend it
-//            (counts, prefix sums, fill) and its split into segments;
+//            (per-tile LDS histograms, one global add per tile and block,
+//            prefix sums, fill) and its even split into segments of at most
+//            kSegRows query rows;
 //   dkv   -- key-centric: a workgroup owns one segment of one block's list;
-//            K and V of the block stay in LDS, chunks of 64 query rows (Q and
-//            dO) stream through a two-stage LDS ring, and dK^T, dV^T stay in
-//            MFMA accumulators (S = Q K^T, dP = dO V^T, dV^T += dO^T P,
-//            dK^T += Q^T dS with Q^T and dO^T from transpose reads). A block
-//            split into several segments adds its partial sums atomically.
+//            K and V of the block stay in LDS, chunks of 64 query rows (Q, dO
+//            and the rows' token, lse and Delta) stream through a three-stage
+//            LDS ring, and dK^T, dV^T stay in MFMA accumulators (S = Q K^T,
+//            dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS with Q^T and dO^T
+//            from transpose reads). A block split into several segments adds
+//            its partial sums atomically, so the fp32 summation order of dk
+//            and dv (and the order of each block's token list) can differ
+//            between runs.
 #include <algorithm>
 
 #include "common.hpp"
@@ -37,8 +42,10 @@ using namespace tile;
 
 namespace {
 
-constexpr int kSegTokens = 256;     // query tokens per dK/dV segment
+constexpr int kSegRows = 4096;      // query rows (token x head) per dK/dV segment, at most
 constexpr int kChunkRows = 64;      // query rows per dK/dV chunk (two 32-row halves)
+constexpr int kIdxTile = 1024;      // query tokens per index workgroup (4 per thread)
+constexpr int kHistMax = 16384;     // blocks per LDS histogram pass of the index kernels
 
 struct BwdLayout {
   int64_t rows, bgs, nblk, emax, smax;
@@ -54,7 +61,7 @@ BwdLayout bwd_layout(const Dims& d, int n_q, int64_t kv_len) {
   // threshold) every block up to its own
   const int64_t dense_blocks = d.dense_thr > 0 ? (int64_t(d.dense_thr) - 2) / kBlock + 1 : 0;
   L.emax = int64_t(n_q) * std::max<int64_t>(d.K + 1, dense_blocks);
-  L.smax = (L.emax + kSegTokens - 1) / kSegTokens + L.nblk;
+  L.smax = (L.emax * d.G + kSegRows - 1) / kSegRows + L.nblk;
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   size_t o = 0;
   L.off_lse2 = o;  o = al(o + size_t(L.rows) * 4);
@@ -311,54 +318,97 @@ __device__ __forceinline__ void for_each_block(const int32_t* __restrict__ idx_r
   f(own);
 }
 
+// One workgroup per (b, g) and tile of kIdxTile tokens, one pass per window of
+// kHistMax blocks: the tile's counts per block gather in an LDS histogram.
+// count adds each nonzero bin to the global count (one atomic per tile and
+// block instead of one per token); fill reserves the tile's run in each
+// block's list with one atomic and hands out slots in it from LDS.
+__device__ __forceinline__ void hist_tokens(const int32_t* __restrict__ idx, int32_t* hist, int bg,
+                                            int t0, int n_q, int64_t P0, int K, int dense_thr,
+                                            int j0, int nj, bool rank, int32_t* __restrict__ list) {
+  for (int x = 0; x < kIdxTile / 256; ++x) {
+    const int t = t0 + x * 256 + int(threadIdx.x);
+    if (t >= n_q) break;
+    for_each_block(idx + (int64_t(bg) * n_q + t) * K, K, P0 + t, dense_thr, [&](int j) {
+      const int b = j - j0;
+      if (b >= 0 && b < nj) {
+        const int o = atomicAdd(&hist[b], 1);
+        if (rank) list[o] = t;
+      }
+    });
+  }
+}
+
 __global__ __launch_bounds__(256) void bwd_count_kernel(const int32_t* __restrict__ idx,
-                                                        int32_t* __restrict__ cnt, int Hkv, int n_q,
+                                                        int32_t* __restrict__ cnt, int n_q,
                                                         int64_t kv_len, int K, int dense_thr,
                                                         int64_t nblk, int ttiles) {
+  extern __shared__ int32_t hist[];
   const int bg = blockIdx.x / ttiles;
-  const int t = (blockIdx.x % ttiles) * 256 + threadIdx.x;
-  if (t >= n_q) return;
-  const int64_t p = kv_len - n_q + t;
+  const int t0 = (blockIdx.x % ttiles) * kIdxTile;
+  const int64_t P0 = kv_len - n_q;
   int32_t* c = cnt + int64_t(bg) * nblk;
-  for_each_block(idx + (int64_t(bg) * n_q + t) * K, K, p, dense_thr,
-                 [&](int j) { atomicAdd(&c[j], 1); });
+  for (int64_t j0 = 0; j0 < nblk; j0 += kHistMax) {
+    const int nj = int(min<int64_t>(kHistMax, nblk - j0));
+    for (int b = threadIdx.x; b < nj; b += 256) hist[b] = 0;
+    __syncthreads();
+    hist_tokens(idx, hist, bg, t0, n_q, P0, K, dense_thr, int(j0), nj, false, nullptr);
+    __syncthreads();
+    for (int b = threadIdx.x; b < nj; b += 256)
+      if (hist[b] > 0) atomicAdd(&c[j0 + b], hist[b]);
+    __syncthreads();
+  }
 }
 
 __global__ __launch_bounds__(256) void bwd_fill_kernel(const int32_t* __restrict__ idx,
                                                        const int32_t* __restrict__ off,
                                                        int32_t* __restrict__ cur,
-                                                       int32_t* __restrict__ list, int Hkv, int n_q,
+                                                       int32_t* __restrict__ list, int n_q,
                                                        int64_t kv_len, int K, int dense_thr,
                                                        int64_t nblk, int64_t emax, int ttiles) {
+  extern __shared__ int32_t hist[];
   const int bg = blockIdx.x / ttiles;
-  const int t = (blockIdx.x % ttiles) * 256 + threadIdx.x;
-  if (t >= n_q) return;
-  const int64_t p = kv_len - n_q + t;
+  const int t0 = (blockIdx.x % ttiles) * kIdxTile;
+  const int64_t P0 = kv_len - n_q;
   const int32_t* o = off + int64_t(bg) * nblk;
   int32_t* c = cur + int64_t(bg) * nblk;
   int32_t* ls = list + int64_t(bg) * emax;
-  for_each_block(idx + (int64_t(bg) * n_q + t) * K, K, p, dense_thr,
-                 [&](int j) { ls[o[j] + atomicAdd(&c[j], 1)] = t; });
+  for (int64_t j0 = 0; j0 < nblk; j0 += kHistMax) {
+    const int nj = int(min<int64_t>(kHistMax, nblk - j0));
+    for (int b = threadIdx.x; b < nj; b += 256) hist[b] = 0;
+    __syncthreads();
+    hist_tokens(idx, hist, bg, t0, n_q, P0, K, dense_thr, int(j0), nj, false, nullptr);
+    __syncthreads();
+    for (int b = threadIdx.x; b < nj; b += 256) {
+      const int n = hist[b];
+      if (n > 0) hist[b] = o[j0 + b] + atomicAdd(&c[j0 + b], n);
+    }
+    __syncthreads();
+    hist_tokens(idx, hist, bg, t0, n_q, P0, K, dense_thr, int(j0), nj, true, ls);
+    __syncthreads();
+  }
 }
 
 // One workgroup per (b, g): exclusive prefix of the per-block counts (list
-// offsets) and the segment table: block j's list is cut into segments of at
-// most kSegTokens tokens, each entry (j, start, length, split flag).
+// offsets) and the segment table. Block j's n tokens (n*G rows) are cut into
+// ceil(n*G / kSegRows) segments of near-equal length, each entry (j, start,
+// length, split flag); a segment then holds at most kSegRows / G tokens.
 __global__ __launch_bounds__(256) void bwd_scan_kernel(const int32_t* __restrict__ cnt,
                                                        int32_t* __restrict__ off,
                                                        int4* __restrict__ seg,
                                                        int32_t* __restrict__ nseg, int64_t nblk,
-                                                       int64_t smax) {
+                                                       int64_t smax, int G) {
   __shared__ int s_a[256], s_b[256];
   const int bg = blockIdx.x;
   const int tid = threadIdx.x;
   const int per = int((nblk + 255) / 256);
   const int lo = min<int64_t>(nblk, int64_t(tid) * per), hi = min<int64_t>(nblk, lo + per);
   const int32_t* c = cnt + int64_t(bg) * nblk;
+  auto nsplit = [&](int n) { return int((int64_t(n) * G + kSegRows - 1) / kSegRows); };
   int ca = 0, cs = 0;
   for (int j = lo; j < hi; ++j) {
     ca += c[j];
-    cs += (c[j] + kSegTokens - 1) / kSegTokens;
+    cs += nsplit(c[j]);
   }
   s_a[tid] = ca;
   s_b[tid] = cs;
@@ -376,9 +426,11 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(const int32_t* __restrict
   for (int j = lo; j < hi; ++j) {
     off[int64_t(bg) * nblk + j] = pa;
     const int n = c[j];
-    const int ns = (n + kSegTokens - 1) / kSegTokens;
-    for (int x = 0; x < ns; ++x)
-      sg[ps + x] = make_int4(j, pa + x * kSegTokens, min(kSegTokens, n - x * kSegTokens), ns > 1);
+    const int ns = nsplit(n);
+    for (int x = 0; x < ns; ++x) {
+      const int s0 = int(int64_t(x) * n / ns), s1 = int(int64_t(x + 1) * n / ns);
+      sg[ps + x] = make_int4(j, pa + s0, s1 - s0, ns > 1);
+    }
     pa += n;
     ps += ns;
   }
@@ -386,30 +438,56 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(const int32_t* __restrict
 }
 
 // ------------------------------------------------------------------ dkv
-// LDS: K and V tiles of the block (swizzled like the ring stages), two
-// stages of Q and dO tiles (64 rows each), the segment's tokens and per-row
-// (lse2, Delta).
-constexpr int kDkvQTile = kChunkRows * kD * 2;          // 16 KB
-constexpr int kDkvStage = 2 * kDkvQTile;                // Q then dO
-constexpr int kDkvLds = kStageBytes + 2 * kDkvStage + kSegTokens * 4 + kSegTokens * 16 * 8 + 64;
+// LDS: K and V tiles of the block (swizzled like the ring stages), three
+// stages of (Q tile, dO tile, row metadata) for 64 query rows each, and the
+// segment's tokens. Row metadata: token, lse2 and Delta of rows 0..63.
+constexpr int kDkvStages = 3;
+constexpr int kDkvQTile = kChunkRows * kD * 2;                    // 16 KB
+constexpr int kDkvMeta = 3 * kChunkRows * 4;
+constexpr int kDkvStage = 2 * kDkvQTile + kDkvMeta;
+static_assert(kDkvStage % 16 == 0, "stage alignment");
 
-// Rows 0..63 of a chunk -> one stage: 16 chunks of 1 KB per tensor (rows
-// 4c..4c+3), lane l's 16 bytes land in slot l % 16 of row 4c + l/16 and it
-// fetches the global piece stored there; rows past the segment repeat its
-// last row (finite; their P and dS are zero).
+constexpr size_t dkv_lds(int G) {
+  return size_t(kStageBytes) + size_t(kDkvStages) * kDkvStage + size_t(kSegRows / G) * 4;
+}
+
+// Direct HBM -> LDS copy of 4 bytes per lane (lane l's word lands at
+// lds_base + 4 l).
+__device__ __forceinline__ void load_lds4(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((gas_void*)gsrc, (las_void*)lds_base, 4, 0, 0);
+}
+
+// Rows row0..row0+63 of the segment -> one stage. Tiles: 16 pieces of 1 KB per
+// tensor (rows 4c..4c+3); lane l's 16 bytes land in slot l % 16 of row
+// 4c + l/16 and it fetches the global piece stored there. Metadata: waves
+// 0, 1, 2 copy the token, lse2 and Delta of row l. Rows past the segment
+// repeat its last row (finite data; the mask drops them). Per stage a wave
+// issues 9 loads (waves 0..2) or 8 (wave 3).
 __device__ __forceinline__ void issue_qd_stage(char* stage, const uint16_t* q, const uint16_t* dout,
-                                               const int32_t* s_tok, int len, int row0, int64_t qb,
-                                               int G, int n_q, int w, int l) {
+                                               const int32_t* list_seg, const float* lse2,
+                                               const float* delta, const int32_t* s_tok, int len,
+                                               int row0, int64_t qb, int G, int n_q, int w, int l) {
 #pragma unroll
   for (int x = 0; x < 8; ++x) {
     const int c = x * 4 + w;                        // 0..31: tensor c / 16, row group c % 16
     const int row = 4 * (c % 16) + l / 16;
-    int rr = row0 + row;                            // (token slot, head) of the segment
+    const int rr = row0 + row;                      // (token slot, head) of the segment
     const int tslot = min(rr / G, len - 1);
     const int hh = rr % G;
-    const int64_t rid = (qb + hh) * n_q + s_tok[tslot];
+    const int64_t rid = (qb + hh) * n_q + lds_read(s_tok + tslot);
     const uint16_t* src = (c < 16 ? q : dout) + rid * kD + (((l % 16) ^ swz(row)) << 3);
     load_lds16(src, stage + c * 1024);
+  }
+  if (w < 3) {
+    const int rr = row0 + l;
+    const int tslot = min(rr / G, len - 1);
+    char* meta = stage + 2 * kDkvQTile + w * (kChunkRows * 4);
+    if (w == 0) {
+      load_lds4(list_seg + tslot, meta);
+    } else {
+      const int64_t rid = (qb + rr % G) * n_q + lds_read(s_tok + tslot);
+      load_lds4((w == 1 ? lse2 : delta) + rid, meta);
+    }
   }
 }
 
@@ -425,9 +503,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
   constexpr int DT = kD / 32;
   extern __shared__ __align__(16) char smem[];
   char* kv_t = smem;                                  // K tile, V tile
-  char* ring = smem + kStageBytes;                    // 2 stages x (Q tile, dO tile)
-  int32_t* s_tok = reinterpret_cast<int32_t*>(ring + 2 * kDkvStage);
-  float2* s_row = reinterpret_cast<float2*>(s_tok + kSegTokens);   // [kSegTokens*G] (lse2, Delta)
+  char* ring = smem + kStageBytes;                    // kDkvStages x (Q, dO, metadata)
+  int32_t* s_tok = reinterpret_cast<int32_t*>(ring + kDkvStages * kDkvStage);
 
   const int bg = blockIdx.x / int(smax);
   const int sidx = blockIdx.x % int(smax);
@@ -444,14 +521,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
   const int key0 = j * kBlock;
   const int64_t P0 = kv_len - n_q;
   const int64_t qb = int64_t(b) * Hq + int64_t(g) * G;      // first head row of the group
+  const int32_t* list_seg = list + int64_t(bg) * emax + start;
+  const int nrows = len * G;
 
-  // the segment's tokens and per-row (lse2, Delta)
-  for (int i = threadIdx.x; i < len; i += 256) s_tok[i] = list[int64_t(bg) * emax + start + i];
+  // the segment's tokens
+  for (int i = threadIdx.x; i < len; i += 256) s_tok[i] = list_seg[i];
   __syncthreads();
-  for (int i = threadIdx.x; i < len * G; i += 256) {
-    const int64_t rid = (qb + i % G) * n_q + s_tok[i / G];
-    s_row[i] = make_float2(lse2[rid], delta[rid]);
-  }
   // K and V of the block -> LDS (swizzled), rows past kv_len read as zeros
   {
     const uint16_t* kb = k + (int64_t(bg) * kv_cap) * kD;
@@ -468,8 +543,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
       load_lds16(src, kv_t + c * 1024);
     }
   }
-  const int nch = (len * G + kChunkRows - 1) / kChunkRows;
-  issue_qd_stage(ring, q, dout, s_tok, len, 0, qb, G, n_q, w, l);
+  const int nch = (nrows + kChunkRows - 1) / kChunkRows;
+  issue_qd_stage(ring, q, dout, list_seg, lse2, delta, s_tok, len, 0, qb, G, n_q, w, l);
+  if (nch > 1)
+    issue_qd_stage(ring + kDkvStage, q, dout, list_seg, lse2, delta, s_tok, len, kChunkRows, qb, G,
+                   n_q, w, l);
 
   f32x16 dkacc[DT], dvacc[DT];
 #pragma unroll
@@ -492,17 +570,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
     const int piece = 2 * ((l / 16) % 2) + (jj % 4) / 2;
     t_lane[qq] = row * (kD * 2) + ((piece ^ swz(row)) << 4) + 8 * (jj & 1);
   }
+  const int key = key0 + 32 * kt + r32;
 
   for (int c = 0; c < nch; ++c) {
-    wait_vmem();
+    // this wave's loads of chunk c (and K, V) landed: at most the next
+    // chunk's loads are still in flight
+    if (c + 1 < nch) {
+      if (w < 3) __builtin_amdgcn_s_waitcnt(0x0F79);            // vmcnt(9)
+      else __builtin_amdgcn_s_waitcnt(0x0F78);                  // vmcnt(8)
+    } else {
+      wait_vmem();
+    }
     wait_lds();
-    ring_barrier();                                 // chunk c (and K, V) landed; other slot free
-    char* const st = ring + (c & 1) * kDkvStage;
-    if (c + 1 < nch)
-      issue_qd_stage(ring + ((c + 1) & 1) * kDkvStage, q, dout, s_tok, len, (c + 1) * kChunkRows,
-                     qb, G, n_q, w, l);
+    ring_barrier();                                 // ... and every wave's; slot of c - 1 free
+    if (c + 2 < nch)
+      issue_qd_stage(ring + ((c + 2) % kDkvStages) * kDkvStage, q, dout, list_seg, lse2, delta,
+                     s_tok, len, (c + 2) * kChunkRows, qb, G, n_q, w, l);
+    char* const st = ring + (c % kDkvStages) * kDkvStage;
     const char* qh = st + rh * (32 * kD * 2);               // this wave's 32 rows of Q
     const char* dh = st + kDkvQTile + rh * (32 * kD * 2);   // and of dO
+    const char* meta = st + 2 * kDkvQTile;
     const char* kk = kv_t + kt * 8192;
     const char* vv = kv_t + kTileBytes + kt * 8192;
     f32x16 sacc, pacc;
@@ -516,22 +603,28 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
       sacc = mfma32(lds_read_k(qh, r_lane ^ (ds << 5)), lds_read_k(kk, r_lane ^ (ds << 5)), sacc);
       pacc = mfma32(lds_read_k(dh, r_lane ^ (ds << 5)), lds_read_k(vv, r_lane ^ (ds << 5)), pacc);
     }
-    // register e of lane l: row 32*rh + 8*(e/4) + 4*hl + e%4 of the chunk,
-    // key 32*kt + r32 of the block
-    const int key = key0 + 32 * kt + r32;
+    // register e of lane l: chunk row 32*rh + 8*(e/4) + 4*hl + e%4, key
+    // 32*kt + r32 of the block; rows 4m..4m+3 of the metadata are one read
     bf16x8 pf[2], sf[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       float pv[8], dv_[8];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int e = 8 * ks + jj;
-        const int rr = c * kChunkRows + 32 * rh + 8 * (e / 4) + 4 * hl + e % 4;   // segment row
-        const bool ok = rr < len * G && key <= P0 + s_tok[min(rr / G, len - 1)];
-        const float2 ld = s_row[min(rr, len * G - 1)];
-        const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sacc[e], scale_log2, -ld.x)) : 0.f;
-        pv[jj] = p;
-        dv_[jj] = p * (pacc[e] - ld.y);
+      for (int gq = 0; gq < 2; ++gq) {
+        const int row = 32 * rh + 8 * (2 * ks + gq) + 4 * hl;
+        const int4 tk = lds_read(reinterpret_cast<const int4*>(meta + row * 4));
+        const float4 ls = lds_read(reinterpret_cast<const float4*>(meta + kChunkRows * 4 + row * 4));
+        const float4 dl = lds_read(reinterpret_cast<const float4*>(meta + 2 * kChunkRows * 4 + row * 4));
+        const int tt[4] = {tk.x, tk.y, tk.z, tk.w};
+        const float lv[4] = {ls.x, ls.y, ls.z, ls.w}, dd[4] = {dl.x, dl.y, dl.z, dl.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 8 * ks + 4 * gq + i;
+          const bool ok = c * kChunkRows + row + i < nrows && key <= P0 + tt[i];
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[e], scale_log2, -lv[i]));
+          pv[4 * gq + i] = ok ? p : 0.f;
+          dv_[4 * gq + i] = ok ? p * (pacc[e] - dd[i]) : 0.f;
+        }
       }
       uint4 a, d;
       a.x = cvt_pk_bf16(pv[0], pv[1]);   a.y = cvt_pk_bf16(pv[2], pv[3]);
@@ -572,7 +665,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
   __syncthreads();
   if (rh == 0) {
     // register e of lane l: d = 32*dt + 8*(e/4) + 4*hl + e%4, key 32*kt + r32
-    const int64_t keyg = key0 + 32 * kt + r32;
+    const int64_t keyg = key;
     if (keyg < kv_len) {
       float* dkr = dk + (int64_t(bg) * kv_cap + keyg) * kD;
       float* dvr = dv + (int64_t(bg) * kv_cap + keyg) * kD;
@@ -589,10 +682,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
           }
           const int d0 = 32 * dt + 8 * rb + 4 * hl;
           if (split) {
+            // hardware fp32 add at L2 (the gradients live in ordinary
+            // coarse-grained device memory), not a compare-and-swap loop
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              atomicAdd(dkr + d0 + i, a4[i]);
-              atomicAdd(dvr + d0 + i, v4[i]);
+              unsafeAtomicAdd(dkr + d0 + i, a4[i]);
+              unsafeAtomicAdd(dvr + d0 + i, v4[i]);
             }
           } else {
             *reinterpret_cast<float4*>(dkr + d0) = make_float4(a4[0], a4[1], a4[2], a4[3]);
@@ -657,12 +752,13 @@ static hipError_t launch_bwd_t(const Dims& d, const uint16_t* q, int n_q, const 
   }
 
   // inverse index
-  const int ttiles = (n_q + 255) / 256;
-  bwd_count_kernel<<<dim3(unsigned(L.bgs * ttiles)), 256, 0, s>>>(idx, cnt, d.Hkv, n_q, kv_len,
-                                                                  d.K, d.dense_thr, L.nblk, ttiles);
-  bwd_scan_kernel<<<dim3(unsigned(L.bgs)), 256, 0, s>>>(cnt, off, seg, nseg, L.nblk, L.smax);
-  bwd_fill_kernel<<<dim3(unsigned(L.bgs * ttiles)), 256, 0, s>>>(
-      idx, off, cur, list, d.Hkv, n_q, kv_len, d.K, d.dense_thr, L.nblk, L.emax, ttiles);
+  const int ttiles = (n_q + kIdxTile - 1) / kIdxTile;
+  const size_t hist_lds = size_t(std::min<int64_t>(L.nblk, kHistMax)) * 4;
+  bwd_count_kernel<<<dim3(unsigned(L.bgs * ttiles)), 256, hist_lds, s>>>(
+      idx, cnt, n_q, kv_len, d.K, d.dense_thr, L.nblk, ttiles);
+  bwd_scan_kernel<<<dim3(unsigned(L.bgs)), 256, 0, s>>>(cnt, off, seg, nseg, L.nblk, L.smax, G);
+  bwd_fill_kernel<<<dim3(unsigned(L.bgs * ttiles)), 256, hist_lds, s>>>(
+      idx, off, cur, list, n_q, kv_len, d.K, d.dense_thr, L.nblk, L.emax, ttiles);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   // dk, dv
@@ -672,7 +768,7 @@ static hipError_t launch_bwd_t(const Dims& d, const uint16_t* q, int n_q, const 
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        160 * 1024);
     if (attr != hipSuccess) return attr;
-    kern<<<dim3(unsigned(L.bgs * L.smax)), 256, kDkvLds, s>>>(
+    kern<<<dim3(unsigned(L.bgs * L.smax)), 256, dkv_lds(G), s>>>(
         q, k, v, dout, lse2, delta, list, seg, nseg, dk, dv, d.Hq, d.Hkv, n_q, kv_cap, kv_len,
         L.emax, L.smax, sl2, d.scale);
   }
