@@ -438,17 +438,18 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(const int32_t* __restrict
 }
 
 // ------------------------------------------------------------------ dkv
-// LDS: K and V tiles of the block (swizzled like the ring stages), three
-// stages of (Q tile, dO tile, row metadata) for 64 query rows each, and the
-// segment's tokens. Row metadata: token, lse2 and Delta of rows 0..63.
-constexpr int kDkvStages = 3;
+// LDS: a four-slot ring of stages, each (Q tile, dO tile, row metadata) for
+// 64 query rows, then the segment's tokens. Row metadata: token, lse2 and
+// Delta of rows 0..63. K and V of the block live in registers as the B
+// fragments of S = Q K^T and dP = dO V^T.
+constexpr int kDkvSlots = 4;
 constexpr int kDkvQTile = kChunkRows * kD * 2;                    // 16 KB
 constexpr int kDkvMeta = 3 * kChunkRows * 4;
 constexpr int kDkvStage = 2 * kDkvQTile + kDkvMeta;
 static_assert(kDkvStage % 16 == 0, "stage alignment");
 
 constexpr size_t dkv_lds(int G) {
-  return size_t(kStageBytes) + size_t(kDkvStages) * kDkvStage + size_t(kSegRows / G) * 4;
+  return size_t(kDkvSlots) * kDkvStage + size_t(kSegRows / G) * 4;
 }
 
 // Direct HBM -> LDS copy of 4 bytes per lane (lane l's word lands at
@@ -457,37 +458,92 @@ __device__ __forceinline__ void load_lds4(const void* gsrc, void* lds_base) {
   __builtin_amdgcn_global_load_lds((gas_void*)gsrc, (las_void*)lds_base, 4, 0, 0);
 }
 
+// Wait until at most N vector-memory loads of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// +inf lse for rows past a segment: their P (and dS) come out exactly 0.
+static __device__ float kLsePad = INFINITY;
+
+// Per-lane constants of the stage loads. Load x (0..3) of tensor Q (dO:
+// x + 4) fills row 16x + 4w + l/16 of the tile; as G divides 64, that row's
+// head and token slot within a chunk are fixed: head row % G, slot
+// row0/G + row/G. Lane l also copies metadata row l (waves 0..2).
+struct StageLanes {
+  const char* qrow[4];     // q (bytes) at the row's head row, plus the lane's swizzled piece
+  int rowq[4];             // row / G
+  const char* mrow;        // wave 1: lse2, wave 2: Delta at the head row of metadata row l
+  int mq;                  // l / G
+  int mrr;                 // l
+};
+
+template <int G>
+__device__ __forceinline__ StageLanes stage_lanes(const uint16_t* q, const float* lse2,
+                                                  const float* delta, int64_t qb, int n_q, int w,
+                                                  int l) {
+  StageLanes s;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int row = 16 * x + 4 * w + l / 16;
+    s.qrow[x] = reinterpret_cast<const char*>(q) +
+                ((qb + row % G) * n_q * kD + (((l % 16) ^ swz(row)) << 3)) * 2;
+    s.rowq[x] = row / G;
+  }
+  s.mrow = reinterpret_cast<const char*>(w == 1 ? lse2 : delta) + (qb + l % G) * n_q * 4;
+  s.mq = l / G;
+  s.mrr = l;
+  return s;
+}
+
 // Rows row0..row0+63 of the segment -> one stage. Tiles: 16 pieces of 1 KB per
 // tensor (rows 4c..4c+3); lane l's 16 bytes land in slot l % 16 of row
 // 4c + l/16 and it fetches the global piece stored there. Metadata: waves
 // 0, 1, 2 copy the token, lse2 and Delta of row l. Rows past the segment
-// repeat its last row (finite data; the mask drops them). Per stage a wave
-// issues 9 loads (waves 0..2) or 8 (wave 3).
-__device__ __forceinline__ void issue_qd_stage(char* stage, const uint16_t* q, const uint16_t* dout,
-                                               const int32_t* list_seg, const float* lse2,
-                                               const float* delta, const int32_t* s_tok, int len,
-                                               int row0, int64_t qb, int G, int n_q, int w, int l) {
+// repeat its last row (finite data) with lse2 = +inf, which zeroes their P
+// and dS. Per stage a wave issues 9 loads (waves 0..2) or 8 (wave 3).
+__device__ __forceinline__ void issue_qd_stage(char* stage, const StageLanes& sl, int64_t dq_off,
+                                               const int32_t* list_seg, const int32_t* s_tok,
+                                               int lenm1, int nrows, int row0, int G, int w) {
+  const int cq = row0 / G;
+  // every token first, so the LDS reads are not held behind the direct loads
+  int tok[4];
 #pragma unroll
-  for (int x = 0; x < 8; ++x) {
-    const int c = x * 4 + w;                        // 0..31: tensor c / 16, row group c % 16
-    const int row = 4 * (c % 16) + l / 16;
-    const int rr = row0 + row;                      // (token slot, head) of the segment
-    const int tslot = min(rr / G, len - 1);
-    const int hh = rr % G;
-    const int64_t rid = (qb + hh) * n_q + lds_read(s_tok + tslot);
-    const uint16_t* src = (c < 16 ? q : dout) + rid * kD + (((l % 16) ^ swz(row)) << 3);
-    load_lds16(src, stage + c * 1024);
+  for (int x = 0; x < 4; ++x) tok[x] = lds_read(s_tok + min(cq + sl.rowq[x], lenm1));
+  const int tslot_m = min(cq + sl.mq, lenm1);
+  const int tok_m = lds_read(s_tok + tslot_m);
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const char* src = sl.qrow[x] + int64_t(uint32_t(tok[x])) * (kD * 2);
+    load_lds16(src, stage + (4 * x + w) * 1024);
+    load_lds16(src + dq_off, stage + (16 + 4 * x + w) * 1024);
   }
   if (w < 3) {
-    const int rr = row0 + l;
-    const int tslot = min(rr / G, len - 1);
     char* meta = stage + 2 * kDkvQTile + w * (kChunkRows * 4);
     if (w == 0) {
-      load_lds4(list_seg + tslot, meta);
+      load_lds4(list_seg + tslot_m, meta);
     } else {
-      const int64_t rid = (qb + rr % G) * n_q + lds_read(s_tok + tslot);
-      load_lds4((w == 1 ? lse2 : delta) + rid, meta);
+      const bool pad = w == 1 && row0 + sl.mrr >= nrows;
+      const void* src = pad ? static_cast<const void*>(&kLsePad)
+                            : static_cast<const void*>(sl.mrow + int64_t(uint32_t(tok_m)) * 4);
+      load_lds4(src, meta);
     }
+  }
+}
+
+// Waits of the ring, per wave: the loads of `after` later stages may stay in
+// flight (0, 1 or 2 stages of 9 or 8 loads).
+__device__ __forceinline__ void wait_stage(int after, int w) {
+  if (w < 3) {
+    if (after >= 2) wait_vmcnt<18>();
+    else if (after == 1) wait_vmcnt<9>();
+    else wait_vmcnt<0>();
+  } else {
+    if (after >= 2) wait_vmcnt<16>();
+    else if (after == 1) wait_vmcnt<8>();
+    else wait_vmcnt<0>();
   }
 }
 
@@ -502,9 +558,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
   constexpr int DS = kD / 16;
   constexpr int DT = kD / 32;
   extern __shared__ __align__(16) char smem[];
-  char* kv_t = smem;                                  // K tile, V tile
-  char* ring = smem + kStageBytes;                    // kDkvStages x (Q, dO, metadata)
-  int32_t* s_tok = reinterpret_cast<int32_t*>(ring + kDkvStages * kDkvStage);
+  char* ring = smem;                                  // kDkvSlots x (Q, dO, metadata)
+  int32_t* s_tok = reinterpret_cast<int32_t*>(ring + kDkvSlots * kDkvStage);
 
   const int bg = blockIdx.x / int(smax);
   const int sidx = blockIdx.x % int(smax);
@@ -518,36 +573,36 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
   const int r32 = l % 32, hl = l / 32;
   const int kt = w & 1;             // keys 32*kt .. of the block
   const int rh = w >> 1;            // rows 32*rh .. of each chunk
-  const int key0 = j * kBlock;
   const int64_t P0 = kv_len - n_q;
   const int64_t qb = int64_t(b) * Hq + int64_t(g) * G;      // first head row of the group
   const int32_t* list_seg = list + int64_t(bg) * emax + start;
   const int nrows = len * G;
+  const int key = j * kBlock + 32 * kt + r32;
+  const int kp = int(key - P0);     // a row of token t sees this key when kp <= t
 
+  // K and V B fragments: key `key`, piece 2*ds + hl (zeros past kv_len)
+  bf16x8 kf[DS], vf[DS];
+  {
+    const bool ok = key < kv_len;
+    const int64_t o = (int64_t(bg) * kv_cap + (ok ? key : 0)) * kD + 8 * hl;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      kf[ds] = as_bf16x8(ldg16_if(ok, k + o + 16 * ds));
+      vf[ds] = as_bf16x8(ldg16_if(ok, v + o + 16 * ds));
+    }
+  }
   // the segment's tokens
   for (int i = threadIdx.x; i < len; i += 256) s_tok[i] = list_seg[i];
   __syncthreads();
-  // K and V of the block -> LDS (swizzled), rows past kv_len read as zeros
-  {
-    const uint16_t* kb = k + (int64_t(bg) * kv_cap) * kD;
-    const uint16_t* vb = v + (int64_t(bg) * kv_cap) * kD;
-#pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      const int c = x * 4 + w;
-      const int row = 4 * (c % 16) + l / 16;
-      const int64_t key = key0 + row;
-      const void* src = key < kv_len
-                            ? static_cast<const void*>((c < 16 ? kb : vb) + key * kD +
-                                                       (((l % 16) ^ swz(row)) << 3))
-                            : static_cast<const void*>(kZeroPiece);
-      load_lds16(src, kv_t + c * 1024);
-    }
-  }
+
   const int nch = (nrows + kChunkRows - 1) / kChunkRows;
-  issue_qd_stage(ring, q, dout, list_seg, lse2, delta, s_tok, len, 0, qb, G, n_q, w, l);
-  if (nch > 1)
-    issue_qd_stage(ring + kDkvStage, q, dout, list_seg, lse2, delta, s_tok, len, kChunkRows, qb, G,
-                   n_q, w, l);
+  auto stage_of = [&](int c) { return ring + (c % kDkvSlots) * kDkvStage; };
+  const StageLanes sl = stage_lanes<G>(q, lse2, delta, qb, n_q, w, l);
+  const int64_t dq_off = reinterpret_cast<const char*>(dout) - reinterpret_cast<const char*>(q);
+#pragma unroll
+  for (int c = 0; c < 3; ++c)
+    if (c < nch)
+      issue_qd_stage(stage_of(c), sl, dq_off, list_seg, s_tok, len - 1, nrows, c * kChunkRows, G, w);
 
   f32x16 dkacc[DT], dvacc[DT];
 #pragma unroll
@@ -558,9 +613,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
       dvacc[dt][e] = 0.f;
     }
   // A fragments of S = Q K^T and dP = dO V^T: row 32*rh + r32, piece 2*ds + hl
-  // (offset r_lane ^ (ds << 5) within the half); B fragments: K / V row of key
-  // 32*kt + r32 (same addressing on the K / V tiles). Transpose fragments
-  // (dt, ks) of the Q / dO half: 4096*ks + (t_lane[q] ^ (dt << 6)).
+  // (offset r_lane ^ (ds << 5) within the half). Transpose fragments (dt, ks)
+  // of the Q / dO half: 4096*ks + (t_lane[q] ^ (dt << 6)).
   const int r_lane = r32 * (kD * 2) + ((hl ^ swz(r32)) << 4);
   int t_lane[2];
 #pragma unroll
@@ -570,29 +624,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
     const int piece = 2 * ((l / 16) % 2) + (jj % 4) / 2;
     t_lane[qq] = row * (kD * 2) + ((piece ^ swz(row)) << 4) + 8 * (jj & 1);
   }
-  const int key = key0 + 32 * kt + r32;
 
-  for (int c = 0; c < nch; ++c) {
-    // this wave's loads of chunk c (and K, V) landed: at most the next
-    // chunk's loads are still in flight
-    if (c + 1 < nch) {
-      if (w < 3) __builtin_amdgcn_s_waitcnt(0x0F79);            // vmcnt(9)
-      else __builtin_amdgcn_s_waitcnt(0x0F78);                  // vmcnt(8)
-    } else {
-      wait_vmem();
-    }
-    wait_lds();
-    ring_barrier();                                 // ... and every wave's; slot of c - 1 free
-    if (c + 2 < nch)
-      issue_qd_stage(ring + ((c + 2) % kDkvStages) * kDkvStage, q, dout, list_seg, lse2, delta,
-                     s_tok, len, (c + 2) * kChunkRows, qb, G, n_q, w, l);
-    char* const st = ring + (c % kDkvStages) * kDkvStage;
-    const char* qh = st + rh * (32 * kD * 2);               // this wave's 32 rows of Q
-    const char* dh = st + kDkvQTile + rh * (32 * kD * 2);   // and of dO
-    const char* meta = st + 2 * kDkvQTile;
-    const char* kk = kv_t + kt * 8192;
-    const char* vv = kv_t + kTileBytes + kt * 8192;
-    f32x16 sacc, pacc;
+  // S and dP of one chunk (this wave's 32 rows x 32 keys)
+  auto s_dp = [&](const char* st, f32x16& sacc, f32x16& pacc) __attribute__((always_inline)) {
+    const char* qh = st + rh * (32 * kD * 2);
+    const char* dh = st + kDkvQTile + rh * (32 * kD * 2);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       sacc[e] = 0.f;
@@ -600,30 +636,91 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
     }
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
-      sacc = mfma32(lds_read_k(qh, r_lane ^ (ds << 5)), lds_read_k(kk, r_lane ^ (ds << 5)), sacc);
-      pacc = mfma32(lds_read_k(dh, r_lane ^ (ds << 5)), lds_read_k(vv, r_lane ^ (ds << 5)), pacc);
+      sacc = mfma32(lds_read_k(qh, r_lane ^ (ds << 5)), kf[ds], sacc);
+      pacc = mfma32(lds_read_k(dh, r_lane ^ (ds << 5)), vf[ds], pacc);
+    }
+  };
+
+  f32x16 sacc, pacc;
+  wait_stage(min(nch - 1, 2), w);                    // chunk 0 landed
+  ring_barrier();
+  s_dp(stage_of(0), sacc, pacc);
+
+  for (int c = 0; c < nch; ++c) {
+    // chunk c + 1 landed (chunk c + 2 may still be in flight); every wave is
+    // done with chunk c - 1, whose slot takes chunk c + 3
+    wait_stage(c + 2 < nch ? 1 : 0, w);
+    wait_lds();
+    ring_barrier();
+    if (c + 3 < nch)
+      issue_qd_stage(stage_of(c + 3), sl, dq_off, list_seg, s_tok, len - 1, nrows,
+                     (c + 3) * kChunkRows, G, w);
+    const char* st = stage_of(c);
+    const char* sn = stage_of(c + 1);
+    // Reads first: A fragments of chunk c + 1 (past the last chunk: stale
+    // slot data, discarded), chunk c's row metadata and its Q^T, dO^T
+    // transpose fragments.
+    bf16x8 qa[DS], da[DS];
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      qa[ds] = lds_read_k(sn + rh * (32 * kD * 2), r_lane ^ (ds << 5));
+      da[ds] = lds_read_k(sn + kDkvQTile + rh * (32 * kD * 2), r_lane ^ (ds << 5));
     }
     // register e of lane l: chunk row 32*rh + 8*(e/4) + 4*hl + e%4, key
     // 32*kt + r32 of the block; rows 4m..4m+3 of the metadata are one read
+    const char* meta = st + 2 * kDkvQTile;
+    int4 tk[4];
+    float4 ls[4], dl4[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int row = 32 * rh + 8 * m + 4 * hl;
+      tk[m] = lds_read(reinterpret_cast<const int4*>(meta + row * 4));
+      ls[m] = lds_read(reinterpret_cast<const float4*>(meta + kChunkRows * 4 + row * 4));
+      dl4[m] = lds_read(reinterpret_cast<const float4*>(meta + 2 * kChunkRows * 4 + row * 4));
+    }
+    const lds_char* ql = (const lds_char*)(st + rh * (32 * kD * 2));
+    const lds_char* dl = (const lds_char*)(st + kDkvQTile + rh * (32 * kD * 2));
+    bf16x8 qt[DT][2], dtr[DT][2];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        dtr[dt][ks] = lds_read_vt(dl + ks * 4096, t_lane[0] ^ (dt << 6), t_lane[1] ^ (dt << 6));
+        qt[dt][ks] = lds_read_vt(ql + ks * 4096, t_lane[0] ^ (dt << 6), t_lane[1] ^ (dt << 6));
+      }
+
+    // S, dP of chunk c + 1
+    f32x16 sacc_n, pacc_n;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      sacc_n[e] = 0.f;
+      pacc_n[e] = 0.f;
+    }
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      sacc_n = mfma32(qa[ds], kf[ds], sacc_n);
+      pacc_n = mfma32(da[ds], vf[ds], pacc_n);
+    }
+
+    // P and dS of chunk c (bf16 B operands); rows past the segment have
+    // lse2 = +inf and so P = 0
     bf16x8 pf[2], sf[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       float pv[8], dv_[8];
 #pragma unroll
       for (int gq = 0; gq < 2; ++gq) {
-        const int row = 32 * rh + 8 * (2 * ks + gq) + 4 * hl;
-        const int4 tk = lds_read(reinterpret_cast<const int4*>(meta + row * 4));
-        const float4 ls = lds_read(reinterpret_cast<const float4*>(meta + kChunkRows * 4 + row * 4));
-        const float4 dl = lds_read(reinterpret_cast<const float4*>(meta + 2 * kChunkRows * 4 + row * 4));
-        const int tt[4] = {tk.x, tk.y, tk.z, tk.w};
-        const float lv[4] = {ls.x, ls.y, ls.z, ls.w}, dd[4] = {dl.x, dl.y, dl.z, dl.w};
+        const int m = 2 * ks + gq;
+        const int tt[4] = {tk[m].x, tk[m].y, tk[m].z, tk[m].w};
+        const float lv[4] = {ls[m].x, ls[m].y, ls[m].z, ls[m].w};
+        const float dd[4] = {dl4[m].x, dl4[m].y, dl4[m].z, dl4[m].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int e = 8 * ks + 4 * gq + i;
-          const bool ok = c * kChunkRows + row + i < nrows && key <= P0 + tt[i];
+          const int e = 4 * m + i;
           const float p = __builtin_amdgcn_exp2f(fmaf(sacc[e], scale_log2, -lv[i]));
-          pv[4 * gq + i] = ok ? p : 0.f;
-          dv_[4 * gq + i] = ok ? p * (pacc[e] - dd[i]) : 0.f;
+          const float pm = kp <= tt[i] ? p : 0.f;      // the key is past the row's position
+          pv[4 * gq + i] = pm;
+          dv_[4 * gq + i] = pm * (pacc[e] - dd[i]);
         }
       }
       uint4 a, d;
@@ -635,17 +732,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
       sf[ks] = as_bf16x8(d);
     }
     // dV^T += dO^T P and dK^T += Q^T dS (rows of this half as the k dimension)
-    const lds_char* ql = (const lds_char*)qh;
-    const lds_char* dl = (const lds_char*)dh;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        dvacc[dt] = mfma32(lds_read_vt(dl + ks * 4096, t_lane[0] ^ (dt << 6), t_lane[1] ^ (dt << 6)),
-                           pf[ks], dvacc[dt]);
-        dkacc[dt] = mfma32(lds_read_vt(ql + ks * 4096, t_lane[0] ^ (dt << 6), t_lane[1] ^ (dt << 6)),
-                           sf[ks], dkacc[dt]);
+        dvacc[dt] = mfma32(dtr[dt][ks], pf[ks], dvacc[dt]);
+        dkacc[dt] = mfma32(qt[dt][ks], sf[ks], dkacc[dt]);
       }
+    // A-fragment and metadata reads, then the S, dP MFMAs of chunk c + 1
+    // interleaved with chunk c's softmax and the transpose reads, then the
+    // dV, dK MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 28, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x002, 60, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    sacc = sacc_n;
+    pacc = pacc_n;
   }
 
   // The two row halves' partial sums meet in LDS (the ring is free now):
@@ -663,38 +770,35 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
       }
   }
   __syncthreads();
-  if (rh == 0) {
+  if (rh == 0 && key < kv_len) {
     // register e of lane l: d = 32*dt + 8*(e/4) + 4*hl + e%4, key 32*kt + r32
-    const int64_t keyg = key;
-    if (keyg < kv_len) {
-      float* dkr = dk + (int64_t(bg) * kv_cap + keyg) * kD;
-      float* dvr = dv + (int64_t(bg) * kv_cap + keyg) * kD;
+    float* dkr = dk + (int64_t(bg) * kv_cap + key) * kD;
+    float* dvr = dv + (int64_t(bg) * kv_cap + key) * kD;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          float a4[4], v4[4];
+      for (int rb = 0; rb < 4; ++rb) {
+        float a4[4], v4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 4 * rb + i;
+          a4[i] = (dkacc[dt][e] + red[(dt * 16 + e) * kWave + l]) * scale;
+          v4[i] = dvacc[dt][e] + red[((DT + dt) * 16 + e) * kWave + l];
+        }
+        const int d0 = 32 * dt + 8 * rb + 4 * hl;
+        if (split) {
+          // hardware fp32 add at L2 (the gradients live in ordinary
+          // coarse-grained device memory), not a compare-and-swap loop
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int e = 4 * rb + i;
-            a4[i] = (dkacc[dt][e] + red[(dt * 16 + e) * kWave + l]) * scale;
-            v4[i] = dvacc[dt][e] + red[((DT + dt) * 16 + e) * kWave + l];
+            unsafeAtomicAdd(dkr + d0 + i, a4[i]);
+            unsafeAtomicAdd(dvr + d0 + i, v4[i]);
           }
-          const int d0 = 32 * dt + 8 * rb + 4 * hl;
-          if (split) {
-            // hardware fp32 add at L2 (the gradients live in ordinary
-            // coarse-grained device memory), not a compare-and-swap loop
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              unsafeAtomicAdd(dkr + d0 + i, a4[i]);
-              unsafeAtomicAdd(dvr + d0 + i, v4[i]);
-            }
-          } else {
-            *reinterpret_cast<float4*>(dkr + d0) = make_float4(a4[0], a4[1], a4[2], a4[3]);
-            *reinterpret_cast<float4*>(dvr + d0) = make_float4(v4[0], v4[1], v4[2], v4[3]);
-          }
+        } else {
+          *reinterpret_cast<float4*>(dkr + d0) = make_float4(a4[0], a4[1], a4[2], a4[3]);
+          *reinterpret_cast<float4*>(dvr + d0) = make_float4(v4[0], v4[1], v4[2], v4[3]);
         }
-    }
+      }
   }
 }
 

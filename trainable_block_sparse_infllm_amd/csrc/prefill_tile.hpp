@@ -23,7 +23,17 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) char lds_char;
 
-__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// Tile rows are 256 bytes = 16 pieces of 16 bytes; row r stores logical piece
+// p at physical piece p ^ swz(r). swz permutes the bits of r % 16 (so
+// swz(r + 16) = swz(r)) such that both read patterns of a tile hit distinct
+// LDS banks per phase, for 128- and 256-byte-per-clock LDS alike:
+//   row reads (16 bytes of one piece from each of 16 consecutive rows):
+//     swz is a bijection on 0..15 and on 0..7 modulo 8;
+//   transpose reads (pieces 0..3 of four consecutive rows 4a..4a+3):
+//     bits 2-3, and bits 1-2, of swz differ across the four rows.
+__device__ __forceinline__ int swz(int r) {
+  return ((r >> 2) & 1) | (r & 2) | ((r & 1) << 2) | ((((r >> 1) ^ (r >> 3)) & 1) << 3);
+}
 
 // Shape of one instance: TPS tokens per wavefront (32 MFMA rows), NW
 // wavefronts, TQ tokens per workgroup, LPS direct loads per thread per stage.
