@@ -36,7 +36,8 @@
 //      taken from the S^T accumulators without data movement).
 //
 // LDS tiles are row-major 64 x 128 bf16 whose 16-byte pieces are XOR-swizzled
-// per row by swz(r) = ((r & 7) << 1) | ((r >> 3) & 1).
+// per row by swz(r) (prefill_tile.hpp), which keeps both the row reads of K
+// and the transpose reads of V free of bank conflicts.
 #include <algorithm>
 #include <type_traits>
 
