@@ -8,8 +8,10 @@ sparse attention (split + LSE combine; infllmv2_sparse_attn_decode_scores,
 which selects inside the attention kernel) for the 8 new tokens, with k̄
 already built. A second leg times the
 32K causal sparse prefill (kernel pooling + fused score/top-K + attention) in
-TFLOP/s, and a third its backward (dq, dk, dv from the forward's selection,
-output and log-sum-exp for one upstream gradient) in TFLOP/s. Inputs are seeded synthetic tensors (synth) resident in HBM;
+TFLOP/s, a third its backward (dq, dk, dv from the forward's selection,
+output and log-sum-exp for one upstream gradient) in TFLOP/s, and a fourth the
+draft model's sliding-window attention (2048 keys) over the same prompt.
+Inputs are seeded synthetic tensors (synth) resident in HBM;
 decode steps rotate over independent copies of K, V and k̄ so that the
 256 MB last-level cache cannot serve a step from the previous one.
 
@@ -60,6 +62,16 @@ def prefill_flops(w) -> dict:
     attn = float((4 * D * Hq * keys).sum()) * w.batch
     score = float((2 * D * Hq * 3 * C[C > w.top_k]).sum()) * w.batch
     return dict(attn=attn, score=score, total=attn + score)
+
+
+WINDOW = 2048   # sliding-window width of the draft-model leg (the pages give no size)
+
+
+def window_flops(w, window: int) -> float:
+    """Algorithmic flops of sliding-window causal attention over the prompt: 4*D per (query
+    head, attended key), a query at position t attending min(t + 1, window) keys."""
+    t = np.arange(w.seq_len, dtype=np.int64)
+    return float(4 * w.head_dim * w.n_q_heads * np.minimum(t + 1, window).sum()) * w.batch
 
 
 def backward_flops(w) -> float:
@@ -321,6 +333,25 @@ def bench_prefill_backward(w, steps, warmup, torch, lib, ops, synth):
     return dict(ms=ms, flops=backward_flops(w), workspace_bytes=nbytes)
 
 
+def bench_window(w, window, steps, warmup, torch, lib, ops, synth):
+    """The draft model's attention: sliding-window causal attention over the whole prompt."""
+    log(f"window: generating {w.name} inputs")
+    d = synth.generate(w, seed=0, threads=16)
+    cfg = lib.make_cfg(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, top_k=w.top_k,
+                       dense_threshold=w.dense_threshold)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    q, k, v = dev(d["q"]), dev(d["k"]), dev(d["v"])
+    T, kv_cap = w.seq_len, d["kv_cap"]
+    del d
+    out = torch.empty((w.batch, w.n_q_heads, T, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    def step(s):
+        return [lambda: lib.infllmv2_sliding_window_attn(cfg, q, T, k, v, kv_cap, T, window, out, None,
+                                                         None)]
+    log(f"window: timing {steps} steps after {warmup} warmup")
+    ms, _, _ = timed_loop(step, steps, warmup, torch)
+    return dict(ms=ms, flops=window_flops(w, window))
+
+
 # ------------------------------------------------------------------ CPU baseline (oracle)
 def cpu_baseline_decode(w, budget_s, synth):
     import oracle as orc
@@ -352,6 +383,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-window", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     ap.add_argument("--summarize-trace", metavar="DB",
@@ -454,6 +486,18 @@ def main():
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(btf / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic("sparse_attn_prefill_backward")},
+        }
+    if not args.no_prefill and not args.no_window:
+        wp = synth.WORKLOADS["prefill_32k"]
+        sw = bench_window(wp, WINDOW, max(3, args.steps // 5), max(1, args.warmup // 5), torch, lib, ops,
+                          synth)
+        wtf = sw["flops"] / (sw["ms"] * 1e-3) / 1e12
+        result["sliding_window"] = {
+            "workload": f"{wp.name}, window {WINDOW}", "ms_per_step": round(sw["ms"], 4),
+            "algorithmic_gflop": round(sw["flops"] / 1e9, 2),
+            "roofline": {"bound": "mfma", "kernel": "sliding_window_attn", "achieved": round(wtf, 2),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(wtf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
         }
     if args.copy_calibration:
         n = 1 << 30

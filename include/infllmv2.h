@@ -215,6 +215,19 @@ INFLLMV2_API int infllmv2_dense_attn(const infllmv2_cfg* cfg, const void* q, int
                         const void* v, int64_t kv_cap, int64_t kv_len, int32_t causal, void* out,
                         float* lse, void* stream);
 
+/* Sliding-window causal attention: query i at position p = kv_len - n_q + i
+ * attends keys max(0, p - window + 1) .. p (QbitAI summary, section on fusing
+ * speculative sampling, quantization and long-context algorithms: the draft
+ * model uses sliding-window attention while the target model uses the sparse
+ * kernels). Serves both a draft prefill (n_q = prompt length) and its decode
+ * steps (n_q = 1 with the new token's K/V already in the cache). Layouts as
+ * infllmv2_dense_attn; top_k and dense_threshold are ignored; window >= 1
+ * (values above kv_len act as kv_len, i.e. dense causal). Requires head_dim
+ * 128 (else INFLLMV2_UNSUPPORTED). */
+INFLLMV2_API int infllmv2_sliding_window_attn(const infllmv2_cfg* cfg, const void* q, int32_t n_q,
+                                 const void* k, const void* v, int64_t kv_cap, int64_t kv_len,
+                                 int64_t window, void* out, float* lse, void* stream);
+
 /* Static text for a status code. */
 INFLLMV2_API const char* infllmv2_strerror(int status);
 

@@ -21,7 +21,7 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-MODE_SPARSE, MODE_TREE, MODE_CAUSAL, MODE_FULL = 0, 1, 2, 3
+MODE_SPARSE, MODE_TREE, MODE_CAUSAL, MODE_FULL, MODE_WINDOW = 0, 1, 2, 3, 4
 
 
 def build(force: bool = True) -> str:
@@ -64,13 +64,13 @@ def lib():
         L.orc_select.restype = i32
         L.orc_select.argtypes = [i32, P, i64, P, i32, P]
         L.orc_keyset.restype = i64
-        L.orc_keyset.argtypes = [i32, i32, i64, i64, P, i32, i32, C.c_uint64, P]
+        L.orc_keyset.argtypes = [i32, i32, i64, i64, P, i32, i32, C.c_uint64, i64, P]
         L.orc_attend.restype = i32
         L.orc_attend.argtypes = [i32, i32, i32, i32, i32, i32, P, i32, P, P, P, i64, i64,
-                                 P, i32, i32, P, dbl, i32, P, P, P, P]
+                                 P, i32, i32, i64, P, dbl, i32, P, P, P, P]
         L.orc_attend_backward.restype = i32
         L.orc_attend_backward.argtypes = [i32, i32, i32, i32, i32, i32, P, i32, P, P, P, i64, i64,
-                                          P, i32, i32, P, dbl, P, P, P, P]
+                                          P, i32, i32, i64, P, dbl, P, P, P, P]
         _lib = L
     return _lib
 
@@ -149,17 +149,19 @@ def select(R: np.ndarray, Cn: np.ndarray, K: int) -> np.ndarray:
 
 
 def keyset(mode: int, p: int, kv_len: int, sel, K: int, dense_threshold: int,
-           mask: int = 0, bs: int = 64) -> np.ndarray:
+           mask: int = 0, bs: int = 64, window: int = 0) -> np.ndarray:
     keys = np.empty(kv_len + 64, dtype=np.int64)
     s = None if sel is None else _c(sel, np.int32)
-    n = lib().orc_keyset(mode, bs, p, kv_len, _ptr(s), K, dense_threshold, int(mask), _ptr(keys))
+    n = lib().orc_keyset(mode, bs, p, kv_len, _ptr(s), K, dense_threshold, int(mask), int(window),
+                         _ptr(keys))
     if n < 0:
         raise ValueError("orc_keyset rejected its arguments")
     return keys[:n].copy()
 
 
 def attend(mode: int, q, k, v, pos, kv_len: int, rows, n_kv_heads: int, *, idx=None, K: int = 0,
-           dense_threshold: int = 0, tree_mask=None, scale: float | None = None, bs: int = 64):
+           dense_threshold: int = 0, tree_mask=None, scale: float | None = None, bs: int = 64,
+           window: int = 0):
     """Attention rows (b, h, i): returns out [n, D] fp64, lse [n], attended-key counts [n]."""
     q = _c(q, np.uint16)
     k = _c(k, np.uint16)
@@ -179,7 +181,8 @@ def attend(mode: int, q, k, v, pos, kv_len: int, rows, n_kv_heads: int, *, idx=N
     lse = np.empty(len(rows), dtype=np.float64)
     nk = np.empty(len(rows), dtype=np.int64)
     rc = lib().orc_attend(mode, B, Hq, n_kv_heads, D, bs, _ptr(q), n_q, _ptr(pos), _ptr(k), _ptr(v),
-                          cap, kv_len, _ptr(idx), K, dense_threshold, _ptr(tree_mask), float(scale),
+                          cap, kv_len, _ptr(idx), K, dense_threshold, int(window), _ptr(tree_mask),
+                          float(scale),
                           len(rows), _ptr(rows), _ptr(out), _ptr(lse), _ptr(nk))
     if rc:
         raise ValueError("orc_attend rejected its arguments")
@@ -188,7 +191,7 @@ def attend(mode: int, q, k, v, pos, kv_len: int, rows, n_kv_heads: int, *, idx=N
 
 def attend_backward(mode: int, q, k, v, pos, kv_len: int, n_kv_heads: int, dout, *, idx=None,
                     K: int = 0, dense_threshold: int = 0, tree_mask=None, scale: float | None = None,
-                    bs: int = 64):
+                    bs: int = 64, window: int = 0):
     """Gradients of sum(dout * o) over every row (b, h, i) of `q`, with the key sets of
     `attend`: returns dq [B][Hq][n_q][D], dk and dv [B][Hkv][kv_cap][D], all fp64."""
     q = _c(q, np.uint16)
@@ -209,7 +212,7 @@ def attend_backward(mode: int, q, k, v, pos, kv_len: int, n_kv_heads: int, dout,
     dk = np.empty((B, n_kv_heads, cap, D), dtype=np.float64)
     dv = np.empty((B, n_kv_heads, cap, D), dtype=np.float64)
     rc = lib().orc_attend_backward(mode, B, Hq, n_kv_heads, D, bs, _ptr(q), n_q, _ptr(pos), _ptr(k),
-                                   _ptr(v), cap, kv_len, _ptr(idx), K, dense_threshold,
+                                   _ptr(v), cap, kv_len, _ptr(idx), K, dense_threshold, int(window),
                                    _ptr(tree_mask), float(scale), _ptr(dout), _ptr(dq), _ptr(dk),
                                    _ptr(dv))
     if rc:
@@ -264,4 +267,19 @@ def dense_forward(q, k, v, *, kv_len: int, n_kv_heads: int, causal: bool = True,
         rows = np.stack([b.ravel(), h.ravel(), i.ravel()], 1).astype(np.int32)
     out, lse, nk = attend(MODE_CAUSAL if causal else MODE_FULL, q, k, v, pos, kv_len, rows,
                           n_kv_heads, scale=scale, bs=bs)
+    return dict(out=out, lse=lse, nkeys=nk, rows=rows, pos=pos)
+
+
+def window_forward(q, k, v, *, kv_len: int, n_kv_heads: int, window: int, rows=None, scale=None,
+                   bs: int = 64):
+    """Sliding-window causal attention (the draft model's): query i sits at position
+    kv_len - n_q + i and attends keys max(0, p - window + 1) .. p."""
+    q = _c(q, np.uint16)
+    B, Hq, n_q, D = q.shape
+    pos = positions("prefill", n_q, kv_len - n_q)
+    if rows is None:
+        b, h, i = np.meshgrid(np.arange(B), np.arange(Hq), np.arange(n_q), indexing="ij")
+        rows = np.stack([b.ravel(), h.ravel(), i.ravel()], 1).astype(np.int32)
+    out, lse, nk = attend(MODE_WINDOW, q, k, v, pos, kv_len, rows, n_kv_heads, scale=scale, bs=bs,
+                          window=window)
     return dict(out=out, lse=lse, nkeys=nk, rows=rows, pos=pos)

@@ -232,11 +232,19 @@ int orc_select(int n_rows, const double* R, int64_t nblk_cap, const int64_t* C,
  *   keys bs*floor(P/bs) .. P-1. Both: tree slots P+j for every set bit j.
  * mode 2 (dense causal): keys 0..p.
  * mode 3 (dense, no mask): keys 0..kv_len-1.
+ * mode 4 (sliding window, [FUSE]: the draft model's attention): the last
+ *   `window` positions up to the row's own, keys max(0, p - window + 1)..p.
  * Writes ascending key positions to keys[], returns their count (or -1). */
 int64_t orc_keyset(int mode, int bs, int64_t p, int64_t kv_len,
                    const int32_t* sel, int K, int dense_threshold,
-                   uint64_t mask, int64_t* keys) {
+                   uint64_t mask, int64_t window, int64_t* keys) {
   int64_t n = 0;
+  if (mode == 4) {
+    if (window < 1) return -1;
+    for (int64_t t = p - window + 1 < 0 ? 0 : p - window + 1; t <= p && t < kv_len; ++t)
+      keys[n++] = t;
+    return n;
+  }
   if (mode == 3) {
     for (int64_t t = 0; t < kv_len; ++t) keys[n++] = t;
     return n;
@@ -296,7 +304,7 @@ int64_t orc_keyset(int mode, int bs, int64_t p, int64_t kv_len,
 int orc_attend(int mode, int B, int Hq, int Hkv, int D, int bs,
                const uint16_t* q, int n_q, const int64_t* pos,
                const uint16_t* k, const uint16_t* v, int64_t kv_cap, int64_t kv_len,
-               const int32_t* idx, int K, int dense_threshold,
+               const int32_t* idx, int K, int dense_threshold, int64_t window,
                const uint64_t* tree_mask, double scale,
                int n_rows, const int32_t* rows,
                double* out, double* lse, int64_t* nkeys) {
@@ -314,7 +322,7 @@ int orc_attend(int mode, int B, int Hq, int Hkv, int D, int bs,
       const int g = h / G;
       const int32_t* sel = idx ? &idx[(((int64_t)b * Hkv + g) * n_q + i) * K] : NULL;
       const uint64_t msk = tree_mask ? tree_mask[(int64_t)b * n_q + i] : 0ull;
-      int64_t n = orc_keyset(mode, bs, pos[i], kv_len, sel, K, dense_threshold, msk, keys);
+      int64_t n = orc_keyset(mode, bs, pos[i], kv_len, sel, K, dense_threshold, msk, window, keys);
       if (n <= 0) { bad = 1; nkeys[r] = n; continue; }
       nkeys[r] = n;
       const uint16_t* qv = &q[(((int64_t)b * Hq + h) * n_q + i) * D];
@@ -357,7 +365,7 @@ int orc_attend(int mode, int B, int Hq, int Hkv, int D, int bs,
 int orc_attend_backward(int mode, int B, int Hq, int Hkv, int D, int bs,
                         const uint16_t* q, int n_q, const int64_t* pos,
                         const uint16_t* k, const uint16_t* v, int64_t kv_cap, int64_t kv_len,
-                        const int32_t* idx, int K, int dense_threshold,
+                        const int32_t* idx, int K, int dense_threshold, int64_t window,
                         const uint64_t* tree_mask, double scale, const uint16_t* dout,
                         double* dq, double* dk, double* dv) {
   if (Hq % Hkv || kv_len > kv_cap) return -1;
@@ -380,7 +388,8 @@ int orc_attend_backward(int mode, int B, int Hq, int Hkv, int D, int bs,
         for (int i = 0; i < n_q; ++i) {
           const int32_t* sel = idx ? &idx[(((int64_t)b * Hkv + g) * n_q + i) * K] : NULL;
           const uint64_t msk = tree_mask ? tree_mask[(int64_t)b * n_q + i] : 0ull;
-          const int64_t n = orc_keyset(mode, bs, pos[i], kv_len, sel, K, dense_threshold, msk, keys);
+          const int64_t n = orc_keyset(mode, bs, pos[i], kv_len, sel, K, dense_threshold, msk, window,
+                                       keys);
           if (n <= 0) { bad = 1; continue; }
           const uint16_t* qv = &q[(((int64_t)b * Hq + h) * n_q + i) * D];
           const uint16_t* gv = &dout[(((int64_t)b * Hq + h) * n_q + i) * D];

@@ -104,6 +104,10 @@ CASES = [
     ("infllmv2_dense_attn", {}, (A, 1, A, A, 64, 0, 1, B, None, None), -1, "kv_len"),
     ("infllmv2_dense_attn", {}, (A, 1, A, None, 64, 64, 1, B, None, None), -1, "v is NULL"),
     ("infllmv2_dense_attn", dict(softmax_scale=float("nan")), (A, 1, A, A, 64, 64, 1, B, None, None), -1, "finite"),
+    ("infllmv2_sliding_window_attn", {}, (A, 1, A, A, 64, 64, 0, B, None, None), -1, "window"),
+    ("infllmv2_sliding_window_attn", {}, (A, 65, A, A, 64, 64, 16, B, None, None), -1, "n_q"),
+    ("infllmv2_sliding_window_attn", {}, (A, 1, A, A, 64, 64, 16, None, None, None), -1, "out is NULL"),
+    ("infllmv2_sliding_window_attn", dict(head_dim=64), (A, 1, A, A, 64, 64, 16, B, None, None), -2, "head_dim 128"),
 ]
 
 

@@ -39,6 +39,10 @@ MUTANTS = {
                                  "    if (dense_threshold > 0 && n_ctx <= dense_threshold) {\n      for (int64_t t = 0; t <= p; ++t)"),
     "tree_drops_prefix_tail": ("for (int64_t t = own * bs; t < P; ++t) keys[n++] = t;", ";"),
     "tree_slot_shift": ("keys[n++] = P + j;\n", "keys[n++] = P + j - (j > 0);\n"),
+    "window_start_off_by_one": ("for (int64_t t = p - window + 1 < 0 ? 0 : p - window + 1;",
+                                "for (int64_t t = p - window < 0 ? 0 : p - window;"),
+    "window_excludes_own_key": ("t <= p && t < kv_len; ++t)\n      keys[n++] = t;",
+                                "t < p && t < kv_len; ++t)\n      keys[n++] = t;"),
     "attn_no_scale": ("s[t] = scale * dot;", "s[t] = dot;"),
     "attn_wrong_group_map": ("const int g = h / G;", "const int g = h % Hkv;"),
     "attn_exp_sign": ("const double p = exp(s[t] - mx);", "const double p = exp(mx - s[t]);"),

@@ -249,6 +249,56 @@ def test_topk_covering_all_blocks_equals_dense_causal(orc):
     assert np.allclose(sp["out"], ref[hr[:, 0], hr[:, 1], hr[:, 2]], rtol=0, atol=1e-12)
 
 
+# ---------------------------------------------------------------- sliding window (draft model)
+def test_window_keyset_rules(orc):
+    assert orc.keyset(orc.MODE_WINDOW, 5, 100, None, 0, 0, window=3).tolist() == [3, 4, 5]
+    assert orc.keyset(orc.MODE_WINDOW, 1, 100, None, 0, 0, window=5).tolist() == [0, 1]
+    assert orc.keyset(orc.MODE_WINDOW, 70, 100, None, 0, 0, window=1).tolist() == [70]
+    assert orc.keyset(orc.MODE_WINDOW, 99, 100, None, 0, 0, window=64).tolist() == list(range(36, 100))
+    with pytest.raises(ValueError):
+        orc.keyset(orc.MODE_WINDOW, 5, 100, None, 0, 0, window=0)
+
+
+def test_window_matches_torch_sdpa_band_mask_fp64(orc):
+    w = tiny("pin_window", seq_len=300)
+    d = synth.generate(w, seed=21)
+    W = 37
+    q = d["q"][:, :, -90:]                                 # positions 210..299
+    res = orc.window_forward(q, d["k"], d["v"], kv_len=300, n_kv_heads=w.n_kv_heads, window=W)
+    G = w.group
+    qf = torch.from_numpy(synth.bf16_to_f32(q).astype(np.float64))
+    kf = torch.from_numpy(synth.bf16_to_f32(d["k"][:, :, :300]).astype(np.float64)).repeat_interleave(G, 1)
+    vf = torch.from_numpy(synth.bf16_to_f32(d["v"][:, :, :300]).astype(np.float64)).repeat_interleave(G, 1)
+    key = torch.arange(300)[None, :]
+    pos = torch.arange(210, 300)[:, None]
+    band = (key <= pos) & (key > pos - W)
+    ref = torch.nn.functional.scaled_dot_product_attention(qf, kf, vf, attn_mask=band).numpy()
+    assert np.allclose(res["out"].reshape(ref.shape), ref, rtol=0, atol=1e-12)
+    assert set(res["nkeys"].tolist()) == {W}
+
+
+def test_window_of_one_returns_own_value(orc):
+    w = tiny("pin_window1", seq_len=200)
+    d = synth.generate(w, seed=22)
+    res = orc.window_forward(d["q"], d["k"], d["v"], kv_len=200, n_kv_heads=w.n_kv_heads, window=1)
+    G = w.group
+    for (b, h, i), o, l in zip(res["rows"], res["out"], res["lse"]):
+        vv = synth.bf16_to_f32(d["v"][b, h // G, i]).astype(np.float64)
+        assert np.array_equal(o, vv)                        # softmax over one key is exactly 1
+        qk = float(np.dot(synth.bf16_to_f32(d["q"][b, h, i]).astype(np.float64),
+                          synth.bf16_to_f32(d["k"][b, h // G, i]).astype(np.float64)))
+        assert math.isclose(l, qk / math.sqrt(w.head_dim), rel_tol=0, abs_tol=1e-12)
+
+
+def test_window_covering_the_prefix_equals_dense_causal(orc):
+    w = tiny("pin_window_all", seq_len=260)
+    d = synth.generate(w, seed=23)
+    wi = orc.window_forward(d["q"], d["k"], d["v"], kv_len=260, n_kv_heads=w.n_kv_heads, window=260)
+    de = orc.dense_forward(d["q"], d["k"], d["v"], kv_len=260, n_kv_heads=w.n_kv_heads)
+    assert np.array_equal(wi["nkeys"], de["nkeys"])
+    assert np.allclose(wi["out"], de["out"], rtol=0, atol=0)
+
+
 def test_threshold_above_every_row_equals_dense(orc):
     w = tiny("pin_thr", seq_len=400)
     d = synth.generate(w, seed=10)

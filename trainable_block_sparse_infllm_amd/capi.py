@@ -20,6 +20,7 @@ EXPORTS = [
     "infllmv2_sparse_attn_prefill", "infllmv2_decode_workspace_bytes",
     "infllmv2_sparse_attn_decode", "infllmv2_sparse_attn_decode_scores", "infllmv2_dense_attn",
     "infllmv2_prefill_backward_workspace_bytes", "infllmv2_sparse_attn_prefill_backward",
+    "infllmv2_sliding_window_attn",
     "infllmv2_strerror",
     "infllmv2_last_error",
 ]
@@ -67,6 +68,7 @@ def lib():
             "infllmv2_sparse_attn_decode": (i32, [cfg, P, i32, P, P, i64, i64, P, P, P, P, P, sz, P]),
             "infllmv2_sparse_attn_decode_scores": (i32, [cfg, P, P, P, i64, i64, P, P, P, P, P, sz, P]),
             "infllmv2_dense_attn": (i32, [cfg, P, i32, P, P, i64, i64, i32, P, P, P]),
+            "infllmv2_sliding_window_attn": (i32, [cfg, P, i32, P, P, i64, i64, i64, P, P, P]),
             "infllmv2_prefill_backward_workspace_bytes": (sz, [cfg, i32, i64]),
             "infllmv2_sparse_attn_prefill_backward": (i32, [cfg, P, i32, P, P, i64, i64, P, P, P, P,
                                                             P, P, P, P, sz, P]),
@@ -146,6 +148,11 @@ def infllmv2_sparse_attn_decode_scores(cfg, q, k_cache, v_cache, kv_cap, kv_len,
 def infllmv2_dense_attn(cfg, q, n_q, k, v, kv_cap, kv_len, causal, out, lse=None, stream=None):
     _check(lib().infllmv2_dense_attn(C.byref(cfg), _p(q), n_q, _p(k), _p(v), kv_cap, kv_len, int(causal),
                                      _p(out), _p(lse), _s(stream)))
+
+
+def infllmv2_sliding_window_attn(cfg, q, n_q, k, v, kv_cap, kv_len, window, out, lse=None, stream=None):
+    _check(lib().infllmv2_sliding_window_attn(C.byref(cfg), _p(q), n_q, _p(k), _p(v), kv_cap, kv_len,
+                                              int(window), _p(out), _p(lse), _s(stream)))
 
 
 def infllmv2_prefill_backward_workspace_bytes(cfg, n_q, kv_len) -> int:

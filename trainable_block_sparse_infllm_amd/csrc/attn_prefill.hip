@@ -8,7 +8,9 @@
 //   mode 0 (sparse): the 64 keys of every block in idx[b][h/G][i] below its own
 //           block, plus its own block up to p; all keys 0..p if
 //           p + 1 < dense_threshold;
-//   mode 1 (dense causal): keys 0..p;      mode 2 (dense): keys 0..kv_len-1.
+//   mode 1 (dense causal): keys 0..p;      mode 2 (dense): keys 0..kv_len-1;
+//   mode 3 (sliding window, the draft model's attention): keys
+//           max(0, p - window + 1)..p.
 //
 // Work layout. A workgroup of NW wavefronts (4; 2 for G = 1) owns TQ <= 64
 // consecutive tokens of one (b, g); each wavefront owns one sub-tile of 32
@@ -54,7 +56,7 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ out, float* __restrict__ lse, int Hq,
     int Hkv, int n_q, int64_t kv_cap, int64_t kv_len, int K, int dense_thr, int mode,
-    float scale_log2, int ntile, int umax) {
+    int64_t window, float scale_log2, int ntile, int umax) {
   using Sh = PrefillShape<G>;
   constexpr int TPS = Sh::TPS, NW = Sh::NW, TQ = Sh::TQ, NT = Sh::NT, LPS = Sh::LPS;
   constexpr int DS = kD / 16;                // k-steps of S^T = K Q^T
@@ -87,6 +89,9 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
   // tokens t < dend attend densely
   const int64_t dend = mode != 0 ? ntok : (dense_thr > 0 ? dense_thr - 1 - base : 0);
   const bool tile_dense = dend >= ntok;
+  // a tile walking a contiguous range starts at block blk0 (mode 3: the block
+  // holding its first token's window start)
+  const int64_t blk0 = mode == 3 ? (base - window + 1 > 0 ? (base - window + 1) / kBlock : 0) : 0;
   const uint16_t* kbase = k + int64_t(bg) * kv_cap * kD;
   const uint16_t* vbase = v + int64_t(bg) * kv_cap * kD;
 
@@ -102,24 +107,26 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
     for (int ds = 0; ds < DS; ++ds) qf[ds] = as_bf16x8(ldg16_if(my_t < n_q, qrow + ds * 16 + hl * 8));
   }
 
-  auto range_mask_t = [&](int64_t j) -> uint64_t { return range_mask(j, mode, base, dend, ntok); };
+  auto range_mask_t = [&](int64_t j) -> uint64_t {
+    return range_mask(j, mode, base, dend, ntok, window);
+  };
 
   // ---------------------------------------------------------------- 1. union
   int U;
   if (tile_dense)
-    U = int(own_hi) + 1;
+    U = int(own_hi - blk0) + 1;
   else
     U = build_union<NT, NW>(idx, bg, n_q, tok0, ntok, base, own_lo, own_hi, dend, K, umax, mode,
                             u_mask, u_blk, bitmap, wbase, wtot, jsel);
   U = __builtin_amdgcn_readfirstlane(U);
   auto blk_of = [&](int u) -> int64_t {
-    return tile_dense ? int64_t(u) : int64_t(__builtin_amdgcn_readfirstlane(lds_read(u_blk + u)));
+    return tile_dense ? blk0 + u : int64_t(__builtin_amdgcn_readfirstlane(lds_read(u_blk + u)));
   };
   // Raw LDS reads of an entry's block / token mask, issued one iteration
   // ahead so that their latency overlaps the stage wait; made uniform at use.
-  auto blk_raw = [&](int u) -> int32_t { return tile_dense ? u : lds_read(u_blk + u); };
+  auto blk_raw = [&](int u) -> int32_t { return tile_dense ? int32_t(blk0) + u : lds_read(u_blk + u); };
   auto mask_raw = [&](int u) -> uint64_t {
-    return tile_dense ? range_mask_t(u) : lds_read(u_mask + u);
+    return tile_dense ? range_mask_t(blk0 + u) : lds_read(u_mask + u);
   };
 
   // ---------------------------------------------------------------- ring prologue
@@ -247,6 +254,17 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
         for (int e = 0; e < 16; ++e)
           sacc[kt][e] = (32 * kt + 8 * (e / 4) + 4 * hl + e % 4 <= lim) ? sacc[kt][e] : -INFINITY;
     }
+    // sliding window: keys before a row's window start, in a block that some
+    // row of the wavefront sees only in part
+    if (mode == 3 && key0 < p_first + TPS - window) {
+      const int64_t rlo = row_p - window + 1 - key0;                  // first visible key
+      const int lo = int(rlo > 0 ? (rlo < kBlock ? rlo : kBlock) : 0);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          sacc[kt][e] = (32 * kt + 8 * (e / 4) + 4 * hl + e % 4 >= lo) ? sacc[kt][e] : -INFINITY;
+    }
     float mb = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -355,7 +373,7 @@ template <int G>
 static hipError_t launch_prefill_t(const Dims& d, int mode, const uint16_t* q, int n_q,
                                    const uint16_t* k, const uint16_t* v, int64_t kv_cap,
                                    int64_t kv_len, const int32_t* idx, uint16_t* out, float* lse,
-                                   hipStream_t s) {
+                                   int64_t window, hipStream_t s) {
   using Sh = PrefillShape<G>;
   const int ntile = (n_q + Sh::TQ - 1) / Sh::TQ;
   const int64_t nb = (kv_len - 1) / kBlock + 1;
@@ -368,20 +386,21 @@ static hipError_t launch_prefill_t(const Dims& d, int mode, const uint16_t* q, i
   if (attr != hipSuccess) return attr;
   const dim3 grid(unsigned(int64_t(d.B) * d.Hkv * ntile));
   kern<<<grid, Sh::NT, prefill_lds(umax, Sh::TQ, d.K), s>>>(
-      q, k, v, idx, out, lse, d.Hq, d.Hkv, n_q, kv_cap, kv_len, d.K, d.dense_thr, mode,
+      q, k, v, idx, out, lse, d.Hq, d.Hkv, n_q, kv_cap, kv_len, d.K, d.dense_thr, mode, window,
       d.scale * 1.4426950408889634f, ntile, int(umax));
   return hipGetLastError();
 }
 
 hipError_t launch_prefill128(const Dims& d, int mode, const uint16_t* q, int n_q,
                              const uint16_t* k, const uint16_t* v, int64_t kv_cap, int64_t kv_len,
-                             const int32_t* idx, uint16_t* out, float* lse, hipStream_t s) {
+                             const int32_t* idx, uint16_t* out, float* lse, hipStream_t s,
+                             int64_t window) {
   switch (d.G) {
-    case 1: return launch_prefill_t<1>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s);
-    case 2: return launch_prefill_t<2>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s);
-    case 4: return launch_prefill_t<4>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s);
-    case 8: return launch_prefill_t<8>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s);
-    case 16: return launch_prefill_t<16>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s);
+#define PREFILL_CASE(GG)                                                                    \
+  case GG:                                                                                  \
+    return launch_prefill_t<GG>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, window, s);
+    PREFILL_CASE(1) PREFILL_CASE(2) PREFILL_CASE(4) PREFILL_CASE(8) PREFILL_CASE(16)
+#undef PREFILL_CASE
     default: return hipErrorInvalidValue;
   }
 }

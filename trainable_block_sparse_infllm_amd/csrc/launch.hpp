@@ -36,13 +36,15 @@ hipError_t launch_topk_prefill128(const Dims& d, const uint16_t* q, const uint16
                                   int64_t q_pos0, int is_tree, int64_t nblk, int64_t cmax,
                                   int32_t* idx, hipStream_t s);
 
-// head_dim 128 prefill / dense attention over a per-tile block union staged
-// through an LDS ring. prefill128_stages() returns the ring depth for the
-// shape, or 0 if it does not fit (then launch_attn_rows is used).
+// head_dim 128 prefill / dense / sliding-window attention over a per-tile
+// block union staged through an LDS ring (mode 3: keys max(0, p-window+1)..p).
+// prefill128_stages() returns the ring depth for the shape, or 0 if it does
+// not fit (then launch_attn_rows is used; it has no mode 3).
 int prefill128_stages(const Dims& d, int mode, int64_t kv_len);
 hipError_t launch_prefill128(const Dims& d, int mode, const uint16_t* q, int n_q,
                              const uint16_t* k, const uint16_t* v, int64_t kv_cap, int64_t kv_len,
-                             const int32_t* idx, uint16_t* out, float* lse, hipStream_t s);
+                             const int32_t* idx, uint16_t* out, float* lse, hipStream_t s,
+                             int64_t window = 0);
 
 size_t decode_workspace_bytes(const Dims& d, int n_q, int64_t kv_len);
 

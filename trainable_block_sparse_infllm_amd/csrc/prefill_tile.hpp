@@ -133,11 +133,14 @@ __device__ __forceinline__ float halves_max(float x) {
 
 
 // Tokens t of a tile (positions base + t) attending block j through their own
-// block or a dense prefix (t < dend); mode 2 (dense, no mask): every token.
+// block or a dense prefix (t < dend); mode 2 (dense, no mask): every token;
+// mode 3 (sliding window of `window` keys): the tokens whose window
+// [p - window + 1, p] meets the block, i.e. j*64 <= p < j*64 + 63 + window.
 __device__ __forceinline__ uint64_t range_mask(int64_t j, int mode, int64_t base, int64_t dend,
-                                               int ntok) {
+                                               int ntok, int64_t window = 0) {
   if (mode == 2) return range_bits(0, ntok, ntok);
   const int64_t lo = j * kBlock - base;
+  if (mode == 3) return range_bits(lo, lo + kBlock - 1 + window, ntok);
   return range_bits(lo, max(lo + kBlock, dend), ntok);
 }
 

@@ -125,5 +125,14 @@ def dense(cfg, q, k, v, kv_len, *, causal=True, with_lse=True, stream=None):
     return dict(out=out, lse=lse)
 
 
+def sliding_window(cfg, q, k, v, kv_len, window, *, with_lse=True, stream=None):
+    """Causal attention of each query over the last `window` positions up to its own."""
+    B, Hq, n_q, D = q.shape
+    out = _bf16_like((B, Hq, n_q, D), q)
+    lse = torch.empty((B, Hq, n_q), dtype=torch.float32, device=q.device) if with_lse else None
+    capi.infllmv2_sliding_window_attn(cfg, q, n_q, k, v, k.shape[2], kv_len, window, out, lse, stream)
+    return dict(out=out, lse=lse)
+
+
 def default_scale(head_dim: int) -> float:
     return 1.0 / math.sqrt(head_dim)
