@@ -215,6 +215,49 @@ INFLLMV2_API int infllmv2_dense_attn(const infllmv2_cfg* cfg, const void* q, int
                         const void* v, int64_t kv_cap, int64_t kv_len, int32_t causal, void* out,
                         float* lse, void* stream);
 
+/* Decode-loop cache maintenance (QbitAI summary, efficiency evaluation: as
+ * the context grows only the semantic-kernel representation grows with it, so
+ * the kernel table is extended as blocks complete). Appends n_new tokens per
+ * sequence: k_new, v_new [B][Hkv][n_new][D] bf16 go to rows len_b ..
+ * len_b + n_new - 1 of k_cache, v_cache [B][Hkv][kv_cap][D], where len_b =
+ * kv_lens[b] (device int64 [B], variable lengths; nullable) or kv_len (every
+ * sequence; then kv_len + n_new <= kv_cap is checked). When kbar is given
+ * (layout of infllmv2_pool_kernels), the kernels of every block the append
+ * completes, blocks len_b/64 .. (len_b + n_new)/64 - 1, are pooled from the
+ * updated cache in the same stream order. Rows that would land at or past
+ * kv_cap are not written (device lengths cannot be checked on the host).
+ * kv_lens is read, not updated: the caller advances it. n_new = 0 is a no-op. */
+INFLLMV2_API int infllmv2_append_kv(const infllmv2_cfg* cfg, const void* k_new, const void* v_new,
+                       int32_t n_new, void* k_cache, void* v_cache, int64_t kv_cap,
+                       const int64_t* kv_lens, int64_t kv_len, void* kbar, void* stream);
+
+/* Block scores of one new token per sequence in a batch of variable lengths
+ * (the scoring of infllmv2_score_blocks): sequence b's token sits at position
+ * kv_lens[b] - 1 (device int64 [B], each >= 1), so its candidates are the
+ * complete blocks j < (kv_lens[b] - 1)/64. q [B][Hq][1][D]; scores
+ * [B][Hkv][1][kv_cap/64] fp32, -inf past each sequence's candidates. */
+INFLLMV2_API int infllmv2_score_blocks_varlen(const infllmv2_cfg* cfg, const void* q,
+                                 const int64_t* kv_lens, const void* kbar, int64_t kv_cap,
+                                 float* scores, void* stream);
+
+/* Bytes of workspace infllmv2_sparse_attn_decode_varlen needs when no
+ * sequence is longer than kv_len_max (0 if the configuration is invalid). */
+INFLLMV2_API size_t infllmv2_decode_varlen_workspace_bytes(const infllmv2_cfg* cfg,
+                                              int64_t kv_len_max);
+
+/* infllmv2_sparse_attn_decode_scores for a batch of variable lengths: one new
+ * token per sequence at position kv_lens[b] - 1 (device int64 [B]), with
+ * 1 <= kv_lens[b] <= kv_len_max <= kv_cap (values outside are clamped to that
+ * range on the device); selection from scores (as written by
+ * infllmv2_score_blocks_varlen), the own block and the dense switch apply per
+ * sequence. Workspace: infllmv2_decode_varlen_workspace_bytes(kv_len_max). */
+INFLLMV2_API int infllmv2_sparse_attn_decode_varlen(const infllmv2_cfg* cfg, const void* q,
+                                       const void* k_cache, const void* v_cache, int64_t kv_cap,
+                                       const int64_t* kv_lens, int64_t kv_len_max,
+                                       const float* scores, int32_t* idx_out, void* out,
+                                       float* lse, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
 /* Sliding-window causal attention: query i at position p = kv_len - n_q + i
  * attends keys max(0, p - window + 1) .. p (QbitAI summary, section on fusing
  * speculative sampling, quantization and long-context algorithms: the draft

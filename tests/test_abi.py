@@ -104,6 +104,18 @@ CASES = [
     ("infllmv2_dense_attn", {}, (A, 1, A, A, 64, 0, 1, B, None, None), -1, "kv_len"),
     ("infllmv2_dense_attn", {}, (A, 1, A, None, 64, 64, 1, B, None, None), -1, "v is NULL"),
     ("infllmv2_dense_attn", dict(softmax_scale=float("nan")), (A, 1, A, A, 64, 64, 1, B, None, None), -1, "finite"),
+    ("infllmv2_append_kv", {}, (A, A, 1, A, A, 64, None, 64, None, None), -1, "exceeds kv_cap"),
+    ("infllmv2_append_kv", {}, (A, A, -1, A, A, 64, None, 0, None, None), -1, "n_new"),
+    ("infllmv2_append_kv", {}, (A, None, 1, A, A, 64, None, 0, None, None), -1, "v_new is NULL"),
+    ("infllmv2_append_kv", {}, (A, A, 1, A, A, 64, A + 4, 0, None, None), -1, "kv_lens"),
+    ("infllmv2_append_kv", {}, (A, A, 1, A, A, 64, None, 0, A + 2, None), -1, "kbar"),
+    ("infllmv2_score_blocks_varlen", {}, (A, None, A, 64, A, None), -1, "kv_lens is NULL"),
+    ("infllmv2_score_blocks_varlen", {}, (A, A, A, 0, A, None), -1, "kv_cap"),
+    ("infllmv2_sparse_attn_decode_varlen", {}, (A, A, A, 64, None, 64, A, None, B, None, 0x100000, 1 << 30, None), -1, "kv_lens is NULL"),
+    ("infllmv2_sparse_attn_decode_varlen", {}, (A, A, A, 64, A, 65, A, None, B, None, 0x100000, 1 << 30, None), -1, "exceeds kv_cap"),
+    ("infllmv2_sparse_attn_decode_varlen", {}, (A, A, A, 64, A, 64, None, None, B, None, 0x100000, 1 << 30, None), -1, "scores is NULL"),
+    ("infllmv2_sparse_attn_decode_varlen", dict(top_k=65), (A, A, A, 64, A, 64, A, None, B, None, 0x100000, 1 << 30, None), -2, "top_k above 64"),
+    ("infllmv2_sparse_attn_decode_varlen", {}, (A, A, A, 64, A, 64, A, None, B, None, 0x100000, 16, None), -3, "workspace"),
     ("infllmv2_sliding_window_attn", {}, (A, 1, A, A, 64, 64, 0, B, None, None), -1, "window"),
     ("infllmv2_sliding_window_attn", {}, (A, 65, A, A, 64, 64, 16, B, None, None), -1, "n_q"),
     ("infllmv2_sliding_window_attn", {}, (A, 1, A, A, 64, 64, 16, None, None, None), -1, "out is NULL"),
@@ -139,6 +151,12 @@ def test_workspace_bytes(t):
     b1 = t.infllmv2_prefill_backward_workspace_bytes(cfg, 32768, 32768)
     assert b1 > 0 and t.infllmv2_prefill_backward_workspace_bytes(cfg, 1024, 1024) < b1
     assert t.infllmv2_prefill_backward_workspace_bytes(cfg, 0, 10) == 0
+    # variable lengths: room for the larger of K + 1 entries and a dense row below the threshold
+    v1 = t.infllmv2_decode_varlen_workspace_bytes(cfg_ok(t, batch=8, top_k=32), 131072)
+    assert v1 >= t.infllmv2_decode_workspace_bytes(cfg_ok(t, batch=8, top_k=32), 1, 131072) > 0
+    vd = t.infllmv2_decode_varlen_workspace_bytes(cfg_ok(t, batch=8, top_k=4, dense_threshold=8192), 131072)
+    assert vd > t.infllmv2_decode_workspace_bytes(cfg_ok(t, batch=8, top_k=4, dense_threshold=8192), 1, 131072)
+    assert t.infllmv2_decode_varlen_workspace_bytes(cfg, 0) == 0
 
 
 def test_binding_raises_with_status(t):

@@ -10,6 +10,8 @@ from .capi import (  # noqa: F401
     infllmv2_sparse_attn_prefill, infllmv2_decode_workspace_bytes,
     infllmv2_sparse_attn_decode, infllmv2_sparse_attn_decode_scores, infllmv2_dense_attn,
     infllmv2_prefill_backward_workspace_bytes, infllmv2_sparse_attn_prefill_backward,
-    infllmv2_sliding_window_attn, infllmv2_strerror, infllmv2_last_error,
+    infllmv2_sliding_window_attn, infllmv2_append_kv, infllmv2_score_blocks_varlen,
+    infllmv2_decode_varlen_workspace_bytes, infllmv2_sparse_attn_decode_varlen,
+    infllmv2_strerror, infllmv2_last_error,
 )
 from . import ops  # noqa: F401

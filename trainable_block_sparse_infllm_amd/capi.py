@@ -20,7 +20,8 @@ EXPORTS = [
     "infllmv2_sparse_attn_prefill", "infllmv2_decode_workspace_bytes",
     "infllmv2_sparse_attn_decode", "infllmv2_sparse_attn_decode_scores", "infllmv2_dense_attn",
     "infllmv2_prefill_backward_workspace_bytes", "infllmv2_sparse_attn_prefill_backward",
-    "infllmv2_sliding_window_attn",
+    "infllmv2_sliding_window_attn", "infllmv2_append_kv", "infllmv2_score_blocks_varlen",
+    "infllmv2_decode_varlen_workspace_bytes", "infllmv2_sparse_attn_decode_varlen",
     "infllmv2_strerror",
     "infllmv2_last_error",
 ]
@@ -69,6 +70,11 @@ def lib():
             "infllmv2_sparse_attn_decode_scores": (i32, [cfg, P, P, P, i64, i64, P, P, P, P, P, sz, P]),
             "infllmv2_dense_attn": (i32, [cfg, P, i32, P, P, i64, i64, i32, P, P, P]),
             "infllmv2_sliding_window_attn": (i32, [cfg, P, i32, P, P, i64, i64, i64, P, P, P]),
+            "infllmv2_append_kv": (i32, [cfg, P, P, i32, P, P, i64, P, i64, P, P]),
+            "infllmv2_score_blocks_varlen": (i32, [cfg, P, P, P, i64, P, P]),
+            "infllmv2_decode_varlen_workspace_bytes": (C.c_size_t, [cfg, i64]),
+            "infllmv2_sparse_attn_decode_varlen": (i32, [cfg, P, P, P, i64, P, i64, P, P, P, P, P,
+                                                         C.c_size_t, P]),
             "infllmv2_prefill_backward_workspace_bytes": (sz, [cfg, i32, i64]),
             "infllmv2_sparse_attn_prefill_backward": (i32, [cfg, P, i32, P, P, i64, i64, P, P, P, P,
                                                             P, P, P, P, sz, P]),
@@ -172,3 +178,26 @@ def infllmv2_strerror(status: int) -> str:
 
 def infllmv2_last_error() -> str:
     return lib().infllmv2_last_error().decode()
+
+
+def infllmv2_append_kv(cfg, k_new, v_new, n_new, k_cache, v_cache, kv_cap, kv_lens, kv_len, kbar,
+                       stream=None):
+    _check(lib().infllmv2_append_kv(C.byref(cfg), _p(k_new), _p(v_new), n_new, _p(k_cache), _p(v_cache),
+                                    kv_cap, _p(kv_lens), kv_len, _p(kbar), _s(stream)))
+
+
+def infllmv2_score_blocks_varlen(cfg, q, kv_lens, kbar, kv_cap, scores, stream=None):
+    _check(lib().infllmv2_score_blocks_varlen(C.byref(cfg), _p(q), _p(kv_lens), _p(kbar), kv_cap,
+                                              _p(scores), _s(stream)))
+
+
+def infllmv2_decode_varlen_workspace_bytes(cfg, kv_len_max):
+    return lib().infllmv2_decode_varlen_workspace_bytes(C.byref(cfg), kv_len_max)
+
+
+def infllmv2_sparse_attn_decode_varlen(cfg, q, k_cache, v_cache, kv_cap, kv_lens, kv_len_max, scores,
+                                       idx_out, out, lse, workspace, workspace_bytes, stream=None):
+    _check(lib().infllmv2_sparse_attn_decode_varlen(C.byref(cfg), _p(q), _p(k_cache), _p(v_cache), kv_cap,
+                                                    _p(kv_lens), kv_len_max, _p(scores), _p(idx_out),
+                                                    _p(out), _p(lse), _p(workspace), workspace_bytes,
+                                                    _s(stream)))

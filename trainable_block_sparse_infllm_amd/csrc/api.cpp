@@ -361,6 +361,92 @@ int infllmv2_dense_attn(const infllmv2_cfg* cfg, const void* q, int32_t n_q, con
   return INFLLMV2_OK;
 }
 
+int infllmv2_append_kv(const infllmv2_cfg* cfg, const void* k_new, const void* v_new, int32_t n_new,
+                       void* k_cache, void* v_cache, int64_t kv_cap, const int64_t* kv_lens,
+                       int64_t kv_len, void* kbar, void* stream) {
+  const char* fn = "infllmv2_append_kv";
+  Dims d;
+  TRY(check_cfg(fn, cfg, false, &d));
+  TRY(check_ptr(fn, k_new, "k_new", 16));
+  TRY(check_ptr(fn, v_new, "v_new", 16));
+  TRY(check_ptr(fn, k_cache, "k_cache", 16));
+  TRY(check_ptr(fn, v_cache, "v_cache", 16));
+  if (kbar) TRY(check_ptr(fn, kbar, "kbar", 16));
+  if (n_new < 0) return fail(INFLLMV2_INVALID_ARGUMENT, fn, "n_new must be >= 0");
+  if (kv_cap < 1 || kv_cap > (int64_t(1) << 31))
+    return fail(INFLLMV2_INVALID_ARGUMENT, fn, "kv_cap must lie in [1, 2^31]");
+  if (kv_lens) {
+    TRY(check_ptr(fn, kv_lens, "kv_lens", 8));
+  } else if (kv_len < 0 || kv_len + n_new > kv_cap) {
+    return fail(INFLLMV2_INVALID_ARGUMENT, fn, "kv_len + n_new exceeds kv_cap");
+  }
+  if (n_new == 0) return INFLLMV2_OK;
+  TRY(check_device(fn));
+  LAUNCH(fn, infllmv2::launch_append(d, static_cast<const uint16_t*>(k_new),
+                                     static_cast<const uint16_t*>(v_new), n_new,
+                                     static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+                                     kv_cap, kv_lens, kv_len, static_cast<uint16_t*>(kbar),
+                                     static_cast<hipStream_t>(stream)));
+  return INFLLMV2_OK;
+}
+
+int infllmv2_score_blocks_varlen(const infllmv2_cfg* cfg, const void* q, const int64_t* kv_lens,
+                                 const void* kbar, int64_t kv_cap, float* scores, void* stream) {
+  const char* fn = "infllmv2_score_blocks_varlen";
+  Dims d;
+  TRY(check_cfg(fn, cfg, false, &d));
+  TRY(check_ptr(fn, q, "q", 16));
+  TRY(check_ptr(fn, kv_lens, "kv_lens", 8));
+  TRY(check_ptr(fn, kbar, "kbar", 16));
+  TRY(check_ptr(fn, scores, "scores", 4));
+  if (kv_cap < 1 || kv_cap > (int64_t(1) << 31))
+    return fail(INFLLMV2_INVALID_ARGUMENT, fn, "kv_cap must lie in [1, 2^31]");
+  TRY(check_device(fn));
+  LAUNCH(fn, infllmv2::launch_scores(d, static_cast<const uint16_t*>(q), 1, 0, 0,
+                                     static_cast<const uint16_t*>(kbar), nblk_of(kv_cap), scores,
+                                     static_cast<hipStream_t>(stream), kv_lens));
+  return INFLLMV2_OK;
+}
+
+size_t infllmv2_decode_varlen_workspace_bytes(const infllmv2_cfg* cfg, int64_t kv_len_max) {
+  Dims d;
+  if (check_cfg("infllmv2_decode_varlen_workspace_bytes", cfg, true, &d) != INFLLMV2_OK) return 0;
+  if (kv_len_max < 1) return 0;
+  return infllmv2::decode_varlen_workspace_bytes(d, kv_len_max);
+}
+
+int infllmv2_sparse_attn_decode_varlen(const infllmv2_cfg* cfg, const void* q, const void* k_cache,
+                                       const void* v_cache, int64_t kv_cap, const int64_t* kv_lens,
+                                       int64_t kv_len_max, const float* scores, int32_t* idx_out,
+                                       void* out, float* lse, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  const char* fn = "infllmv2_sparse_attn_decode_varlen";
+  Dims d;
+  TRY(check_cfg(fn, cfg, true, &d));
+  TRY(check_attn(fn, d, q, 1, k_cache, v_cache, kv_cap, kv_len_max, out, lse));
+  TRY(check_ptr(fn, kv_lens, "kv_lens", 8));
+  TRY(check_ptr(fn, scores, "scores", 4));
+  if (idx_out) TRY(check_ptr(fn, idx_out, "idx_out", 4));
+  if (d.K > 64) return fail(INFLLMV2_UNSUPPORTED, fn, "top_k above 64");
+  if ((kv_len_max - 1) / 64 > 4096)
+    return fail(INFLLMV2_UNSUPPORTED, fn, "more than 4096 candidate blocks");
+  TRY(check_ptr(fn, workspace, "workspace", 256));
+  const size_t need = infllmv2::decode_varlen_workspace_bytes(d, kv_len_max);
+  if (workspace_bytes < need) {
+    char msg[128];
+    std::snprintf(msg, sizeof msg, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    return fail(INFLLMV2_WORKSPACE_TOO_SMALL, fn, msg);
+  }
+  TRY(check_device(fn));
+  LAUNCH(fn, infllmv2::launch_decode(d, static_cast<const uint16_t*>(q), 1,
+                                     static_cast<const uint16_t*>(k_cache),
+                                     static_cast<const uint16_t*>(v_cache), kv_cap, kv_len_max,
+                                     nullptr, nullptr, static_cast<uint16_t*>(out), lse, workspace,
+                                     workspace_bytes, static_cast<hipStream_t>(stream), scores,
+                                     idx_out, kv_lens));
+  return INFLLMV2_OK;
+}
+
 int infllmv2_sliding_window_attn(const infllmv2_cfg* cfg, const void* q, int32_t n_q,
                                  const void* k, const void* v, int64_t kv_cap, int64_t kv_len,
                                  int64_t window, void* out, float* lse, void* stream) {

@@ -44,13 +44,18 @@ struct DecodeLayout {
   size_t off_union, off_mask, off_count, off_ml, off_o, total;
 };
 
-DecodeLayout decode_layout(const Dims& d, int n_q, int64_t kv_len) {
+// varlen: single-token rows of sequences with lengths up to kv_len, any of
+// which may be below the dense threshold.
+DecodeLayout decode_layout(const Dims& d, int n_q, int64_t kv_len, bool varlen = false) {
   DecodeLayout L{};
   L.bgs = int64_t(d.B) * d.Hkv;
   const int64_t P = kv_len - n_q;
   const int64_t last_blk = (kv_len - 1) / kBlock;
   const bool maybe_dense = d.dense_thr > 0 && P + 1 < d.dense_thr;
-  if (n_q == 1) {
+  if (n_q == 1 && varlen) {
+    const int64_t dense_e = d.dense_thr > 1 ? (int64_t(d.dense_thr) - 2) / kBlock + 1 : 0;
+    L.max_e = std::max<int64_t>(int64_t(d.K) + 1, std::min(last_blk + 1, dense_e));
+  } else if (n_q == 1) {
     L.max_e = maybe_dense ? last_blk + 1 : int64_t(d.K) + 1;
   } else {
     const int64_t local = last_blk - P / kBlock + 1;
@@ -202,7 +207,7 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
     uint16_t* __restrict__ out, float* __restrict__ lse, int Hq, int Hkv, int G, int n_q,
     int64_t kv_cap, int64_t kv_len, int K, int dense_thr, int is_tree, int sb, int nsplit,
     int max_e, int rows, float scale_log2, const float* __restrict__ scores, int64_t nblk,
-    int32_t* __restrict__ idx_out) {
+    int32_t* __restrict__ idx_out, const int64_t* __restrict__ kv_lens) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   constexpr int WR = 16 * NSTD;                       // rows of a workgroup
@@ -218,6 +223,9 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
   const int bg = item / nsplit;
   const int b = bg / Hkv, g = bg % Hkv;
   const int row0 = blockIdx.y * 16 * NSTD;
+  // per-sequence length (single-token rows), kept within 1 .. the bound the
+  // grid and workspace were sized for
+  if (kv_lens) kv_len = min(max(kv_lens[b], int64_t(1)), kv_len);
   const int64_t P = kv_len - n_q;
   const uint16_t* kbase = k + int64_t(bg) * kv_cap * D;
   const uint16_t* vbase = v + int64_t(bg) * kv_cap * D;
@@ -560,11 +568,17 @@ size_t decode_workspace_bytes(const Dims& d, int n_q, int64_t kv_len) {
   return decode_layout(d, n_q, kv_len).total;
 }
 
+size_t decode_varlen_workspace_bytes(const Dims& d, int64_t kv_len_max) {
+  return decode_layout(d, 1, kv_len_max, true).total;
+}
+
 hipError_t launch_decode(const Dims& d, const uint16_t* q, int n_q, const uint16_t* k,
                          const uint16_t* v, int64_t kv_cap, int64_t kv_len, const int32_t* idx,
                          const uint64_t* tree_mask, uint16_t* out, float* lse, void* ws,
-                         size_t ws_bytes, hipStream_t s, const float* scores, int32_t* idx_out) {
-  const DecodeLayout L = decode_layout(d, n_q, kv_len);
+                         size_t ws_bytes, hipStream_t s, const float* scores, int32_t* idx_out,
+                         const int64_t* kv_lens) {
+  if (kv_lens && n_q != 1) return hipErrorInvalidValue;
+  const DecodeLayout L = decode_layout(d, n_q, kv_len, kv_lens != nullptr);
   if (ws_bytes < L.total) return hipErrorInvalidValue;
   char* base = static_cast<char*>(ws);
   int32_t* u_blk = reinterpret_cast<int32_t*>(base + L.off_union);
@@ -608,7 +622,7 @@ hipError_t launch_decode(const Dims& d, const uint16_t* q, int n_q, const uint16
     kern<<<grid, 64 * sb, size_t(sb) * kBlock * DD * 2, s>>>(                                     \
         q, k, v, idx, tree_mask, u_blk, u_mask, u_count, part_ml, part_o, out, lse, d.Hq, d.Hkv,  \
         d.G, n_q, kv_cap, kv_len, d.K, d.dense_thr, is_tree, sb, int(L.nsplit), int(L.max_e),     \
-        int(L.rows), sl2, scores, nblk, idx_out);                                                 \
+        int(L.rows), sl2, scores, nblk, idx_out, kv_lens);                                        \
   } else
 #define SPLIT_SEL(DD)                                                                             \
   SPLIT_CASE(DD, 1, 1) SPLIT_CASE(DD, 1, 2) SPLIT_CASE(DD, 1, 4) SPLIT_CASE(DD, 1, 8)            \

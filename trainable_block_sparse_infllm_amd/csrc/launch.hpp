@@ -12,11 +12,23 @@ struct Dims {
   float scale;
 };
 
+// Blocks first..last-1 of every sequence; with lens (device, [B]): the
+// blocks an append of n_new tokens completes in each sequence.
 hipError_t launch_pool(const Dims& d, const uint16_t* k, int64_t kv_cap, int64_t nblk,
-                       int64_t first, int64_t last, uint16_t* kbar, hipStream_t s);
+                       int64_t first, int64_t last, uint16_t* kbar, hipStream_t s,
+                       const int64_t* lens = nullptr, int64_t n_new = 0);
 
+// Cache append of n_new tokens at each sequence's length (lens[b], or kv_len
+// when lens is null), then pooling of the blocks it completes (kbar != null).
+hipError_t launch_append(const Dims& d, const uint16_t* k_new, const uint16_t* v_new,
+                         int64_t n_new, uint16_t* k_cache, uint16_t* v_cache, int64_t kv_cap,
+                         const int64_t* lens, int64_t kv_len, uint16_t* kbar, hipStream_t s);
+
+// kv_lens (device, [B], single-token non-tree rows only): sequence b's new
+// token sits at kv_lens[b] - 1 instead of q_pos0.
 hipError_t launch_scores(const Dims& d, const uint16_t* q, int n_q, int64_t q_pos0, int is_tree,
-                         const uint16_t* kbar, int64_t nblk, float* scores, hipStream_t s);
+                         const uint16_t* kbar, int64_t nblk, float* scores, hipStream_t s,
+                         const int64_t* kv_lens = nullptr);
 
 hipError_t launch_topk_from_scores(const Dims& d, const float* scores, int n_q, int64_t q_pos0,
                                    int is_tree, int64_t nblk, int32_t* idx, hipStream_t s);
@@ -50,11 +62,14 @@ size_t decode_workspace_bytes(const Dims& d, int n_q, int64_t kv_len);
 
 // scores != nullptr (single-token rows only): the block lists are selected in
 // the kernel from scores [B][Hkv][1][nblk] (written to idx_out when given).
+// kv_lens (device, [B], single-token rows only): per-sequence cache lengths,
+// kv_len then bounds them (it sizes the grid and the workspace).
 hipError_t launch_decode(const Dims& d, const uint16_t* q, int n_q, const uint16_t* k,
                          const uint16_t* v, int64_t kv_cap, int64_t kv_len, const int32_t* idx,
                          const uint64_t* tree_mask, uint16_t* out, float* lse, void* ws,
                          size_t ws_bytes, hipStream_t s, const float* scores = nullptr,
-                         int32_t* idx_out = nullptr);
+                         int32_t* idx_out = nullptr, const int64_t* kv_lens = nullptr);
+size_t decode_varlen_workspace_bytes(const Dims& d, int64_t kv_len_max);
 
 // Backward of the head_dim-128 sparse prefill (mode 0): dq, dk, dv (fp32).
 bool prefill_backward_ok(const Dims& d, int64_t kv_len);

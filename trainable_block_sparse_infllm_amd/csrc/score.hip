@@ -29,7 +29,8 @@ __global__ __launch_bounds__(64) void score_kernel(const uint16_t* __restrict__ 
                                                    const uint16_t* __restrict__ kbar,
                                                    float* __restrict__ scores, int Hq, int Hkv,
                                                    int n_q, int64_t q_pos0, int is_tree,
-                                                   int64_t nblk, int ntile) {
+                                                   int64_t nblk, int ntile,
+                                                   const int64_t* __restrict__ kv_lens) {
   constexpr int DS = D / 16;
   const int l = lane_id();
   const int r32 = l % 32, hl = l / 32;
@@ -37,6 +38,7 @@ __global__ __launch_bounds__(64) void score_kernel(const uint16_t* __restrict__ 
   const int tile = item % ntile;
   const int bg = item / ntile;
   const int b = bg / Hkv, g = bg % Hkv;
+  if (kv_lens) q_pos0 = kv_lens[b] - 1;              // per-sequence single-token position
   const int64_t j0 = int64_t(tile) * 32;
   const int row0 = blockIdx.y * NR * 32;
   const int node_hi = min(n_q - 1, (row0 + NR * 32 - 1) / G);
@@ -122,7 +124,8 @@ __global__ __launch_bounds__(64) void score_kernel(const uint16_t* __restrict__ 
 }
 
 hipError_t launch_scores(const Dims& d, const uint16_t* q, int n_q, int64_t q_pos0, int is_tree,
-                         const uint16_t* kbar, int64_t nblk, float* scores, hipStream_t s) {
+                         const uint16_t* kbar, int64_t nblk, float* scores, hipStream_t s,
+                         const int64_t* kv_lens) {
   const int rows = n_q * d.G;
   const int NR = rows > 32 ? 2 : 1;
   const int ntile = int((nblk + 31) / 32);
@@ -130,7 +133,7 @@ hipError_t launch_scores(const Dims& d, const uint16_t* q, int n_q, int64_t q_po
 #define SCORE_CASE(DD, GG, NN)                                                                   \
   if (d.D == DD && d.G == GG && NR == NN) {                                                      \
     score_kernel<DD, GG, NN><<<grid, 64, 0, s>>>(q, kbar, scores, d.Hq, d.Hkv, n_q, q_pos0,      \
-                                                 is_tree, nblk, ntile);                          \
+                                                 is_tree, nblk, ntile, kv_lens);                 \
     return hipGetLastError();                                                                    \
   }
 #define SCORE_G(DD, GG) SCORE_CASE(DD, GG, 1) SCORE_CASE(DD, GG, 2)

@@ -125,6 +125,36 @@ def dense(cfg, q, k, v, kv_len, *, causal=True, with_lse=True, stream=None):
     return dict(out=out, lse=lse)
 
 
+def append_kv(cfg, k_new, v_new, k_cache, v_cache, kbar=None, *, kv_len=None, kv_lens=None, stream=None):
+    """Write k_new, v_new [B][Hkv][n_new][D] at each sequence's length (kv_lens, a device int64
+    tensor [B], or the scalar kv_len) and pool the blocks this completes into kbar."""
+    if (kv_len is None) == (kv_lens is None):
+        raise ValueError("give exactly one of kv_len and kv_lens")
+    capi.infllmv2_append_kv(cfg, k_new, v_new, k_new.shape[2], k_cache, v_cache, k_cache.shape[2], kv_lens,
+                            0 if kv_len is None else kv_len, kbar, stream)
+
+
+def decode_step_varlen(cfg, q, k_cache, v_cache, kbar, kv_lens, kv_len_max, *, ws: Workspace | None = None,
+                       with_lse=True, stream=None):
+    """One decode step for a batch of variable lengths: sequence b's new token sits at
+    kv_lens[b] - 1 (device int64 [B], at most kv_len_max)."""
+    B, Hq, n_q, D = q.shape
+    if n_q != 1:
+        raise ValueError("decode_step_varlen takes one new token per sequence")
+    kv_cap = k_cache.shape[2]
+    scores = torch.empty((B, cfg.n_kv_heads, 1, nblk(kv_cap)), dtype=torch.float32, device=q.device)
+    capi.infllmv2_score_blocks_varlen(cfg, q, kv_lens, kbar, kv_cap, scores, stream)
+    idx = torch.empty((B, cfg.n_kv_heads, 1, cfg.top_k), dtype=torch.int32, device=q.device)
+    out = _bf16_like((B, Hq, 1, D), q)
+    lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=q.device) if with_lse else None
+    nbytes = capi.infllmv2_decode_varlen_workspace_bytes(cfg, kv_len_max)
+    ws = ws or Workspace(q.device)
+    buf = ws.get(nbytes)
+    capi.infllmv2_sparse_attn_decode_varlen(cfg, q, k_cache, v_cache, kv_cap, kv_lens, kv_len_max, scores,
+                                            idx, out, lse, buf, buf.numel(), stream)
+    return dict(scores=scores, idx=idx, out=out, lse=lse)
+
+
 def sliding_window(cfg, q, k, v, kv_len, window, *, with_lse=True, stream=None):
     """Causal attention of each query over the last `window` positions up to its own."""
     B, Hq, n_q, D = q.shape
