@@ -6,7 +6,9 @@ decode_128k_b8 workload (8 sequences, 32 query / 8 KV heads, head_dim 128,
 over the whole k̄ table (infllmv2_score_blocks), then top-K selection and
 sparse attention (split + LSE combine; infllmv2_sparse_attn_decode_scores,
 which selects inside the attention kernel) for the 8 new tokens, with k̄
-already built. A second leg times the
+already built. The same caches also time a decode-loop step with per-sequence lengths
+(append one token each, then varlen scoring, selection and attention). A
+second leg times the
 32K causal sparse prefill (kernel pooling + fused score/top-K + attention) in
 TFLOP/s, a third its backward (dq, dk, dv from the forward's selection,
 output and log-sum-exp for one upstream gradient) in TFLOP/s, and a fourth the
@@ -49,6 +51,21 @@ def decode_bytes(w) -> dict:
     kv = bg * (sel * 64 + own_keys) * w.head_dim * 2 * 2
     qo = w.batch * w.n_q_heads * w.head_dim * 2 * 2
     return dict(score=kbar + w.batch * w.n_q_heads * w.head_dim * 2, attn=kv + qo, total=kbar + kv + qo)
+
+
+def decode_loop_bytes(w, lens) -> dict:
+    """Bytes of one variable-length decode-loop step: per sequence the append (K and V rows of the
+    new token), the k̄ scan over its candidates and the selected plus own blocks of K and V."""
+    hk, D = w.n_kv_heads, w.head_dim
+    tot = dict(append=0, score=0, attn=0)
+    for L in lens:
+        C = (L - 1) // 64
+        tot["append"] += hk * 2 * D * 2 * 2                       # read new rows, write cache rows
+        tot["score"] += hk * C * 3 * D * 2 + w.n_q_heads * D * 2
+        own = (L - 1) % 64 + 1
+        tot["attn"] += hk * (min(C, w.top_k) * 64 + own) * D * 2 * 2 + w.n_q_heads * D * 2 * 2
+    tot["total"] = sum(tot.values())
+    return tot
 
 
 def prefill_flops(w) -> dict:
@@ -271,7 +288,29 @@ def bench_decode(w, steps, warmup, rotations, torch, lib, ops, synth):
     ms, stage_ms, _ = timed_loop(step, steps, warmup, torch)
     log("decode: capturing one graph of rotation steps and timing its replays")
     g_ms = graph_loop(step, len(sets), steps, warmup, torch)
-    return dict(ms=g_ms, eager_ms=ms, stage_ms=stage_ms, bytes=decode_bytes(w))
+
+    # the decode loop with per-sequence lengths: append one token per sequence (pooling the
+    # block it completes), then scores, selection and attention at the new lengths
+    lens = [kv_len - 1 - 4096 * b for b in range(w.batch)]
+    lens_old = torch.tensor(lens, dtype=torch.int64, device="cuda")
+    lens_new = lens_old + 1
+    k_new = torch.randn((w.batch, w.n_kv_heads, 1, w.head_dim), device="cuda").to(torch.bfloat16)
+    v_new = torch.randn_like(k_new)
+    nbv = lib.infllmv2_decode_varlen_workspace_bytes(cfg, kv_len)
+    wsv = torch.empty(nbv, dtype=torch.uint8, device="cuda")
+    def vstep(s):
+        k, v, kbar = sets[s % len(sets)]
+        return [
+            lambda: lib.infllmv2_append_kv(cfg, k_new, v_new, 1, k, v, kv_cap, lens_old, 0, kbar, None),
+            lambda: lib.infllmv2_score_blocks_varlen(cfg, q, lens_new, kbar, kv_cap, scores, None),
+            lambda: lib.infllmv2_sparse_attn_decode_varlen(cfg, q, k, v, kv_cap, lens_new, kv_len, scores, idx,
+                                                           out, None, wsv, nbv, None),
+        ]
+    log("decode loop (variable lengths): eager per-stage timing, then one graph of rotation steps")
+    _, vstage_ms, _ = timed_loop(vstep, steps, warmup, torch)
+    v_ms = graph_loop(vstep, len(sets), steps, warmup, torch)
+    varlen = dict(ms=v_ms, stage_ms=vstage_ms, lens=lens, bytes=decode_loop_bytes(w, [L + 1 for L in lens]))
+    return dict(ms=g_ms, eager_ms=ms, stage_ms=stage_ms, bytes=decode_bytes(w), varlen=varlen)
 
 
 # ------------------------------------------------------------------ prefill leg
@@ -457,6 +496,17 @@ def main():
         "step_hbm": {"algorithmic_bytes": b["total"], "achieved_gbs": round(step_gbs, 1),
                      "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
         "stages_ms": {k: round(v, 5) for k, v in stage.items()},
+    }
+    vl = dec["varlen"]
+    vb = vl["bytes"]
+    result["decode_loop_varlen"] = {
+        "workload": f"{wd.name} with per-sequence lengths 131071 - 4096 b, one appended token each",
+        "tok_s": round(wd.batch / (vl["ms"] * 1e-3), 1), "ms_per_step": round(vl["ms"], 5),
+        "stages_ms": {k: round(v, 5) for k, v in zip(["append_kv", "score_blocks_varlen",
+                                                       "sparse_attn_decode_varlen"], vl["stage_ms"])},
+        "step_hbm": {"algorithmic_bytes": vb["total"],
+                     "achieved_gbs": round(vb["total"] / (vl["ms"] * 1e-3) / 1e9, 1),
+                     "frac": round(vb["total"] / (vl["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
     if not args.no_prefill:
         wp = synth.WORKLOADS["prefill_32k"]
