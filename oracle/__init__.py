@@ -61,6 +61,8 @@ def lib():
         L.orc_pool.argtypes = [i32, i32, i32, i32, i32, i32, i64, i64, P, P]
         L.orc_scores.restype = i32
         L.orc_scores.argtypes = [i32, i32, i32, i32, i32, i32, P, i32, P, P, i64, i32, P, P, P]
+        L.orc_scores_lse.restype = i32
+        L.orc_scores_lse.argtypes = [i32, i32, i32, i32, i32, i32, P, i32, P, P, i64, dbl, i32, P, P, P]
         L.orc_select.restype = i32
         L.orc_select.argtypes = [i32, P, i64, P, i32, P]
         L.orc_keyset.restype = i64
@@ -135,6 +137,27 @@ def scores(q: np.ndarray, kbar: np.ndarray, pos: np.ndarray, rows: np.ndarray,
                           nblk_cap, len(rows), _ptr(rows), _ptr(R), _ptr(Cn))
     if rc:
         raise ValueError("orc_scores rejected its arguments")
+    return R, Cn
+
+
+def scores_lse(q: np.ndarray, kbar: np.ndarray, pos: np.ndarray, rows: np.ndarray,
+               n_kv_heads: int, scale: float | None = None, bs: int = 64):
+    """LSE-normalized block scores (orc_scores_lse): R [n_rows, nblk_cap] fp64, -inf past the
+    candidates, and candidate counts. scale defaults to 1/sqrt(D)."""
+    q = _c(q, np.uint16)
+    kbar = _c(kbar, np.uint16)
+    B, Hq, n_q, D = q.shape
+    nblk_cap, kpb = kbar.shape[2], kbar.shape[3]
+    rows = _c(rows, np.int32).reshape(-1, 3)
+    pos = _c(pos, np.int64)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    R = np.empty((len(rows), nblk_cap), dtype=np.float64)
+    Cn = np.empty(len(rows), dtype=np.int64)
+    rc = lib().orc_scores_lse(B, Hq, n_kv_heads, D, bs, kpb, _ptr(q), n_q, _ptr(pos), _ptr(kbar),
+                              nblk_cap, float(scale), len(rows), _ptr(rows), _ptr(R), _ptr(Cn))
+    if rc:
+        raise ValueError("orc_scores_lse rejected its arguments")
     return R, Cn
 
 

@@ -176,6 +176,62 @@ int orc_scores(int B, int Hq, int Hkv, int D, int bs, int kpb,
   return bad ? -1 : 0;
 }
 
+/* ------------------------------------------------ 2b. LSE-normalized scores
+ * [ARCH] "more efficient operators": a LogSumExp estimate lets the top-K
+ * blocks be chosen cheaply. The pages describe no formula; the reading taken
+ * here: per head h of the group, the kernel scores s = scale * q_h . kbar[j][m]
+ * over every candidate kernel (j < C, m < kpb) are softmax-normalized by their
+ * log-sum-exp LSE_h = log sum_{j,m} exp(s), a block's normalized relevance is
+ * the max over its kernels (as in section 2), and the group sums the heads:
+ *   R[j] = sum_h exp(max_m s_{h,j,m} - LSE_h),  j < C;  -inf elsewhere.
+ * Same rows, layouts and candidate rule as orc_scores. */
+int orc_scores_lse(int B, int Hq, int Hkv, int D, int bs, int kpb,
+                   const uint16_t* q, int n_q, const int64_t* pos,
+                   const uint16_t* kbar, int64_t nblk_cap, double scale,
+                   int n_rows, const int32_t* rows, double* R, int64_t* C) {
+  if (Hq % Hkv) return -1;
+  const int G = Hq / Hkv;
+  int bad = 0;
+  #pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)(nblk_cap * kpb + 1));
+    #pragma omp for schedule(dynamic)
+    for (int r = 0; r < n_rows; ++r) {
+      const int b = rows[3 * r], g = rows[3 * r + 1], i = rows[3 * r + 2];
+      if (b < 0 || b >= B || g < 0 || g >= Hkv || i < 0 || i >= n_q) { bad = 1; continue; }
+      int64_t c = pos[i] / bs;
+      if (c > nblk_cap) c = nblk_cap;
+      C[r] = c;
+      double* Rr = &R[(int64_t)r * nblk_cap];
+      for (int64_t j = 0; j < nblk_cap; ++j) Rr[j] = j < c ? 0.0 : -INFINITY;
+      for (int hh = 0; hh < G; ++hh) {
+        const int h = g * G + hh;
+        const uint16_t* qv = &q[(((int64_t)b * Hq + h) * n_q + i) * D];
+        double mx = -INFINITY;
+        for (int64_t j = 0; j < c; ++j)
+          for (int m = 0; m < kpb; ++m) {
+            const uint16_t* kv = &kbar[((((int64_t)b * Hkv + g) * nblk_cap + j) * kpb + m) * D];
+            double dot = 0.0;
+            for (int e = 0; e < D; ++e) dot += bf(&qv[e]) * bf(&kv[e]);
+            s[j * kpb + m] = scale * dot;
+            if (s[j * kpb + m] > mx) mx = s[j * kpb + m];
+          }
+        double l = 0.0;
+        for (int64_t t = 0; t < c * kpb; ++t) l += exp(s[t] - mx);
+        const double lse = mx + log(l);
+        for (int64_t j = 0; j < c; ++j) {
+          double best = -INFINITY;
+          for (int m = 0; m < kpb; ++m)
+            if (s[j * kpb + m] > best) best = s[j * kpb + m];
+          Rr[j] += exp(best - lse);
+        }
+      }
+    }
+    free(s);
+  }
+  return bad ? -1 : 0;
+}
+
 /* --------------------------------------------------------- 3. selection
  * [ARCH] section text and [LAUNCH] section 1: only the few most relevant
  * blocks take part in attention. Top-K by score (compared as fp32, the

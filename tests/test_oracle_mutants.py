@@ -39,6 +39,12 @@ MUTANTS = {
                                  "    if (dense_threshold > 0 && n_ctx <= dense_threshold) {\n      for (int64_t t = 0; t <= p; ++t)"),
     "tree_drops_prefix_tail": ("for (int64_t t = own * bs; t < P; ++t) keys[n++] = t;", ";"),
     "tree_slot_shift": ("keys[n++] = P + j;\n", "keys[n++] = P + j - (j > 0);\n"),
+    "lse_over_block_maxima": ("for (int64_t t = 0; t < c * kpb; ++t) l += exp(s[t] - mx);",
+                              "for (int64_t t = 0; t < c * kpb; t += kpb) l += exp(s[t] - mx);"),
+    "lse_unscaled": ("s[j * kpb + m] = scale * dot;", "s[j * kpb + m] = dot;"),
+    "lse_max_over_heads": ("Rr[j] += exp(best - lse);", "Rr[j] = fmax(Rr[j], exp(best - lse));"),
+    "lse_mean_not_max_over_kernels": ("if (s[j * kpb + m] > best) best = s[j * kpb + m];",
+                                      "best = (best == -INFINITY ? 0.0 : best) + s[j * kpb + m] / kpb;"),
     "window_start_off_by_one": ("for (int64_t t = p - window + 1 < 0 ? 0 : p - window + 1;",
                                 "for (int64_t t = p - window < 0 ? 0 : p - window;"),
     "window_excludes_own_key": ("t <= p && t < kv_len; ++t)\n      keys[n++] = t;",

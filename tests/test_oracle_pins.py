@@ -249,6 +249,87 @@ def test_topk_covering_all_blocks_equals_dense_causal(orc):
     assert np.allclose(sp["out"], ref[hr[:, 0], hr[:, 1], hr[:, 2]], rtol=0, atol=1e-12)
 
 
+# ---------------------------------------------------------------- LSE-normalized scores
+def _onehot_case(G):
+    """One group of G heads, D = 8, a row at position 130 (candidates: blocks 0 and 1).
+    Block 0's kernels: e0, 0, 0; block 1's: 0, 0, 0. Head 0's query is e0, the others 0."""
+    D, nblk = 8, 3
+    kbar = np.zeros((1, 1, nblk, 3, D), np.uint16)
+    kbar[0, 0, 0, 0, 0] = bfbits(1.0)
+    q = np.zeros((1, G, 1, D), np.uint16)
+    q[0, 0, 0, 0] = bfbits(1.0)
+    return q, kbar, np.array([130]), np.array([[0, 0, 0]], np.int32)
+
+
+def test_lse_scores_hand_example(orc):
+    # scale ln 2: head 0's kernel scores are ln2, 0, 0 | 0, 0, 0, so exp gives 2,1,1 | 1,1,1
+    # (sum 7): blocks get 2/7 and 1/7; every zero query sees six equal kernels: 1/6 each
+    q, kbar, pos, rows = _onehot_case(1)
+    R, C = orc.scores_lse(q, kbar, pos, rows, 1, scale=math.log(2.0))
+    assert C.tolist() == [2] and np.isneginf(R[0, 2])
+    assert np.allclose(R[0, :2], [2 / 7, 1 / 7], rtol=1e-14, atol=0)
+    q, kbar, pos, rows = _onehot_case(2)
+    R, _ = orc.scores_lse(q, kbar, pos, rows, 1, scale=math.log(2.0))
+    assert np.allclose(R[0, :2], [2 / 7 + 1 / 6, 1 / 7 + 1 / 6], rtol=1e-14, atol=0)
+
+
+def test_lse_scores_zero_query_closed_form(orc):
+    w = tiny("pin_lse0", seq_len=640)
+    d = synth.generate(w, seed=31)
+    kbar = orc.pool(d["k"], 640)
+    q = np.zeros_like(d["q"])
+    pos = np.arange(640)
+    rows = orc.all_group_rows(1, w.n_kv_heads, 640)
+    R, C = orc.scores_lse(q, kbar, pos, rows, w.n_kv_heads)
+    for r in range(0, len(rows), 37):                 # all 3C kernels tie: each block gets G / (3C)
+        c = int(C[r])
+        if c:
+            assert np.allclose(R[r, :c], w.group / (3 * c), rtol=1e-13, atol=0)
+        assert np.isneginf(R[r, c:]).all()
+
+
+def _selection_gap_ok(R, C, K):
+    """Rows whose K-th and (K+1)-th raw scores differ clearly (no fp32 near-ties)."""
+    ok = []
+    for r, c in enumerate(C):
+        if c <= K:
+            ok.append(True)
+            continue
+        srt = np.sort(R[r, :c])[::-1]
+        ok.append(srt[K - 1] - srt[K] > 1e-6 * max(1.0, abs(srt[K])))
+    return np.array(ok)
+
+
+def test_lse_selection_equals_raw_with_one_head_per_group(orc):
+    _lse_selection_equals_raw(orc, identical_heads=False)
+
+
+def test_lse_selection_equals_raw_with_identical_heads(orc):
+    _lse_selection_equals_raw(orc, identical_heads=True)
+
+
+def _lse_selection_equals_raw(orc, identical_heads):
+    """One head per group (or identical heads): R_lse = G exp(max_m s - LSE) is an increasing
+    function of the raw score, so both select the same blocks."""
+    if identical_heads:
+        w = tiny("pin_lse_same", n_q_heads=4, n_kv_heads=1, seq_len=900, top_k=3)
+    else:
+        w = tiny("pin_lse_g1", n_q_heads=2, n_kv_heads=2, seq_len=900, top_k=3)
+    d = synth.generate(w, seed=32)
+    q = d["q"].copy()
+    if identical_heads:
+        q[:, 1:] = q[:, :1]
+    kbar = orc.pool(d["k"], 900)
+    pos = np.arange(900)
+    rows = orc.all_group_rows(1, w.n_kv_heads, 900)
+    Rr, C = orc.scores(q, kbar, pos, rows, w.n_kv_heads)
+    Rl, C2 = orc.scores_lse(q, kbar, pos, rows, w.n_kv_heads)
+    assert np.array_equal(C, C2)
+    ok = _selection_gap_ok(Rr, C, w.top_k)
+    assert ok.mean() > 0.9
+    assert np.array_equal(orc.select(Rr, C, w.top_k)[ok], orc.select(Rl, C, w.top_k)[ok])
+
+
 # ---------------------------------------------------------------- sliding window (draft model)
 def test_window_keyset_rules(orc):
     assert orc.keyset(orc.MODE_WINDOW, 5, 100, None, 0, 0, window=3).tolist() == [3, 4, 5]
