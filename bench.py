@@ -7,7 +7,8 @@ over the whole k̄ table (infllmv2_score_blocks), then top-K selection and
 sparse attention (split + LSE combine; infllmv2_sparse_attn_decode_scores,
 which selects inside the attention kernel) for the 8 new tokens, with k̄
 already built. The same caches also time a decode-loop step with per-sequence lengths
-(append one token each, then varlen scoring, selection and attention). A
+(append one token each, then varlen scoring, selection and attention), and a
+decode step whose top-K comes from the LSE-normalized scores. A
 second leg times the
 32K causal sparse prefill (kernel pooling + fused score/top-K + attention) in
 TFLOP/s, a third its backward (dq, dk, dv from the forward's selection,
@@ -310,7 +311,25 @@ def bench_decode(w, steps, warmup, rotations, torch, lib, ops, synth):
     _, vstage_ms, _ = timed_loop(vstep, steps, warmup, torch)
     v_ms = graph_loop(vstep, len(sets), steps, warmup, torch)
     varlen = dict(ms=v_ms, stage_ms=vstage_ms, lens=lens, bytes=decode_loop_bytes(w, [L + 1 for L in lens]))
-    return dict(ms=g_ms, eager_ms=ms, stage_ms=stage_ms, bytes=decode_bytes(w), varlen=varlen)
+
+    # the same step with the LSE-normalized scores deciding the top-K
+    nbl = lib.infllmv2_score_lse_workspace_bytes(cfg, n_q, kv_cap)
+    wsl = torch.empty(nbl, dtype=torch.uint8, device="cuda")
+    def lstep(s):
+        k, v, kbar = sets[s % len(sets)]
+        return [
+            lambda: lib.infllmv2_score_blocks_lse(cfg, q, n_q, kv_len - 1, 0, kbar, kv_cap, scores, wsl, nbl,
+                                                  None),
+            lambda: lib.infllmv2_sparse_attn_decode_scores(cfg, q, k, v, kv_cap, kv_len, scores, idx, out, None,
+                                                           ws, nbytes, None),
+        ]
+    log("decode with LSE-normalized selection: eager per-stage timing, then one graph of rotation steps")
+    _, lstage_ms, _ = timed_loop(lstep, steps, warmup, torch)
+    l_ms = graph_loop(lstep, len(sets), steps, warmup, torch)
+    # the LSE scores add a write and a read of the per-head block values and tile partials
+    lse_extra = 2 * nbl
+    lsel = dict(ms=l_ms, stage_ms=lstage_ms, extra_bytes=lse_extra)
+    return dict(ms=g_ms, eager_ms=ms, stage_ms=stage_ms, bytes=decode_bytes(w), varlen=varlen, lse=lsel)
 
 
 # ------------------------------------------------------------------ prefill leg
@@ -496,6 +515,16 @@ def main():
         "step_hbm": {"algorithmic_bytes": b["total"], "achieved_gbs": round(step_gbs, 1),
                      "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
         "stages_ms": {k: round(v, 5) for k, v in stage.items()},
+    }
+    ls = dec["lse"]
+    lb = b["total"] + ls["extra_bytes"]
+    result["decode_lse_selection"] = {
+        "workload": f"{wd.name}, top-K from LSE-normalized scores",
+        "tok_s": round(wd.batch / (ls["ms"] * 1e-3), 1), "ms_per_step": round(ls["ms"], 5),
+        "stages_ms": {k: round(v, 5) for k, v in zip(["score_blocks_lse", "sparse_attn_decode_scores"],
+                                                     ls["stage_ms"])},
+        "step_hbm": {"algorithmic_bytes": lb, "achieved_gbs": round(lb / (ls["ms"] * 1e-3) / 1e9, 1),
+                     "frac": round(lb / (ls["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
     vl = dec["varlen"]
     vb = vl["bytes"]

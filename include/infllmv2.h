@@ -215,6 +215,27 @@ INFLLMV2_API int infllmv2_dense_attn(const infllmv2_cfg* cfg, const void* q, int
                         const void* v, int64_t kv_cap, int64_t kv_len, int32_t causal, void* out,
                         float* lse, void* stream);
 
+/* Bytes of workspace infllmv2_score_blocks_lse needs (0 if invalid). */
+INFLLMV2_API size_t infllmv2_score_lse_workspace_bytes(const infllmv2_cfg* cfg, int32_t n_q,
+                                          int64_t kv_cap);
+
+/* LSE-normalized block scores for the top-K choice (QbitAI summary,
+ * "Model architecture: InfLLM v2", item on more efficient operators: the
+ * top-K blocks are picked with the help of a LogSumExp estimate; the pages
+ * give no formula, so this is a reading). Per head h of a group, the kernel
+ * scores s = softmax_scale * q_h . kbar[j][m] over every candidate kernel
+ * (j < C, m < 3) are normalized by their log-sum-exp LSE_h, and
+ *   scores[j] = sum over the group's heads of exp(max_m s_{h,j,m} - LSE_h)
+ * for j < C, -inf otherwise (C as for infllmv2_score_blocks). Arguments,
+ * layouts and row positions as infllmv2_score_blocks, plus a workspace of
+ * infllmv2_score_lse_workspace_bytes() (per-head block values and per-tile
+ * partial sums; no initial contents). The output feeds infllmv2_topk_blocks
+ * (scores mode) and infllmv2_sparse_attn_decode_scores unchanged. */
+INFLLMV2_API int infllmv2_score_blocks_lse(const infllmv2_cfg* cfg, const void* q, int32_t n_q,
+                              int64_t q_pos0, int32_t is_tree, const void* kbar, int64_t kv_cap,
+                              float* scores, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* Decode-loop cache maintenance (QbitAI summary, efficiency evaluation: as
  * the context grows only the semantic-kernel representation grows with it, so
  * the kernel table is extended as blocks complete). Appends n_new tokens per

@@ -11,17 +11,21 @@ import numpy as np
 import synth
 
 
-def boundary_gaps(R, Cn, K):
+def boundary_gaps(R, Cn, K, relative=False):
     gaps = np.full(len(Cn), np.inf)
     for r, c in enumerate(Cn):
         if c > K:
             s = np.sort(R[r, :c])[::-1]
             gaps[r] = s[K - 1] - s[K]
+            if relative:
+                gaps[r] /= abs(s[K - 1])
     return gaps
 
 
-def open_gaps(d, orc, group_rows=None, min_gap=1e-3, max_attempts=64, kbar=None, pos=None):
-    """Redraw query tokens in-place in d["q"] until every listed row clears min_gap.
+def open_gaps(d, orc, group_rows=None, min_gap=1e-3, max_attempts=64, kbar=None, pos=None,
+              score_fn=None, relative=False):
+    """Redraw query tokens in-place in d["q"] until every listed row clears min_gap (relative to
+    the K-th score when `relative`; scores from score_fn, default the oracle's raw scores).
 
     Returns (kbar, number of token redraws, smallest gap seen after fixing)."""
     w = d["workload"]
@@ -35,8 +39,8 @@ def open_gaps(d, orc, group_rows=None, min_gap=1e-3, max_attempts=64, kbar=None,
     redrawn = 0
     min_seen = np.inf
     for attempt in range(max_attempts):
-        R, Cn = orc.scores(d["q"], kbar, pos, pending, w.n_kv_heads)
-        gaps = boundary_gaps(R, Cn, K)
+        R, Cn = (score_fn or orc.scores)(d["q"], kbar, pos, pending, w.n_kv_heads)
+        gaps = boundary_gaps(R, Cn, K, relative)
         bad = pending[gaps <= min_gap]
         ok = gaps[gaps > min_gap]
         if len(ok):

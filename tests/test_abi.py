@@ -116,6 +116,9 @@ CASES = [
     ("infllmv2_sparse_attn_decode_varlen", {}, (A, A, A, 64, A, 64, None, None, B, None, 0x100000, 1 << 30, None), -1, "scores is NULL"),
     ("infllmv2_sparse_attn_decode_varlen", dict(top_k=65), (A, A, A, 64, A, 64, A, None, B, None, 0x100000, 1 << 30, None), -2, "top_k above 64"),
     ("infllmv2_sparse_attn_decode_varlen", {}, (A, A, A, 64, A, 64, A, None, B, None, 0x100000, 16, None), -3, "workspace"),
+    ("infllmv2_score_blocks_lse", {}, (A, 1, 0, 0, B, 64, A, None, 0, None), -1, "workspace is NULL"),
+    ("infllmv2_score_blocks_lse", {}, (A, 1, 0, 0, B, 64, A, 0x100000, 16, None), -3, "workspace"),
+    ("infllmv2_score_blocks_lse", {}, (A, 1, 640, 0, B, 64, A, 0x100000, 1 << 30, None), -1, "beyond kv_cap"),
     ("infllmv2_sliding_window_attn", {}, (A, 1, A, A, 64, 64, 0, B, None, None), -1, "window"),
     ("infllmv2_sliding_window_attn", {}, (A, 65, A, A, 64, 64, 16, B, None, None), -1, "n_q"),
     ("infllmv2_sliding_window_attn", {}, (A, 1, A, A, 64, 64, 16, None, None, None), -1, "out is NULL"),
@@ -157,6 +160,8 @@ def test_workspace_bytes(t):
     vd = t.infllmv2_decode_varlen_workspace_bytes(cfg_ok(t, batch=8, top_k=4, dense_threshold=8192), 131072)
     assert vd > t.infllmv2_decode_workspace_bytes(cfg_ok(t, batch=8, top_k=4, dense_threshold=8192), 1, 131072)
     assert t.infllmv2_decode_varlen_workspace_bytes(cfg, 0) == 0
+    assert t.infllmv2_score_lse_workspace_bytes(cfg, 1, 131072) > 2048 * 4
+    assert t.infllmv2_score_lse_workspace_bytes(cfg, 0, 131072) == 0
 
 
 def test_binding_raises_with_status(t):

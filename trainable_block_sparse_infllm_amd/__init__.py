@@ -12,6 +12,7 @@ from .capi import (  # noqa: F401
     infllmv2_prefill_backward_workspace_bytes, infllmv2_sparse_attn_prefill_backward,
     infllmv2_sliding_window_attn, infllmv2_append_kv, infllmv2_score_blocks_varlen,
     infllmv2_decode_varlen_workspace_bytes, infllmv2_sparse_attn_decode_varlen,
+    infllmv2_score_lse_workspace_bytes, infllmv2_score_blocks_lse,
     infllmv2_strerror, infllmv2_last_error,
 )
 from . import ops  # noqa: F401

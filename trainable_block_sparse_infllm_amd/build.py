@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libinfllmv2.so")
-SOURCES = ["api.cpp", "pool.hip", "score.hip", "topk.hip", "topk_prefill.hip", "attn_rows.hip", "attn_prefill.hip",
+SOURCES = ["api.cpp", "pool.hip", "score.hip", "score_lse.hip", "topk.hip", "topk_prefill.hip", "attn_rows.hip", "attn_prefill.hip",
            "attn_decode.hip", "attn_backward.hip"]
 ARCH = "gfx950"
 

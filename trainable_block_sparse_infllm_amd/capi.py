@@ -22,6 +22,7 @@ EXPORTS = [
     "infllmv2_prefill_backward_workspace_bytes", "infllmv2_sparse_attn_prefill_backward",
     "infllmv2_sliding_window_attn", "infllmv2_append_kv", "infllmv2_score_blocks_varlen",
     "infllmv2_decode_varlen_workspace_bytes", "infllmv2_sparse_attn_decode_varlen",
+    "infllmv2_score_lse_workspace_bytes", "infllmv2_score_blocks_lse",
     "infllmv2_strerror",
     "infllmv2_last_error",
 ]
@@ -71,6 +72,8 @@ def lib():
             "infllmv2_dense_attn": (i32, [cfg, P, i32, P, P, i64, i64, i32, P, P, P]),
             "infllmv2_sliding_window_attn": (i32, [cfg, P, i32, P, P, i64, i64, i64, P, P, P]),
             "infllmv2_append_kv": (i32, [cfg, P, P, i32, P, P, i64, P, i64, P, P]),
+            "infllmv2_score_lse_workspace_bytes": (C.c_size_t, [cfg, i32, i64]),
+            "infllmv2_score_blocks_lse": (i32, [cfg, P, i32, i64, i32, P, i64, P, P, C.c_size_t, P]),
             "infllmv2_score_blocks_varlen": (i32, [cfg, P, P, P, i64, P, P]),
             "infllmv2_decode_varlen_workspace_bytes": (C.c_size_t, [cfg, i64]),
             "infllmv2_sparse_attn_decode_varlen": (i32, [cfg, P, P, P, i64, P, i64, P, P, P, P, P,
@@ -201,3 +204,13 @@ def infllmv2_sparse_attn_decode_varlen(cfg, q, k_cache, v_cache, kv_cap, kv_lens
                                                     _p(kv_lens), kv_len_max, _p(scores), _p(idx_out),
                                                     _p(out), _p(lse), _p(workspace), workspace_bytes,
                                                     _s(stream)))
+
+
+def infllmv2_score_lse_workspace_bytes(cfg, n_q, kv_cap):
+    return lib().infllmv2_score_lse_workspace_bytes(C.byref(cfg), n_q, kv_cap)
+
+
+def infllmv2_score_blocks_lse(cfg, q, n_q, q_pos0, is_tree, kbar, kv_cap, scores, workspace, workspace_bytes,
+                              stream=None):
+    _check(lib().infllmv2_score_blocks_lse(C.byref(cfg), _p(q), n_q, q_pos0, int(is_tree), _p(kbar), kv_cap,
+                                           _p(scores), _p(workspace), workspace_bytes, _s(stream)))

@@ -172,6 +172,37 @@ int infllmv2_score_blocks(const infllmv2_cfg* cfg, const void* q, int32_t n_q, i
   return INFLLMV2_OK;
 }
 
+size_t infllmv2_score_lse_workspace_bytes(const infllmv2_cfg* cfg, int32_t n_q, int64_t kv_cap) {
+  Dims d;
+  if (check_cfg("infllmv2_score_lse_workspace_bytes", cfg, false, &d) != INFLLMV2_OK) return 0;
+  if (n_q < 1 || kv_cap < 1) return 0;
+  return infllmv2::score_lse_workspace_bytes(d, n_q, nblk_of(kv_cap));
+}
+
+int infllmv2_score_blocks_lse(const infllmv2_cfg* cfg, const void* q, int32_t n_q, int64_t q_pos0,
+                              int32_t is_tree, const void* kbar, int64_t kv_cap, float* scores,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "infllmv2_score_blocks_lse";
+  Dims d;
+  TRY(check_cfg(fn, cfg, false, &d));
+  TRY(check_ptr(fn, q, "q", 16));
+  TRY(check_ptr(fn, kbar, "kbar", 16));
+  TRY(check_ptr(fn, scores, "scores", 4));
+  TRY(check_rows(fn, d, n_q, q_pos0, is_tree, kv_cap));
+  TRY(check_ptr(fn, workspace, "workspace", 256));
+  const size_t need = infllmv2::score_lse_workspace_bytes(d, n_q, nblk_of(kv_cap));
+  if (workspace_bytes < need) {
+    char msg[128];
+    std::snprintf(msg, sizeof msg, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    return fail(INFLLMV2_WORKSPACE_TOO_SMALL, fn, msg);
+  }
+  TRY(check_device(fn));
+  LAUNCH(fn, infllmv2::launch_scores_lse(d, static_cast<const uint16_t*>(q), n_q, q_pos0, is_tree != 0,
+                                         static_cast<const uint16_t*>(kbar), nblk_of(kv_cap), scores,
+                                         workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+  return INFLLMV2_OK;
+}
+
 int infllmv2_topk_blocks(const infllmv2_cfg* cfg, const float* scores, const void* q,
                          const void* kbar, int32_t n_q, int64_t q_pos0, int32_t is_tree,
                          int64_t kv_cap, int32_t* idx, void* stream) {

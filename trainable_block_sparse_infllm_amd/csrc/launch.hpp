@@ -30,6 +30,13 @@ hipError_t launch_scores(const Dims& d, const uint16_t* q, int n_q, int64_t q_po
                          const uint16_t* kbar, int64_t nblk, float* scores, hipStream_t s,
                          const int64_t* kv_lens = nullptr);
 
+// LSE-normalized block scores (same layout as launch_scores), through a
+// workspace of score_lse_workspace_bytes().
+size_t score_lse_workspace_bytes(const Dims& d, int n_q, int64_t nblk);
+hipError_t launch_scores_lse(const Dims& d, const uint16_t* q, int n_q, int64_t q_pos0,
+                             int is_tree, const uint16_t* kbar, int64_t nblk, float* scores,
+                             void* ws, size_t ws_bytes, hipStream_t s);
+
 hipError_t launch_topk_from_scores(const Dims& d, const float* scores, int n_q, int64_t q_pos0,
                                    int is_tree, int64_t nblk, int32_t* idx, hipStream_t s);
 

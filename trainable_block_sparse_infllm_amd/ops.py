@@ -125,6 +125,36 @@ def dense(cfg, q, k, v, kv_len, *, causal=True, with_lse=True, stream=None):
     return dict(out=out, lse=lse)
 
 
+def score_blocks_lse(cfg, q, kbar, q_pos0, kv_cap, *, is_tree=False, ws: Workspace | None = None, stream=None):
+    """LSE-normalized block scores [B][Hkv][n_q][kv_cap/64] (the layout of the raw scores)."""
+    B, Hq, n_q, D = q.shape
+    scores = torch.empty((B, cfg.n_kv_heads, n_q, nblk(kv_cap)), dtype=torch.float32, device=q.device)
+    nbytes = capi.infllmv2_score_lse_workspace_bytes(cfg, n_q, kv_cap)
+    ws = ws or Workspace(q.device)
+    buf = ws.get(nbytes)
+    capi.infllmv2_score_blocks_lse(cfg, q, n_q, q_pos0, is_tree, kbar, kv_cap, scores, buf, buf.numel(), stream)
+    return scores
+
+
+def decode_step_lse(cfg, q, k_cache, v_cache, kbar, kv_len, *, ws: Workspace | None = None, with_lse=True,
+                    stream=None):
+    """A single-token decode step whose top-K uses the LSE-normalized scores."""
+    B, Hq, n_q, D = q.shape
+    if n_q != 1:
+        raise ValueError("decode_step_lse takes one new token per sequence")
+    kv_cap = k_cache.shape[2]
+    ws = ws or Workspace(q.device)
+    scores = score_blocks_lse(cfg, q, kbar, kv_len - 1, kv_cap, ws=ws, stream=stream)
+    idx = torch.empty((B, cfg.n_kv_heads, 1, cfg.top_k), dtype=torch.int32, device=q.device)
+    out = _bf16_like((B, Hq, 1, D), q)
+    lse = torch.empty((B, Hq, 1), dtype=torch.float32, device=q.device) if with_lse else None
+    nbytes = capi.infllmv2_decode_workspace_bytes(cfg, 1, kv_len)
+    buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    capi.infllmv2_sparse_attn_decode_scores(cfg, q, k_cache, v_cache, kv_cap, kv_len, scores, idx, out, lse,
+                                            buf, nbytes, stream)
+    return dict(scores=scores, idx=idx, out=out, lse=lse)
+
+
 def append_kv(cfg, k_new, v_new, k_cache, v_cache, kbar=None, *, kv_len=None, kv_lens=None, stream=None):
     """Write k_new, v_new [B][Hkv][n_new][D] at each sequence's length (kv_lens, a device int64
     tensor [B], or the scalar kv_len) and pool the blocks this completes into kbar."""
