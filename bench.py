@@ -107,7 +107,9 @@ ENTRY_KERNELS = {
                            ("attn_decode.hip", "topk_select.hpp")),
     "sparse_attn_decode_scores": (("decode_split_kernel", "decode_combine_kernel"),
                                   ("attn_decode.hip", "topk_select.hpp")),
-    "sparse_attn_prefill": (("prefill_attn_kernel",), ("attn_prefill.hip",)),
+    "sparse_attn_prefill": (("prefill_attn_kernel",), ("attn_prefill.hip", "prefill_tile.hpp")),
+    "sliding_window_attn": (("window_attn_kernel",), ("attn_prefill.hip", "prefill_tile.hpp")),
+    "score_blocks_lse": (("score_lse_kernel", "score_lse_combine_kernel"), ("score_lse.hip",)),
     "topk_blocks_fused": (("topk_prefill_kernel", "topk_fused_kernel"),
                           ("topk.hip", "topk_prefill.hip", "topk_select.hpp")),
     "sparse_attn_prefill_backward": (("bwd_zero_kernel", "bwd_zero_rows_kernel", "bwd_prep_kernel",
@@ -160,6 +162,17 @@ def summarize_trace(db: str, title: str, command: str) -> str:
     for n, c, sm, a, mn, mx in rows:
         out.append(f"| `{_short(n)}` | {c} | {a / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} | "
                    f"{sm / 1e3:.1f} | {100 * sm / tot:.1f} |")
+    return "\n".join(out) + "\n"
+
+
+def traffic_markdown(t: dict) -> str:
+    """Markdown table of the per-kernel counters and calibrated bytes stored in traffic.json."""
+    out = ["| entry point | kernel | dispatches | FETCH KiB | WRITE KiB | HBM bytes / launch (calibrated) |",
+           "|---|---|---|---|---|---|"]
+    for entry, e in t["entries"].items():
+        for kn, k in e["kernels"].items():
+            out.append(f"| {entry} | `{kn}` | {k['dispatches']} | {k['fetch_kib']:.0f} | {k['write_kib']:.0f} | "
+                       f"{e['bytes_per_launch']:,} |")
     return "\n".join(out) + "\n"
 
 
@@ -448,11 +461,17 @@ def main():
                     help="print a markdown summary of a rocprofv3 --kernel-trace database and exit")
     ap.add_argument("--title", default="kernel trace")
     ap.add_argument("--command", default="")
+    ap.add_argument("--traffic-md", action="store_true",
+                    help="print profiles/traffic.json as a markdown table and exit")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="write profiles/traffic.json from FETCH_SIZE and WRITE_SIZE runs of this bench and exit")
     args = ap.parse_args()
     if args.summarize_trace:
         sys.stdout.write(summarize_trace(args.summarize_trace, args.title, args.command))
+        return
+    if args.traffic_md:
+        with open(TRAFFIC_FILE) as fh:
+            sys.stdout.write(traffic_markdown(json.load(fh)))
         return
     if args.summarize_pmc:
         # the decode leg clones the 2 GiB K and V caches of decode_128k_b8 for its rotations
@@ -576,7 +595,8 @@ def main():
             "algorithmic_gflop": round(sw["flops"] / 1e9, 2),
             "roofline": {"bound": "mfma", "kernel": "sliding_window_attn", "achieved": round(wtf, 2),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(wtf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+                         "frac": round(wtf / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic("sliding_window_attn")},
         }
     if args.copy_calibration:
         n = 1 << 30

@@ -51,12 +51,16 @@ namespace infllmv2 {
 
 using namespace tile;
 
-template <int G>
-__global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void prefill_attn_kernel(
+// The kernel body; WINDOW (mode 3) is a template flag so the sliding-window
+// code is compiled out of modes 0-2 and the two run as separately named
+// kernels.
+template <int G, bool WINDOW>
+__device__ __forceinline__ void prefill_attn_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ out, float* __restrict__ lse, int Hq,
     int Hkv, int n_q, int64_t kv_cap, int64_t kv_len, int K, int dense_thr, int mode,
     int64_t window, float scale_log2, int ntile, int umax) {
+  if constexpr (WINDOW) mode = 3;
   using Sh = PrefillShape<G>;
   constexpr int TPS = Sh::TPS, NW = Sh::NW, TQ = Sh::TQ, NT = Sh::NT, LPS = Sh::LPS;
   constexpr int DS = kD / 16;                // k-steps of S^T = K Q^T
@@ -91,7 +95,7 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
   const bool tile_dense = dend >= ntok;
   // a tile walking a contiguous range starts at block blk0 (mode 3: the block
   // holding its first token's window start)
-  const int64_t blk0 = mode == 3 ? (base - window + 1 > 0 ? (base - window + 1) / kBlock : 0) : 0;
+  const int64_t blk0 = WINDOW ? (base - window + 1 > 0 ? (base - window + 1) / kBlock : 0) : 0;
   const uint16_t* kbase = k + int64_t(bg) * kv_cap * kD;
   const uint16_t* vbase = v + int64_t(bg) * kv_cap * kD;
 
@@ -256,7 +260,7 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
     }
     // sliding window: keys before a row's window start, in a block that some
     // row of the wavefront sees only in part
-    if (mode == 3 && key0 < p_first + TPS - window) {
+    if (WINDOW && key0 < p_first + TPS - window) {
       const int64_t rlo = row_p - window + 1 - key0;                  // first visible key
       const int lo = int(rlo > 0 ? (rlo < kBlock ? rlo : kBlock) : 0);
 #pragma unroll
@@ -357,6 +361,26 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void pr
   }
 }
 
+template <int G>
+__global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void prefill_attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ idx, uint16_t* __restrict__ out, float* __restrict__ lse, int Hq,
+    int Hkv, int n_q, int64_t kv_cap, int64_t kv_len, int K, int dense_thr, int mode,
+    int64_t window, float scale_log2, int ntile, int umax) {
+  prefill_attn_body<G, false>(q, k, v, idx, out, lse, Hq, Hkv, n_q, kv_cap, kv_len, K, dense_thr,
+                              mode, window, scale_log2, ntile, umax);
+}
+
+template <int G>
+__global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void window_attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ idx, uint16_t* __restrict__ out, float* __restrict__ lse, int Hq,
+    int Hkv, int n_q, int64_t kv_cap, int64_t kv_len, int K, int dense_thr, int mode,
+    int64_t window, float scale_log2, int ntile, int umax) {
+  prefill_attn_body<G, true>(q, k, v, idx, out, lse, Hq, Hkv, n_q, kv_cap, kv_len, K, dense_thr,
+                             mode, window, scale_log2, ntile, umax);
+}
+
 int prefill128_stages(const Dims& d, int mode, int64_t kv_len) {
   if (d.D != 128) return 0;
   const int64_t nb = (kv_len - 1) / kBlock + 1;
@@ -379,11 +403,15 @@ static hipError_t launch_prefill_t(const Dims& d, int mode, const uint16_t* q, i
   const int64_t nb = (kv_len - 1) / kBlock + 1;
   if (prefill128_stages(d, mode, kv_len) == 0) return hipErrorInvalidValue;
   const int64_t umax = prefill_umax(d, mode, nb);
-  auto kern = prefill_attn_kernel<G>;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     160 * 1024);
+  auto kern = mode == 3 ? window_attn_kernel<G> : prefill_attn_kernel<G>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(prefill_attn_kernel<G>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  static const hipError_t attr_w = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(window_attn_kernel<G>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
+  if (attr_w != hipSuccess) return attr_w;
   const dim3 grid(unsigned(int64_t(d.B) * d.Hkv * ntile));
   kern<<<grid, Sh::NT, prefill_lds(umax, Sh::TQ, d.K), s>>>(
       q, k, v, idx, out, lse, d.Hq, d.Hkv, n_q, kv_cap, kv_len, d.K, d.dense_thr, mode, window,
