@@ -37,6 +37,10 @@ CASES = {
                     dense_threshold=0, n_plant=1),
     "g16_dense": W0.scaled(name="bwd_g16", n_q_heads=16, n_kv_heads=1, head_dim=128, seq_len=500, top_k=2,
                            dense_threshold=600, n_plant=1),
+    # the 32K workload's shape rules at 3K tokens and batch 2: K = 16, a 1024-token dense
+    # prefix, many segments per block, split blocks and full chunk rings
+    "t3072_k16_b2": W0.scaled(name="bwd_t3k", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, seq_len=3072,
+                              top_k=16, dense_threshold=1024, n_plant=8),
 }
 
 

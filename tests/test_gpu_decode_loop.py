@@ -173,3 +173,37 @@ def test_varlen_scores_match_oracle_and_mask_past_candidates():
             row = gs[b, g, 0]
             assert np.all(np.isneginf(row[C:])), (b, g)
             assert np.allclose(row[:C], R[g, :C], rtol=1e-5, atol=1e-3), (b, g)
+
+
+def test_varlen_decode_128k_batch8_full_size():
+    """The measured decode_128k_b8 shapes with per-sequence lengths 131072 - 4096 b: an append
+    of one token per sequence, then varlen scores, selection and attention, checked against the
+    oracle for every sequence."""
+    w = synth.WORKLOADS["decode_128k_b8"]
+    d = synth.generate(w, seed=0, threads=16)
+    kf, vf, cap = d["k"], d["v"], d["kv_cap"]
+    B = w.batch
+    lens0 = [131071 - 4096 * b for b in range(B)]
+    cur = [L + 1 for L in lens0]
+    note(f"varlen full size: lengths {cur}")
+    cfg = cfg_of(w)
+    k_cache, v_cache = dev_bf16(kf), dev_bf16(vf)
+    kbar = ops.pool_kernels(cfg, k_cache, cap, min(lens0))
+    for b, l0 in enumerate(lens0):                       # each sequence's complete blocks
+        ops.pool_kernels(cfg_of(w, batch=1), k_cache[b:b + 1], cap, l0, kbar=kbar[b:b + 1])
+    kn = np.stack([kf[b, :, lens0[b]:lens0[b] + 1] for b in range(B)])
+    vn = np.stack([vf[b, :, lens0[b]:lens0[b] + 1] for b in range(B)])
+    lens = torch.tensor(lens0, dtype=torch.int64, device="cuda")
+    ops.append_kv(cfg, dev_bf16(kn), dev_bf16(vn), k_cache, v_cache, kbar, kv_lens=lens)
+    lens += 1
+    q = _open_step_gaps(w, d["q"].copy(), kf, cur, 0)
+    res = ops.decode_step_varlen(cfg, dev_bf16(q), k_cache, v_cache, kbar, lens, max(cur))
+    torch.cuda.synchronize()
+    gidx = res["idx"].cpu().numpy()
+    gout, glse = host_f64(res["out"]), host_f64(res["lse"])
+    for b in range(B):
+        ref = _oracle_step(w, q, kf, vf, b, cur[b])
+        assert np.array_equal(gidx[b:b + 1], ref["idx"]), f"seq {b}: block indices differ"
+        hr = ref["head_rows"]
+        assert_close_rows(gout[b][hr[:, 1], hr[:, 2]], ref["out"], f"seq {b} out")
+        assert np.abs(glse[b][hr[:, 1], hr[:, 2]] - ref["lse"]).max() <= LSE_ABS

@@ -554,15 +554,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
     const float* __restrict__ delta, const int32_t* __restrict__ list,
     const int4* __restrict__ seg, const int32_t* __restrict__ nseg, float* __restrict__ dk,
     float* __restrict__ dv, int Hq, int Hkv, int n_q, int64_t kv_cap, int64_t kv_len,
-    int64_t emax, int64_t smax, float scale_log2, float scale) {
+    int64_t emax, int64_t smax, int64_t total_items, float scale_log2, float scale) {
   constexpr int DS = kD / 16;
   constexpr int DT = kD / 32;
   extern __shared__ __align__(16) char smem[];
   char* ring = smem;                                  // kDkvSlots x (Q, dO, metadata)
   int32_t* s_tok = reinterpret_cast<int32_t*>(ring + kDkvSlots * kDkvStage);
 
-  const int bg = blockIdx.x / int(smax);
-  const int sidx = blockIdx.x % int(smax);
+  // Workgroups go to the XCDs round-robin by index; chunks of 8 consecutive
+  // segments are dealt to the XCDs in turn, so the segments of one split
+  // block (adjacent in the table) share an L2 for their atomic adds while the
+  // workgroups running at once still cover consecutive segments.
+  const int x = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
+  const int64_t item = (int64_t(slot / 8) * kNumXcd + x) * 8 + slot % 8;
+  if (item >= total_items) return;
+  const int bg = int(item / smax);
+  const int sidx = int(item % smax);
   if (sidx >= nseg[bg]) return;
   const int4 sg = seg[int64_t(bg) * smax + sidx];
   const int j = sg.x, start = sg.y, len = sg.z;
@@ -872,9 +879,11 @@ static hipError_t launch_bwd_t(const Dims& d, const uint16_t* q, int n_q, const 
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        160 * 1024);
     if (attr != hipSuccess) return attr;
-    kern<<<dim3(unsigned(L.bgs * L.smax)), 256, dkv_lds(G), s>>>(
+    const int64_t items = L.bgs * L.smax;
+    const int64_t grid = (items + 8 * kNumXcd - 1) / (8 * kNumXcd) * (8 * kNumXcd);
+    kern<<<dim3(unsigned(grid)), 256, dkv_lds(G), s>>>(
         q, k, v, dout, lse2, delta, list, seg, nseg, dk, dv, d.Hq, d.Hkv, n_q, kv_cap, kv_len,
-        L.emax, L.smax, sl2, d.scale);
+        L.emax, L.smax, items, sl2, d.scale);
   }
   return hipGetLastError();
 }
