@@ -249,6 +249,22 @@ def test_topk_covering_all_blocks_equals_dense_causal(orc):
     assert np.allclose(sp["out"], ref[hr[:, 0], hr[:, 1], hr[:, 2]], rtol=0, atol=1e-12)
 
 
+# ---------------------------------------------------------------- the pages' figures
+def test_attended_fraction_matches_the_pages_bound(orc):
+    """tests/golden/page_claims.json: at the pages' context lengths (32K pretraining window,
+    128K evaluation) a long-context row attends fewer than 5% of the keys before it, under the
+    top-K settings of the measured workloads (K = 16 at 32K, K = 32 at 128K)."""
+    import json, os
+    claims = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_claims.json")))
+    bound = claims["attended_fraction_below"]["value"]
+    for L, K in [(claims["pretrain_context"]["value"], 16), (claims["eval_context"]["value"], 32)]:
+        p = L - 1
+        sel = np.arange(K, dtype=np.int32) * ((p // 64) // K)          # any K distinct candidates
+        keys = orc.keyset(orc.MODE_SPARSE, p, L, sel, K, 1024)
+        assert len(keys) == K * 64 + p % 64 + 1
+        assert len(keys) / (p + 1) < bound, (L, K, len(keys))
+
+
 # ---------------------------------------------------------------- LSE-normalized scores
 def _onehot_case(G):
     """One group of G heads, D = 8, a row at position 130 (candidates: blocks 0 and 1).
