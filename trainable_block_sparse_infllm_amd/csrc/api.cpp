@@ -86,19 +86,19 @@ int check_kv(const char* fn, int64_t kv_cap, int64_t kv_len) {
 // Device check (first HIP call of an accepted request): gfx950 only.
 int check_device(const char* fn) {
   static std::mutex mu;
-  static int verdict[64] = {0};   // 0 unknown, 1 ok, -1 unsupported
+  static int arch_ok[64] = {0};   // 0 unknown, 1 gfx950, -1 another device
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail_hip(fn, e);
   if (dev < 0 || dev >= 64) return fail(INFLLMV2_UNSUPPORTED, fn, "device ordinal above 63");
   std::lock_guard<std::mutex> lock(mu);
-  if (verdict[dev] == 0) {
+  if (arch_ok[dev] == 0) {
     hipDeviceProp_t prop;
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return fail_hip(fn, e);
-    verdict[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    arch_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
   }
-  if (verdict[dev] < 0) return fail(INFLLMV2_UNSUPPORTED, fn, "device is not gfx950 (MI355X)");
+  if (arch_ok[dev] < 0) return fail(INFLLMV2_UNSUPPORTED, fn, "device is not gfx950 (MI355X)");
   return INFLLMV2_OK;
 }
 
