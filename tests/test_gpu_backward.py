@@ -125,3 +125,36 @@ def test_prefill_backward_heavy_keys_split_atomically(case):
     fw = ops.sparse_prefill(cfg, dev_bf16(d["q"]), dev_bf16(d["k"]), dev_bf16(d["v"]))
     rows = _rows_per_block(fw["idx"].cpu().numpy(), w.seq_len, w.top_k, w.group, w.dense_threshold)
     assert rows.max() > 4096, f"no block needs a split (max rows {rows.max()})"
+
+
+@pytest.mark.parametrize("n_q,kv_len,thr", [(500, 1200, 0), (333, 900, 700), (64, 2000, 0)])
+def test_prefill_backward_chunk_after_prefix(n_q, kv_len, thr):
+    """A chunk of n_q queries at positions kv_len - n_q .. kv_len - 1 over a longer cache:
+    prefix keys get dk, dv from the rows that attend them; rows past kv_len stay untouched."""
+    w = W0.scaled(name="bwd_chunk", n_q_heads=8, n_kv_heads=2, head_dim=128, seq_len=kv_len, top_k=4,
+                  dense_threshold=thr, n_plant=2)
+    note(f"backward chunk n_q{n_q} kv_len{kv_len} thr{thr}")
+    d = synth.generate(w, seed=9)
+    cfg = cfg_of(w)
+    cap = d["kv_cap"]
+    P = kv_len - n_q
+    qh = np.ascontiguousarray(d["q"][:, :, P:])
+    q, k, v = dev_bf16(qh), dev_bf16(d["k"]), dev_bf16(d["v"])
+    kbar = ops.pool_kernels(cfg, k, cap, kv_len)
+    idx = torch.empty((1, w.n_kv_heads, n_q, w.top_k), dtype=torch.int32, device="cuda")
+    lib.infllmv2_topk_blocks(cfg, None, q, kbar, n_q, P, 0, cap, idx, None)
+    out = torch.empty_like(q)
+    lse = torch.empty((1, w.n_q_heads, n_q), dtype=torch.float32, device="cuda")
+    lib.infllmv2_sparse_attn_prefill(cfg, q, n_q, k, v, cap, kv_len, idx, out, lse, None)
+    rng = np.random.default_rng(11)
+    dout_h = synth.to_bf16_bits(rng.standard_normal(qh.shape).astype(np.float32)).reshape(qh.shape)
+    g = ops.sparse_prefill_backward(cfg, q, k, v, idx, out, lse, dev_bf16(dout_h), kv_len=kv_len)
+    torch.cuda.synchronize()
+    pos = orc.positions("prefill", n_q, P)
+    dq, dk, dv = orc.attend_backward(orc.MODE_SPARSE, qh, d["k"], d["v"], pos, kv_len, w.n_kv_heads, dout_h,
+                                     idx=idx.cpu().numpy(), dense_threshold=thr)
+    bad = _close("dq", g["dq"].cpu().numpy(), dq, 1e-2)
+    bad += _close("dk", g["dk"].cpu().numpy()[:, :, :kv_len], dk[:, :, :kv_len], 2e-3)
+    bad += _close("dv", g["dv"].cpu().numpy()[:, :, :kv_len], dv[:, :, :kv_len], 2e-3)
+    assert not bad, bad
+    assert (g["dk"][:, :, kv_len:] == 0).all() and (g["dv"][:, :, kv_len:] == 0).all()
