@@ -134,6 +134,12 @@ def test_rejected_before_any_hip_call(t, name, over, args, status, frag):
     assert frag in msg and name in msg
 
 
+def test_empty_append_is_a_no_op_without_device_work(t):
+    cfg = cfg_ok(t)
+    rc, msg = call(t, "infllmv2_append_kv", cfg, A, A, 0, A, A, 64, None, 64, None, None)
+    assert rc == 0, msg
+
+
 def test_strerror(t):
     assert t.infllmv2_strerror(0) == "ok"
     assert t.infllmv2_strerror(-1) == "invalid argument"
