@@ -22,9 +22,9 @@
 //            prefix sums, fill) and its even split into segments of at most
 //            kSegRows query rows;
 //   dkv   -- key-centric: a workgroup owns one segment of one block's list;
-//            K and V of the block stay in LDS, chunks of 64 query rows (Q, dO
-//            and the rows' token, lse and Delta) stream through a three-stage
-//            LDS ring, and dK^T, dV^T stay in MFMA accumulators (S = Q K^T,
+//            K and V of the block stay in registers, chunks of 64 query rows
+//            (Q, dO and the rows' token, lse and Delta) stream through a
+//            four-slot LDS ring, and dK^T, dV^T stay in MFMA accumulators (S = Q K^T,
 //            dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS with Q^T and dO^T
 //            from transpose reads). A block split into several segments adds
 //            its partial sums atomically, so the fp32 summation order of dk
@@ -277,14 +277,29 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void bw
       uu.w = cvt_pk_bf16(ds_[6], ds_[7]);
       sf[ks] = as_bf16x8(uu);
     }
-    // dQ^T += K^T dS^T: K^T fragments by transpose reads of the K tile.
-    const lds_char* kt_l = (const lds_char*)kt_b;
+    // dQ^T += K^T dS^T: K^T fragments by transpose reads of the K tile, run
+    // ahead of the MFMAs that use them (S and dP are dead by now, so their
+    // registers hold the fragments).
+    {
+      const lds_char* kt_l = (const lds_char*)kt_b;
+      bf16x8 kfr[DT][4];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        dqacc[dt] = mfma32(lds_read_vt(kt_l + ks * 4096, t_lane[0] ^ (dt << 6), t_lane[1] ^ (dt << 6)),
-                           sf[ks], dqacc[dt]);
+        for (int ks = 0; ks < 4; ++ks)
+          kfr[dt][ks] = lds_read_vt(kt_l + ks * 4096, t_lane[0] ^ (dt << 6), t_lane[1] ^ (dt << 6));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) dqacc[dt] = mfma32(kfr[dt][ks], sf[ks], dqacc[dt]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
   }
 
   // dqacc[dt] register r of lane l: d = 32*dt + 8*(r/4) + 4*hl + r%4 of row r32.
