@@ -242,6 +242,11 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
   }
   const int u0 = split * sb;
   const int u1 = min(u0 + sb, n_e);
+  // A multi-row call sizes its splits for the largest possible union, and its
+  // combine reads only the splits that hold entries (u_count): a split past
+  // the union has nothing to write. (Single-token rows keep every split: their
+  // combine reads all of them.)
+  if (n_q > 1 && nsplit > 1 && u0 >= n_e) return;
 
   // block list of a single-token row selected here from its scores
   __shared__ int32_t s_sel[SKPL > 0 ? 64 : 1];
