@@ -45,6 +45,10 @@ PREFILL_CASES = {
                                      dense_threshold=0, n_plant=0),
     "tiny_prefill_2k": W["tiny_prefill_2k"],
     "prefill_4k_full_heads": P0.scaled(name="p_4k", seq_len=4096),
+    # head_dim 64 with enough (b, g) tiles for the rows kernel's full sub-tile count (the small
+    # cases above take its one-sub-tile form)
+    "d64_full_tiles": P0.scaled(name="p_d64_big", batch=2, n_q_heads=16, n_kv_heads=8, head_dim=64,
+                                seq_len=4096, top_k=8, dense_threshold=1024, n_plant=4),
 }
 
 DECODE_CASES = {

@@ -358,9 +358,19 @@ hipError_t launch_attn_rows(const Dims& d, int mode, const uint16_t* q, int n_q,
                             uint16_t* out, float* lse, hipStream_t s) {
   if (prefill128_stages(d, mode, kv_len) > 0)
     return launch_prefill128(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s);
+  // Sub-tiles per wavefront: the full count when the grid fills the chip,
+  // one when it would leave most CUs idle (a short or single-group call),
+  // which gives four times as many workgroups.
+  auto workgroups = [&](int nst) {
+    const int tq = 4 * nst * (16 / d.G);
+    return int64_t(d.B) * d.Hkv * ((n_q + tq - 1) / tq);
+  };
+  const bool few = workgroups(d.D == 128 ? 2 : 4) < 512;
 #define ROWS_CASE(DD, GG, NN)                                                                    \
-  if (d.D == DD && d.G == GG)                                                                    \
-    return launch_rows_t<DD, GG, NN>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s);
+  if (d.D == DD && d.G == GG) {                                                                  \
+    if (few) return launch_rows_t<DD, GG, 1>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s); \
+    return launch_rows_t<DD, GG, NN>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s);   \
+  }
   ROWS_CASE(128, 4, 2) ROWS_CASE(128, 1, 2) ROWS_CASE(128, 2, 2) ROWS_CASE(128, 8, 2)
   ROWS_CASE(128, 16, 2)
   ROWS_CASE(64, 4, 4) ROWS_CASE(64, 1, 4) ROWS_CASE(64, 2, 4) ROWS_CASE(64, 8, 4)
