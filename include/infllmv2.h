@@ -197,8 +197,11 @@ INFLLMV2_API size_t infllmv2_prefill_backward_workspace_bytes(const infllmv2_cfg
  *   (tokens x heads of the group) are split over workgroups and added with
  *   fp32 atomics, so their last bits may differ between runs; dk and dv must
  *   therefore be ordinary device memory (hipMalloc), not host or fine-grained
- *   memory. Requires head_dim 128 (else INFLLMV2_UNSUPPORTED); workspace of at
- *   least infllmv2_prefill_backward_workspace_bytes(), no initial contents. */
+ *   memory. head_dim 64 runs the head_dim-128 kernels on copies zero-padded
+ *   to 128 columns (zero columns change no dot product; the softmax scale
+ *   stays the head_dim-64 one), kept in the workspace with the fp32 padded
+ *   gradients. Workspace of at least
+ *   infllmv2_prefill_backward_workspace_bytes(), no initial contents. */
 INFLLMV2_API int infllmv2_sparse_attn_prefill_backward(const infllmv2_cfg* cfg, const void* q,
                                           int32_t n_q, const void* k, const void* v,
                                           int64_t kv_cap, int64_t kv_len, const int32_t* idx,

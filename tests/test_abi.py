@@ -98,7 +98,6 @@ CASES = [
     ("infllmv2_sparse_attn_prefill_backward", {}, (A, 64, A, A, 64, 64, B, A, None, A, A, A, A, 0x100000, 1 << 30, None), -1, "lse is NULL"),
     ("infllmv2_sparse_attn_prefill_backward", {}, (A, 64, A, A, 64, 64, B, A, B, None, A, A, A, 0x100000, 1 << 30, None), -1, "dout is NULL"),
     ("infllmv2_sparse_attn_prefill_backward", {}, (A, 64, A, A, 64, 64, B, A, B, A, A + 4, A, A, 0x100000, 1 << 30, None), -1, "dq"),
-    ("infllmv2_sparse_attn_prefill_backward", dict(head_dim=64), (A, 64, A, A, 64, 64, B, A, B, A, A, A, A, 0x100000, 1 << 30, None), -2, "head_dim 128"),
     ("infllmv2_sparse_attn_prefill_backward", {}, (A, 64, A, A, 64, 64, B, A, B, A, A, A, A, 0x100000, 16, None), -3, "workspace"),
     ("infllmv2_sparse_attn_prefill_backward", {}, (A, 65, A, A, 64, 64, B, A, B, A, A, A, A, 0x100000, 1 << 30, None), -1, "n_q"),
     ("infllmv2_dense_attn", {}, (A, 1, A, A, 64, 0, 1, B, None, None), -1, "kv_len"),
@@ -160,6 +159,12 @@ def test_workspace_bytes(t):
     b1 = t.infllmv2_prefill_backward_workspace_bytes(cfg, 32768, 32768)
     assert b1 > 0 and t.infllmv2_prefill_backward_workspace_bytes(cfg, 1024, 1024) < b1
     assert t.infllmv2_prefill_backward_workspace_bytes(cfg, 0, 10) == 0
+    # head_dim 64 adds zero-padded bf16 copies (q, out, dout, k, v) and fp32 dq, dk, dv at width 128
+    c64 = cfg_ok(t, head_dim=64)
+    b64 = t.infllmv2_prefill_backward_workspace_bytes(c64, 1024, 1024)
+    b128 = t.infllmv2_prefill_backward_workspace_bytes(cfg_ok(t), 1024, 1024)
+    rq, rk = 32 * 1024, 8 * 1024   # query rows (heads x tokens), key rows
+    assert b64 >= b128 + 128 * (3 * 2 * rq + 2 * 2 * rk + 4 * rq + 2 * 4 * rk)
     # variable lengths: room for the larger of K + 1 entries and a dense row below the threshold
     v1 = t.infllmv2_decode_varlen_workspace_bytes(cfg_ok(t, batch=8, top_k=32), 131072)
     assert v1 >= t.infllmv2_decode_workspace_bytes(cfg_ok(t, batch=8, top_k=32), 1, 131072) > 0

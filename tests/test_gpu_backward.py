@@ -39,6 +39,11 @@ CASES = {
                            dense_threshold=600, n_plant=1),
     # the 32K workload's shape rules at 3K tokens and batch 2: K = 16, a 1024-token dense
     # prefix, many segments per block, split blocks and full chunk rings
+    # head_dim 64: the library pads q, k, v, out, dO to 128 zero columns and runs the same kernels
+    "d64_g4": W0.scaled(name="bwd_d64_g4", n_q_heads=8, n_kv_heads=2, head_dim=64, seq_len=1000, top_k=4,
+                        dense_threshold=300, n_plant=2),
+    "d64_g2_b2": W0.scaled(name="bwd_d64_g2", batch=2, n_q_heads=4, n_kv_heads=2, head_dim=64, seq_len=777,
+                           top_k=3, dense_threshold=0, n_plant=2),
     "t3072_k16_b2": W0.scaled(name="bwd_t3k", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, seq_len=3072,
                               top_k=16, dense_threshold=1024, n_plant=8),
 }
@@ -127,13 +132,14 @@ def test_prefill_backward_heavy_keys_split_atomically(case):
     assert rows.max() > 4096, f"no block needs a split (max rows {rows.max()})"
 
 
-@pytest.mark.parametrize("n_q,kv_len,thr", [(500, 1200, 0), (333, 900, 700), (64, 2000, 0)])
-def test_prefill_backward_chunk_after_prefix(n_q, kv_len, thr):
+@pytest.mark.parametrize("n_q,kv_len,thr,D", [(500, 1200, 0, 128), (333, 900, 700, 128), (64, 2000, 0, 128),
+                                               (300, 1100, 0, 64)])
+def test_prefill_backward_chunk_after_prefix(n_q, kv_len, thr, D):
     """A chunk of n_q queries at positions kv_len - n_q .. kv_len - 1 over a longer cache:
     prefix keys get dk, dv from the rows that attend them; rows past kv_len stay untouched."""
-    w = W0.scaled(name="bwd_chunk", n_q_heads=8, n_kv_heads=2, head_dim=128, seq_len=kv_len, top_k=4,
+    w = W0.scaled(name="bwd_chunk", n_q_heads=8, n_kv_heads=2, head_dim=D, seq_len=kv_len, top_k=4,
                   dense_threshold=thr, n_plant=2)
-    note(f"backward chunk n_q{n_q} kv_len{kv_len} thr{thr}")
+    note(f"backward chunk n_q{n_q} kv_len{kv_len} thr{thr} D{D}")
     d = synth.generate(w, seed=9)
     cfg = cfg_of(w)
     cap = d["kv_cap"]

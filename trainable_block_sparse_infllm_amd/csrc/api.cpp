@@ -292,7 +292,7 @@ int infllmv2_sparse_attn_prefill_backward(const infllmv2_cfg* cfg, const void* q
   TRY(check_ptr(fn, dk, "dk", 16));
   TRY(check_ptr(fn, dv, "dv", 16));
   if (!infllmv2::prefill_backward_ok(d, kv_len))
-    return fail(INFLLMV2_UNSUPPORTED, fn, "backward needs head_dim 128 and a tile that fits LDS");
+    return fail(INFLLMV2_UNSUPPORTED, fn, "backward needs head_dim 64 or 128 and a tile that fits LDS");
   TRY(check_ptr(fn, workspace, "workspace", 256));
   const size_t need = infllmv2::prefill_backward_workspace_bytes(d, n_q, kv_len);
   if (workspace_bytes < need) {

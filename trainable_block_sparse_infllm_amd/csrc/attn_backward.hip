@@ -825,12 +825,74 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
 }
 
 // ------------------------------------------------------------------ launch
+// ------------------------------------------------------------------ head_dim 64
+// A head_dim-64 call runs the kernels above on zero-padded copies: appending
+// 64 zero columns to q, k, v, out and dO leaves every dot product (scores, dP,
+// Delta) unchanged, and the first 64 columns of the padded dq, dk, dv are the
+// gradients (the softmax scale stays the head_dim-64 one). The copies live in
+// the workspace: q, out, dO [B*Hq][n_q][128] and k, v [B*Hkv][kv_len][128]
+// bf16; dq [B*Hq][n_q][128] and dk, dv [B*Hkv][kv_len][128] fp32.
+struct PadLayout {
+  size_t off_q, off_out, off_dout, off_k, off_v, off_dq, off_dk, off_dv, off_bwd, total;
+};
+
+PadLayout pad_layout(const Dims& d, int n_q, int64_t kv_len) {
+  PadLayout P{};
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t rq = size_t(d.B) * d.Hq * n_q, rk = size_t(d.B) * d.Hkv * kv_len;
+  size_t o = 0;
+  P.off_q = o;    o = al(o + rq * kD * 2);
+  P.off_out = o;  o = al(o + rq * kD * 2);
+  P.off_dout = o; o = al(o + rq * kD * 2);
+  P.off_k = o;    o = al(o + rk * kD * 2);
+  P.off_v = o;    o = al(o + rk * kD * 2);
+  P.off_dq = o;   o = al(o + rq * kD * 4);
+  P.off_dk = o;   o = al(o + rk * kD * 4);
+  P.off_dv = o;   o = al(o + rk * kD * 4);
+  P.off_bwd = o;
+  Dims d128 = d;
+  d128.D = kD;
+  P.total = o + bwd_layout(d128, n_q, kv_len).total;
+  return P;
+}
+
+// Rows r < nrows of each of nb matrices: bf16 [src_cap][64] -> [dst_cap][128],
+// columns 64..127 zero. One thread per 16-byte piece of a padded row.
+__global__ __launch_bounds__(256) void pad64_kernel(const uint16_t* __restrict__ src,
+                                                    uint16_t* __restrict__ dst, int64_t nb,
+                                                    int64_t nrows, int64_t src_cap,
+                                                    int64_t dst_cap) {
+  const int64_t total = nb * nrows * 16;
+  for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < total;
+       e += int64_t(gridDim.x) * 256) {
+    const int64_t piece = e % 16, r = (e / 16) % nrows, m = e / (16 * nrows);
+    const uint4 val = piece < 8 ? ldg16(src + (m * src_cap + r) * 64 + piece * 8) : uint4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<uint4*>(dst + (m * dst_cap + r) * kD + piece * 8) = val;
+  }
+}
+
+// Rows r < nrows: fp32 [src_cap][128] -> the first 64 columns, [dst_cap][64].
+__global__ __launch_bounds__(256) void unpad64_kernel(const float* __restrict__ src,
+                                                      float* __restrict__ dst, int64_t nb,
+                                                      int64_t nrows, int64_t src_cap,
+                                                      int64_t dst_cap) {
+  const int64_t total = nb * nrows * 16;
+  for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < total;
+       e += int64_t(gridDim.x) * 256) {
+    const int64_t piece = e % 16, r = (e / 16) % nrows, m = e / (16 * nrows);
+    *reinterpret_cast<float4*>(dst + (m * dst_cap + r) * 64 + piece * 4) =
+        *reinterpret_cast<const float4*>(src + (m * src_cap + r) * kD + piece * 4);
+  }
+}
+
 size_t prefill_backward_workspace_bytes(const Dims& d, int n_q, int64_t kv_len) {
-  return bwd_layout(d, n_q, kv_len).total;
+  return d.D == 64 ? pad_layout(d, n_q, kv_len).total : bwd_layout(d, n_q, kv_len).total;
 }
 
 bool prefill_backward_ok(const Dims& d, int64_t kv_len) {
-  return d.D == kD && prefill128_stages(d, 0, kv_len) > 0;
+  Dims d128 = d;
+  d128.D = kD;
+  return (d.D == kD || d.D == 64) && prefill128_stages(d128, 0, kv_len) > 0;
 }
 
 template <int G>
@@ -903,12 +965,56 @@ static hipError_t launch_bwd_t(const Dims& d, const uint16_t* q, int n_q, const 
   return hipGetLastError();
 }
 
+static hipError_t launch_bwd_any(const Dims& d, const uint16_t* q, int n_q, const uint16_t* k,
+                                 const uint16_t* v, int64_t kv_cap, int64_t kv_len,
+                                 const int32_t* idx, const uint16_t* out, const float* lse,
+                                 const uint16_t* dout, float* dq, float* dk, float* dv, void* ws,
+                                 hipStream_t s);
+
 hipError_t launch_prefill_backward(const Dims& d, const uint16_t* q, int n_q, const uint16_t* k,
                                    const uint16_t* v, int64_t kv_cap, int64_t kv_len,
                                    const int32_t* idx, const uint16_t* out, const float* lse,
                                    const uint16_t* dout, float* dq, float* dk, float* dv, void* ws,
                                    size_t ws_bytes, hipStream_t s) {
-  if (ws_bytes < bwd_layout(d, n_q, kv_len).total) return hipErrorInvalidValue;
+  if (ws_bytes < prefill_backward_workspace_bytes(d, n_q, kv_len)) return hipErrorInvalidValue;
+  if (d.D == kD)
+    return launch_bwd_any(d, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, dout, dq, dk, dv, ws, s);
+  if (d.D != 64) return hipErrorInvalidValue;
+  const PadLayout P = pad_layout(d, n_q, kv_len);
+  char* w8 = static_cast<char*>(ws);
+  uint16_t* qp = reinterpret_cast<uint16_t*>(w8 + P.off_q);
+  uint16_t* op = reinterpret_cast<uint16_t*>(w8 + P.off_out);
+  uint16_t* gp = reinterpret_cast<uint16_t*>(w8 + P.off_dout);
+  uint16_t* kp = reinterpret_cast<uint16_t*>(w8 + P.off_k);
+  uint16_t* vp = reinterpret_cast<uint16_t*>(w8 + P.off_v);
+  float* dqp = reinterpret_cast<float*>(w8 + P.off_dq);
+  float* dkp = reinterpret_cast<float*>(w8 + P.off_dk);
+  float* dvp = reinterpret_cast<float*>(w8 + P.off_dv);
+  const int64_t nbq = int64_t(d.B) * d.Hq, nbk = int64_t(d.B) * d.Hkv;
+  auto grid_of = [](int64_t pieces) { return dim3(unsigned(std::min<int64_t>(4096, (pieces + 255) / 256))); };
+  pad64_kernel<<<grid_of(nbq * n_q * 16), 256, 0, s>>>(q, qp, nbq, n_q, n_q, n_q);
+  pad64_kernel<<<grid_of(nbq * n_q * 16), 256, 0, s>>>(out, op, nbq, n_q, n_q, n_q);
+  pad64_kernel<<<grid_of(nbq * n_q * 16), 256, 0, s>>>(dout, gp, nbq, n_q, n_q, n_q);
+  pad64_kernel<<<grid_of(nbk * kv_len * 16), 256, 0, s>>>(k, kp, nbk, kv_len, kv_cap, kv_len);
+  pad64_kernel<<<grid_of(nbk * kv_len * 16), 256, 0, s>>>(v, vp, nbk, kv_len, kv_cap, kv_len);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  Dims d128 = d;
+  d128.D = kD;
+  e = launch_bwd_any(d128, qp, n_q, kp, vp, kv_len, kv_len, idx, op, lse, gp, dqp, dkp, dvp,
+                     w8 + P.off_bwd, s);
+  if (e != hipSuccess) return e;
+  unpad64_kernel<<<grid_of(nbq * n_q * 16), 256, 0, s>>>(dqp, dq, nbq, n_q, n_q, n_q);
+  unpad64_kernel<<<grid_of(nbk * kv_len * 16), 256, 0, s>>>(dkp, dk, nbk, kv_len, kv_len, kv_cap);
+  unpad64_kernel<<<grid_of(nbk * kv_len * 16), 256, 0, s>>>(dvp, dv, nbk, kv_len, kv_len, kv_cap);
+  return hipGetLastError();
+}
+
+static hipError_t launch_bwd_any(const Dims& d, const uint16_t* q, int n_q, const uint16_t* k,
+                                 const uint16_t* v, int64_t kv_cap, int64_t kv_len,
+                                 const int32_t* idx, const uint16_t* out, const float* lse,
+                                 const uint16_t* dout, float* dq, float* dk, float* dv, void* ws,
+                                 hipStream_t s) {
   switch (d.G) {
 #define BWD_CASE(GG)                                                                              \
   case GG:                                                                                        \
