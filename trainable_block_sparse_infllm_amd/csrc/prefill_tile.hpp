@@ -165,17 +165,30 @@ __device__ __forceinline__ int build_union(const int32_t* __restrict__ idx, int6
   for (int i = tid; i < nwords; i += NT)
     bitmap[i] = uint32_t(range_bits(rlo - int64_t(i) * 32, own_hi + 1 - int64_t(i) * 32, 32));
   __syncthreads();
-  for (int e = tid; e < ntok * K; e += NT) {
-    const int t = e / K;
-    int j = -1;
-    if (t >= dend) {
-      j = idx[(bg * n_q + tok0 + t) * K + e % K];
-      if (j >= 0 && j < (base + t) / kBlock)
-        atomicOr(&bitmap[j >> 5], 1u << (j & 31));
-      else
-        j = -1;
+  // four index loads per thread are issued before any of them is used, so
+  // their latencies overlap
+  const int nsel = ntok * K;
+  for (int e0 = tid; e0 < nsel; e0 += 4 * NT) {
+    int jv[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int e = e0 + x * NT;
+      const int t = e / K;
+      jv[x] = (e < nsel && t >= dend) ? idx[(bg * n_q + tok0 + t) * K + e % K] : -1;
     }
-    jsel[e] = j;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int e = e0 + x * NT;
+      if (e < nsel) {
+        const int t = e / K;
+        int j = jv[x];
+        if (j >= 0 && j < (base + t) / kBlock)
+          atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+        else
+          j = -1;
+        jsel[e] = j;
+      }
+    }
   }
   __syncthreads();
   // exclusive prefix of the words' popcounts (thread t owns words t*WPT ..),
