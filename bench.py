@@ -619,7 +619,7 @@ def main():
         print(json.dumps(t, indent=1))
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for {args.gpus})",
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
 

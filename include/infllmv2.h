@@ -77,7 +77,7 @@ extern "C" {
 
 #define INFLLMV2_OK 0
 #define INFLLMV2_INVALID_ARGUMENT (-1)   /* null pointer, bad shape, misaligned pointer */
-#define INFLLMV2_UNSUPPORTED (-2)        /* valid request this build does not run (device, shape) */
+#define INFLLMV2_UNSUPPORTED (-2)        /* valid request the library does not run (device, shape) */
 #define INFLLMV2_WORKSPACE_TOO_SMALL (-3)
 #define INFLLMV2_HIP_ERROR (-4)          /* a HIP runtime call or kernel launch failed */
 
