@@ -187,6 +187,47 @@ def _pmc_per_kernel(db: str, counter: str) -> dict:
     return agg
 
 
+def summarize_counters(db: str, trace_db: str, title: str, command: str) -> str:
+    """Markdown table of every counter in a rocprofv3 --pmc database, averaged per kernel over its
+    dispatches. With MfmaFlopsBF16 and a --kernel-trace database of the same command, adds the
+    issued bf16 MFMA rate (issued MFMA flops per dispatch over the kernel's average duration)."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    names = [r[0] for r in con.execute("select distinct counter_name from counters_collection order by 1")]
+    per = {n: _pmc_per_kernel(db, n) for n in names}
+    dur = {}
+    if trace_db:
+        tcon = sqlite3.connect(trace_db)
+        for n, a in tcon.execute("select name, avg(duration) from kernels group by name"):
+            dur[_short(n)] = float(a)
+    kernels = sorted({k for d in per.values() for k in d},
+                     key=lambda k: -max((sum(v) / len(v) for d in per.values() for kk, v in d.items() if kk == k),
+                                        default=0.0))
+    head = ["kernel", "dispatches"] + names
+    if "MfmaFlopsBF16" in per and dur:
+        head += ["avg us (trace)", "issued bf16 MFMA TFLOP/s", "of 2.5 PF"]
+    out = [f"# {title}", "", "Commands (from the repository root, one MI355X):", "", "```", command, "```", "",
+           "| " + " | ".join(head) + " |", "|" + "---|" * len(head)]
+    for k in kernels:
+        if all(sum(per[n].get(k, [0.0])) == 0 for n in names):
+            continue                      # no counter activity (fills, copies)
+        n_disp = max(len(d.get(k, [])) for d in per.values())
+        row = [f"`{k}`", str(n_disp)]
+        for n in names:
+            v = per[n].get(k)
+            row.append(f"{sum(v) / len(v):.4g}" if v else "")
+        if len(head) > len(names) + 2:
+            fl = per["MfmaFlopsBF16"].get(k)
+            us = dur.get(k)
+            if fl and us:
+                rate = sum(fl) / len(fl) / (us * 1e-9) / 1e12
+                row += [f"{us / 1e3:.1f}", f"{rate:.0f}", f"{rate / 2500:.1%}"]
+            else:
+                row += ["", "", ""]
+        out.append("| " + " | ".join(row) + " |")
+    return "\n".join(out) + "\n"
+
+
 def summarize_pmc(fetch_db: str, write_db: str, copy_bytes: int) -> dict:
     """Per-launch HBM traffic of each entry point from FETCH_SIZE / WRITE_SIZE runs (KiB per
     dispatch). Each counter is scaled by what it reads for the largest plain copies in the same run
@@ -600,11 +641,18 @@ def main():
     ap.add_argument("--command", default="")
     ap.add_argument("--traffic-md", action="store_true",
                     help="print profiles/traffic.json as a markdown table and exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("PMC_DB", "TRACE_DB"),
+                    help="print a markdown table of the counters in a --pmc database (durations from a "
+                         "--kernel-trace database of the same command) and exit")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="write profiles/traffic.json from FETCH_SIZE and WRITE_SIZE runs of this bench and exit")
     args = ap.parse_args()
     if args.summarize_trace:
         sys.stdout.write(summarize_trace(args.summarize_trace, args.title, args.command))
+        return
+    if args.summarize_counters:
+        sys.stdout.write(summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.title,
+                                            args.command))
         return
     if args.traffic_md:
         with open(TRAFFIC_FILE) as fh:
