@@ -33,3 +33,29 @@ def test_gpus_above_one_exits_with_message(capsys):
     finally:
         sys.argv = old
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_counter_summary_rates_from_counter_and_trace_databases(tmp_path):
+    """Issued MFMA rate = flops per dispatch over the kernel's average traced duration; kernels
+    without counter activity are left out."""
+    import sqlite3
+    pmc, trace = tmp_path / "pmc.db", tmp_path / "trace.db"
+    con = sqlite3.connect(pmc)
+    con.execute("create table counters_collection (kernel_name text, counter_name text, value real)")
+    rows = [("void infllmv2::attn_k<4>(int)", "MfmaFlopsBF16", 2.0e12), ("void infllmv2::attn_k<4>(int)",
+            "MfmaFlopsBF16", 1.0e12), ("void infllmv2::attn_k<4>(int)", "MfmaUtil", 40.0),
+            ("void infllmv2::attn_k<4>(int)", "MfmaUtil", 20.0), ("fill_k(int)", "MfmaFlopsBF16", 0.0),
+            ("fill_k(int)", "MfmaUtil", 0.0)]
+    con.executemany("insert into counters_collection values (?, ?, ?)", rows)
+    con.commit()
+    con = sqlite3.connect(trace)
+    con.execute("create table kernels (name text, duration real)")
+    con.executemany("insert into kernels values (?, ?)", [("void infllmv2::attn_k<4>(int)", 1.0e6)] * 3)
+    con.commit()
+    md = bench.summarize_counters(str(pmc), str(trace), "t", "cmd")
+    line = next(x for x in md.splitlines() if "attn_k<4>" in x)
+    cells = [c.strip() for c in line.strip("|").split("|")]
+    # dispatches 2; MfmaFlopsBF16 1.5e12 per dispatch; MfmaUtil 30; 1 ms -> 1500 TFLOP/s = 60% of 2.5 PF
+    assert cells[1] == "2" and cells[2] == "1.5e+12" and cells[3] == "30"
+    assert cells[4] == "1000.0" and cells[5] == "1500" and cells[6] == "60.0%"
+    assert "fill_k" not in md
