@@ -289,8 +289,8 @@ INFLLMV2_API int infllmv2_sparse_attn_decode_varlen(const infllmv2_cfg* cfg, con
  * kernels). Serves both a draft prefill (n_q = prompt length) and its decode
  * steps (n_q = 1 with the new token's K/V already in the cache). Layouts as
  * infllmv2_dense_attn; top_k and dense_threshold are ignored; window >= 1
- * (values above kv_len act as kv_len, i.e. dense causal). Requires head_dim
- * 128 (else INFLLMV2_UNSUPPORTED). */
+ * (values above kv_len act as kv_len, i.e. dense causal). head_dim 64 or
+ * 128. */
 INFLLMV2_API int infllmv2_sliding_window_attn(const infllmv2_cfg* cfg, const void* q, int32_t n_q,
                                  const void* k, const void* v, int64_t kv_cap, int64_t kv_len,
                                  int64_t window, void* out, float* lse, void* stream);

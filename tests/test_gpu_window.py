@@ -3,8 +3,8 @@
 Row i sits at position p = kv_len - n_q + i and attends keys max(0, p - W + 1)
 .. p. Cases cover windows inside one block, windows not a multiple of the
 block size, a window of one key, windows wider than the prefix (dense
-causal), chunked calls (n_q < kv_len), single-token decode steps and every
-GQA group size. Tolerances as for the other attention outputs: bf16 out
+causal), chunked calls (n_q < kv_len), single-token decode steps, every
+GQA group size, and head_dim 64 (served by the rows kernel). Tolerances as for the other attention outputs: bf16 out
 max-abs <= 2e-2, mean-abs <= 2e-3; lse within LSE_ABS.
 """
 import numpy as np
@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 P0 = synth.WORKLOADS["prefill_32k"]
 
-# (Hq, Hkv, B, n_q, kv_len, window)
+# (Hq, Hkv, B, n_q, kv_len, window[, head_dim])
 CASES = [
     (8, 2, 1, 1100, 1100, 300),      # prefill, window spans ~5 blocks, not a multiple of 64
     (8, 2, 2, 700, 700, 64),         # exactly one block wide
@@ -33,15 +33,22 @@ CASES = [
     (2, 2, 1, 600, 600, 130),        # G = 1
     (16, 1, 1, 300, 300, 90),        # G = 16
     (16, 2, 1, 260, 900, 33),        # G = 8, chunk
+    # head_dim 64 (the rows kernel's window mode)
+    (2, 1, 1, 1100, 1100, 300, 64),  # G = 2, prefill
+    (8, 2, 2, 97, 1500, 200, 64),    # chunk of a longer prompt
+    (8, 2, 1, 1, 5000, 1024, 64),    # draft decode step
+    (4, 1, 1, 400, 400, 1, 64),      # only the own key
+    (8, 2, 1, 333, 333, 5000, 64),   # wider than the prefix: dense causal
 ]
 
 
 @pytest.mark.parametrize("dims", CASES, ids=lambda c: "x".join(map(str, c)))
 def test_sliding_window_matches_oracle(dims):
-    Hq, Hkv, B, n_q, kv_len, W = dims
-    w = P0.scaled(name="window", batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=128, seq_len=kv_len,
+    Hq, Hkv, B, n_q, kv_len, W = dims[:6]
+    D = dims[6] if len(dims) > 6 else 128
+    w = P0.scaled(name="window", batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, seq_len=kv_len,
                   n_plant=0, dense_threshold=0)
-    note(f"window case B{B} Hq{Hq}/Hkv{Hkv} n_q{n_q} kv_len{kv_len} W{W}")
+    note(f"window case B{B} Hq{Hq}/Hkv{Hkv} n_q{n_q} kv_len{kv_len} W{W} D{D}")
     d = synth.generate(w, seed=11)
     qn = np.ascontiguousarray(d["q"][:, :, kv_len - n_q:])
     ref = orc.window_forward(qn, d["k"], d["v"], kv_len=kv_len, n_kv_heads=Hkv, window=W)

@@ -486,15 +486,13 @@ int infllmv2_sliding_window_attn(const infllmv2_cfg* cfg, const void* q, int32_t
   TRY(check_cfg(fn, cfg, false, &d));
   TRY(check_attn(fn, d, q, n_q, k, v, kv_cap, kv_len, out, lse));
   if (window < 1) return fail(INFLLMV2_INVALID_ARGUMENT, fn, "window must be >= 1");
-  if (infllmv2::prefill128_stages(d, 3, kv_len) == 0)
-    return fail(INFLLMV2_UNSUPPORTED, fn, "sliding-window attention needs head_dim 128");
   TRY(check_device(fn));
-  LAUNCH(fn, infllmv2::launch_prefill128(d, 3, static_cast<const uint16_t*>(q), n_q,
-                                         static_cast<const uint16_t*>(k),
-                                         static_cast<const uint16_t*>(v), kv_cap, kv_len, nullptr,
-                                         static_cast<uint16_t*>(out), lse,
-                                         static_cast<hipStream_t>(stream),
-                                         std::min<int64_t>(window, kv_len)));
+  LAUNCH(fn, infllmv2::launch_attn_rows(d, 3, static_cast<const uint16_t*>(q), n_q,
+                                        static_cast<const uint16_t*>(k),
+                                        static_cast<const uint16_t*>(v), kv_cap, kv_len, nullptr,
+                                        static_cast<uint16_t*>(out), lse,
+                                        static_cast<hipStream_t>(stream),
+                                        std::min<int64_t>(window, kv_len)));
   return INFLLMV2_OK;
 }
 

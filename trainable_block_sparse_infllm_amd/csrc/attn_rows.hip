@@ -7,7 +7,8 @@
 // Row (b, h, i) sits at position p = kv_len - n_q + i and attends
 //   mode 0 (sparse): the 64 keys of every block in idx[b][h/G][i] plus its own
 //           block up to p; all keys 0..p if p + 1 < dense_threshold;
-//   mode 1 (dense causal): keys 0..p;      mode 2 (dense): keys 0..kv_len-1.
+//   mode 1 (dense causal): keys 0..p;      mode 2 (dense): keys 0..kv_len-1;
+//   mode 3 (sliding window): keys max(0, p - window + 1)..p.
 //
 // Layout of the work: a workgroup (4 wavefronts) owns 4*NST*16/G consecutive
 // tokens of one (b, g); each wavefront owns NST sub-tiles of 16 MFMA rows =
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ out, float* __restrict__ lse, int Hq,
     int Hkv, int n_q, int64_t kv_cap, int64_t kv_len, int K, int dense_thr, int mode,
-    float scale_log2, int ntile) {
+    int64_t window, float scale_log2, int ntile) {
   using S = AttnSmem<D>;
   constexpr int KS = D / 32;        // k-steps over D for S
   constexpr int DT = D / 16;        // 16-wide d tiles of O
@@ -160,11 +161,13 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(
   const int64_t last_blk = (kv_len - 1) / kBlock;
   const int my_own = tok_ok ? int(mode == 2 ? last_blk : my_p / kBlock) : -1;
   const bool my_dense = mode != 0 || (dense_thr > 0 && my_p + 1 < dense_thr);
+  // mode 3: the block holding the token's first visible key
+  const int my_lo = mode == 3 && my_p - window + 1 > 0 ? int((my_p - window + 1) / kBlock) : 0;
   const int32_t* my_idx = s_idx + (w * TPW + l) * K;
   int my_ptr = 0;
   auto next_needed = [&](int cur) -> int {
     if (!tok_ok || cur >= my_own) return kEnd;
-    if (my_dense) return cur + 1;
+    if (my_dense) return max(cur + 1, my_lo);
     while (my_ptr < K && my_idx[my_ptr] >= 0 && my_idx[my_ptr] <= cur) ++my_ptr;
     if (my_ptr < K && my_idx[my_ptr] >= 0 && my_idx[my_ptr] < my_own) return my_idx[my_ptr];
     return my_own;                       // own block last (entries past it are ignored)
@@ -246,13 +249,14 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(
     for (int s = 0; s < NST; ++s) {
       if (!sub_on[s]) continue;
       const int64_t lim = mode == 2 ? kv_len - 1 : row_p[s];   // last visible key
+      const int64_t lo = mode == 3 ? row_p[s] - window + 1 : 0;  // first visible key
       float mb = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int64_t key = int64_t(j_cur) * kBlock + kt * 16 + kg * 4 + i;
-          const float x = (row_on[s] && key <= lim) ? sacc[s][kt][i] * scale_log2 : -INFINITY;
+          const float x = (row_on[s] && key <= lim && key >= lo) ? sacc[s][kt][i] * scale_log2 : -INFINITY;
           sacc[s][kt][i] = x;
           mb = fmaxf(mb, x);
         }
@@ -335,7 +339,7 @@ template <int D, int G, int NST>
 static hipError_t launch_rows_t(const Dims& d, int mode, const uint16_t* q, int n_q,
                                 const uint16_t* k, const uint16_t* v, int64_t kv_cap,
                                 int64_t kv_len, const int32_t* idx, uint16_t* out, float* lse,
-                                hipStream_t s) {
+                                hipStream_t s, int64_t window) {
   using S = AttnSmem<D>;
   constexpr int TQ = 4 * NST * (16 / G);
   const int ntile = (n_q + TQ - 1) / TQ;
@@ -349,15 +353,15 @@ static hipError_t launch_rows_t(const Dims& d, int mode, const uint16_t* q, int 
   if (attr != hipSuccess) return attr;
   const dim3 grid(unsigned(int64_t(d.B) * d.Hkv * ntile));
   kern<<<grid, 256, lds, s>>>(q, k, v, idx, out, lse, d.Hq, d.Hkv, n_q, kv_cap, kv_len, d.K,
-                              d.dense_thr, mode, d.scale * 1.4426950408889634f, ntile);
+                              d.dense_thr, mode, window, d.scale * 1.4426950408889634f, ntile);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_rows(const Dims& d, int mode, const uint16_t* q, int n_q, const uint16_t* k,
                             const uint16_t* v, int64_t kv_cap, int64_t kv_len, const int32_t* idx,
-                            uint16_t* out, float* lse, hipStream_t s) {
+                            uint16_t* out, float* lse, hipStream_t s, int64_t window) {
   if (prefill128_stages(d, mode, kv_len) > 0)
-    return launch_prefill128(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s);
+    return launch_prefill128(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s, window);
   // Sub-tiles per wavefront: the full count when the grid fills the chip,
   // one when it would leave most CUs idle (a short or single-group call),
   // which gives four times as many workgroups.
@@ -368,8 +372,8 @@ hipError_t launch_attn_rows(const Dims& d, int mode, const uint16_t* q, int n_q,
   const bool few = workgroups(d.D == 128 ? 2 : 4) < 512;
 #define ROWS_CASE(DD, GG, NN)                                                                    \
   if (d.D == DD && d.G == GG) {                                                                  \
-    if (few) return launch_rows_t<DD, GG, 1>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s); \
-    return launch_rows_t<DD, GG, NN>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s);   \
+    if (few) return launch_rows_t<DD, GG, 1>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s, window); \
+    return launch_rows_t<DD, GG, NN>(d, mode, q, n_q, k, v, kv_cap, kv_len, idx, out, lse, s, window); \
   }
   ROWS_CASE(128, 4, 2) ROWS_CASE(128, 1, 2) ROWS_CASE(128, 2, 2) ROWS_CASE(128, 8, 2)
   ROWS_CASE(128, 16, 2)

@@ -43,10 +43,11 @@ hipError_t launch_topk_from_scores(const Dims& d, const float* scores, int n_q, 
 hipError_t launch_topk_fused(const Dims& d, const uint16_t* q, const uint16_t* kbar, int n_q,
                              int64_t q_pos0, int is_tree, int64_t nblk, int32_t* idx, hipStream_t s);
 
-// mode: 0 sparse (idx + dense threshold), 1 dense causal, 2 dense without mask.
+// mode: 0 sparse (idx + dense threshold), 1 dense causal, 2 dense without mask,
+// 3 sliding window (keys max(0, p - window + 1)..p).
 hipError_t launch_attn_rows(const Dims& d, int mode, const uint16_t* q, int n_q, const uint16_t* k,
                             const uint16_t* v, int64_t kv_cap, int64_t kv_len, const int32_t* idx,
-                            uint16_t* out, float* lse, hipStream_t s);
+                            uint16_t* out, float* lse, hipStream_t s, int64_t window = 0);
 
 // head_dim 128 fused scoring + top-K for prefill chunks (at most 512
 // candidate blocks); topk_prefill128_ok() says whether it takes the shape.
@@ -58,7 +59,7 @@ hipError_t launch_topk_prefill128(const Dims& d, const uint16_t* q, const uint16
 // head_dim 128 prefill / dense / sliding-window attention over a per-tile
 // block union staged through an LDS ring (mode 3: keys max(0, p-window+1)..p).
 // prefill128_stages() returns the ring depth for the shape, or 0 if it does
-// not fit (then launch_attn_rows is used; it has no mode 3).
+// not fit (then launch_attn_rows runs the rows kernel).
 int prefill128_stages(const Dims& d, int mode, int64_t kv_len);
 hipError_t launch_prefill128(const Dims& d, int mode, const uint16_t* q, int n_q,
                              const uint16_t* k, const uint16_t* v, int64_t kv_cap, int64_t kv_len,
