@@ -36,15 +36,16 @@ def _kbar_host(kbar):
     return kbar_rows(kbar)
 
 
+@pytest.mark.parametrize("D", [128, 64], ids=["d128", "d64"])
 @pytest.mark.parametrize("varlen", [False, True], ids=["same_len", "varlen"])
 @pytest.mark.parametrize("n_new", [1, 5, 64, 150])
-def test_append_writes_rows_and_pools_completed_blocks(varlen, n_new):
+def test_append_writes_rows_and_pools_completed_blocks(varlen, n_new, D):
     B, L = 3, 1400
-    w = _workload(B, L)
+    w = _workload(B, L, head_dim=D)
     d = synth.generate(w, seed=5)
     cap = d["kv_cap"]
     lens0 = [130, 63, 1000] if varlen else [700] * B
-    note(f"append case n_new{n_new} lens{lens0}")
+    note(f"append case D{D} n_new{n_new} lens{lens0}")
     kf, vf = d["k"], d["v"]                                   # the full sequences
     kc = np.full_like(kf, SENTINEL)
     vc = np.full_like(vf, SENTINEL)
@@ -97,13 +98,14 @@ def _open_step_gaps(w, q, kf, lens, seed):
     return q
 
 
+@pytest.mark.parametrize("D", [128, 64], ids=["d128", "d64"])
 @pytest.mark.parametrize("varlen", [False, True], ids=["same_len", "varlen"])
-def test_decode_loop_append_then_attend(varlen):
+def test_decode_loop_append_then_attend(varlen, D):
     """Three steps of append(1 token) -> scores -> select -> attend. The lengths cross
     block boundaries (a block completed by one step's append is a candidate in the
     next) and one sequence stays below the dense threshold."""
     B, steps = 4, 3
-    w = _workload(B, 3300)
+    w = _workload(B, 3300, head_dim=D)
     d = synth.generate(w, seed=6)
     kf, vf, cap = d["k"], d["v"], d["kv_cap"]
     lens0 = [127, 3000, 900, 64 * 40 - 1] if varlen else [2047] * B
