@@ -164,3 +164,67 @@ def test_prefill_backward_chunk_after_prefix(n_q, kv_len, thr, D):
     bad += _close("dv", g["dv"].cpu().numpy()[:, :, :kv_len], dv[:, :, :kv_len], 2e-3)
     assert not bad, bad
     assert (g["dk"][:, :, kv_len:] == 0).all() and (g["dv"][:, :, kv_len:] == 0).all()
+
+
+def test_prefill_backward_32k_full_size_sampled():
+    """The benchmark's backward workload (32K tokens, 32/8 heads, K = 16, dense below 1024) in
+    its launch configuration. dq is checked on sampled rows: a row's gradient depends only on its
+    own key set, so the oracle computes it from those rows alone. dk and dv are checked on
+    sampled key blocks of two groups: the oracle runs every row that attends the block (from the
+    GPU forward's selection), which makes its dk, dv of that block exact."""
+    w = synth.WORKLOADS["prefill_32k"]
+    T, G, K, thr = w.seq_len, w.group, w.top_k, w.dense_threshold
+    d = synth.generate(w, seed=0, threads=16)
+    cfg = cfg_of(w)
+    q, k, v = dev_bf16(d["q"]), dev_bf16(d["k"]), dev_bf16(d["v"])
+    fw = ops.sparse_prefill(cfg, q, k, v)
+    rng = np.random.default_rng(21)
+    dout_h = synth.to_bf16_bits(rng.standard_normal(d["q"].shape).astype(np.float32)).reshape(d["q"].shape)
+    g_res = ops.sparse_prefill_backward(cfg, q, k, v, fw["idx"], fw["out"], fw["lse"], dev_bf16(dout_h),
+                                        kv_len=T)
+    torch.cuda.synchronize()
+    idx = fw["idx"].cpu().numpy()
+    dq_gpu = g_res["dq"].cpu().numpy()
+
+    # dq: sampled tokens (block edges, the dense threshold, the last token), every head
+    toks = np.array(sorted(set([0, 63, 64, 1022, 1023, 1024, 4095, 4096, 20000, T - 1]
+                               + rng.integers(0, T, 22).tolist())), dtype=np.int64)
+    note(f"backward 32K: dq on {len(toks)} tokens x {w.n_q_heads} heads")
+    dq_ref, _, _ = orc.attend_backward(orc.MODE_SPARSE, np.ascontiguousarray(d["q"][:, :, toks]), d["k"], d["v"],
+                                       toks, T, w.n_kv_heads, np.ascontiguousarray(dout_h[:, :, toks]),
+                                       idx=np.ascontiguousarray(idx[:, :, toks]), dense_threshold=thr)
+    bad = _close("dq (sampled rows)", dq_gpu[:, :, toks], dq_ref, 1e-2)
+
+    # dk, dv: per group, the last block (attended by its own tokens only), the sparse-region
+    # block attended by the most tokens up to 1500 (selected by many rows), and the last block
+    # of the dense prefix (attended by every dense row past it and by selecting rows) when it
+    # has at most 3000 attending tokens
+    own = np.arange(T) // 64
+    for g in (0, 5):
+        att = np.zeros((T, T // 64), dtype=bool)
+        att[np.arange(T), own] = True
+        dense = np.arange(T) + 1 < thr
+        att[dense] = np.arange(T // 64)[None, :] <= own[dense, None]
+        sel = idx[0, g]
+        ok = (sel >= 0) & (sel < own[:, None])
+        tt, kk = np.nonzero(ok)
+        att[tt, sel[tt, kk]] = True
+        counts = att.sum(axis=0)
+        sparse_blocks = np.arange(thr // 64 + 1, T // 64 - 1)
+        modest = sparse_blocks[counts[sparse_blocks] <= 1500]
+        picks = [T // 64 - 1, int(modest[np.argmax(counts[modest])])]
+        if counts[thr // 64 - 1] <= 3000:
+            picks.append(thr // 64 - 1)
+        for j in picks:
+            rows_t = np.nonzero(att[:, j])[0].astype(np.int64)
+            note(f"backward 32K: group {g} block {j}: {len(rows_t)} attending tokens")
+            hs = slice(g * G, (g + 1) * G)
+            _, dk_ref, dv_ref = orc.attend_backward(
+                orc.MODE_SPARSE, np.ascontiguousarray(d["q"][:, hs][:, :, rows_t]),
+                np.ascontiguousarray(d["k"][:, g:g + 1]), np.ascontiguousarray(d["v"][:, g:g + 1]), rows_t, T, 1,
+                np.ascontiguousarray(dout_h[:, hs][:, :, rows_t]),
+                idx=np.ascontiguousarray(idx[:, g:g + 1][:, :, rows_t]), dense_threshold=thr)
+            keys = slice(j * 64, (j + 1) * 64)
+            bad += _close(f"dk g{g} b{j}", g_res["dk"][0, g, keys].cpu().numpy(), dk_ref[0, 0, keys], 2e-3)
+            bad += _close(f"dv g{g} b{j}", g_res["dv"][0, g, keys].cpu().numpy(), dv_ref[0, 0, keys], 2e-3)
+    assert not bad, bad
