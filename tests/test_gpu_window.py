@@ -71,3 +71,24 @@ def test_sliding_window_wider_than_prefix_equals_dense_causal():
     torch.cuda.synchronize()
     # the same kernel walks the same blocks in the same order: identical bits
     assert torch.equal(a["out"], b["out"]) and torch.equal(a["lse"], b["lse"])
+
+
+def test_sliding_window_32k_full_size_sampled_rows():
+    """The benchmark's window leg (the 32K prompt's shapes, W = 2048) in its launch
+    configuration; the oracle computes sampled rows of every head: the first rows (window
+    wider than the prefix), rows at block edges, the window's first full row and the last."""
+    w = P0
+    W = 2048
+    T = w.seq_len
+    d = synth.generate(w, seed=0, threads=16)
+    res = ops.sliding_window(cfg_of(w), dev_bf16(d["q"]), dev_bf16(d["k"]), dev_bf16(d["v"]), T, W)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(31)
+    toks = sorted(set([0, 1, 63, 64, W - 2, W - 1, W, W + 1, 4095, 4096, T - 1] + rng.integers(0, T, 12).tolist()))
+    rows = np.array([(0, h, t) for h in range(w.n_q_heads) for t in toks], dtype=np.int32)
+    note(f"window 32K full size: {len(rows)} sampled rows")
+    ref = orc.window_forward(d["q"], d["k"], d["v"], kv_len=T, n_kv_heads=w.n_kv_heads, window=W, rows=rows)
+    r = ref["rows"]
+    assert set(ref["nkeys"].tolist()) <= set(range(1, W + 1))
+    assert_close_rows(host_f64(res["out"])[r[:, 0], r[:, 1], r[:, 2]], ref["out"], "window 32K out")
+    assert np.abs(host_f64(res["lse"])[r[:, 0], r[:, 1], r[:, 2]] - ref["lse"]).max() <= LSE_ABS
