@@ -112,3 +112,31 @@ def test_lse_decode_step_end_to_end():
     assert_close_rows(go, out_o, "lse decode out")
     gl = host_f64(res["lse"])[hrows[:, 0], hrows[:, 1], hrows[:, 2]]
     assert np.abs(gl - lse_o).max() <= LSE_ABS
+
+
+def test_lse_decode_128k_batch8_full_size():
+    """The benchmark's LSE-selection leg (128K, batch 8, K = 32) in its launch configuration:
+    selection exact and outputs within tolerance for every (sequence, head)."""
+    w = synth.WORKLOADS["decode_128k_b8"]
+    d = synth.generate(w, seed=6, threads=16)
+    L = d["kv_len"]
+    pos = np.array([L - 1])
+    kbar_o, _, _ = open_gaps(d, orc, pos=pos, score_fn=orc.scores_lse, relative=True)
+    rows = orc.all_group_rows(w.batch, w.n_kv_heads, 1)
+    R, Cn = orc.scores_lse(d["q"], kbar_o, pos, rows, w.n_kv_heads)
+    idx_o = orc.select(R, Cn, w.top_k).reshape(w.batch, w.n_kv_heads, 1, w.top_k)
+    G = w.group
+    hrows = np.array([(b, g * G + hh, 0) for (b, g, _) in rows for hh in range(G)], np.int32)
+    note(f"lse 128K full size: {len(hrows)} rows")
+    out_o, lse_o, _ = orc.attend(orc.MODE_SPARSE, d["q"], d["k"], d["v"], pos, L, hrows, w.n_kv_heads,
+                                 idx=idx_o, dense_threshold=w.dense_threshold)
+    cfg = cfg_of(w)
+    k, v = dev_bf16(d["k"]), dev_bf16(d["v"])
+    kbar = ops.pool_kernels(cfg, k, d["kv_cap"], L)
+    res = ops.decode_step_lse(cfg, dev_bf16(d["q"]), k, v, kbar, L)
+    torch.cuda.synchronize()
+    assert np.array_equal(res["idx"].cpu().numpy(), idx_o)
+    go = host_f64(res["out"])[hrows[:, 0], hrows[:, 1], hrows[:, 2]]
+    assert_close_rows(go, out_o, "lse decode 128K out")
+    gl = host_f64(res["lse"])[hrows[:, 0], hrows[:, 1], hrows[:, 2]]
+    assert np.abs(gl - lse_o).max() <= LSE_ABS
