@@ -626,7 +626,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--rotations", type=int, default=4)
+    # independent K, V and k-bar sets cycled through by the decode graph: ten steps' selected
+    # K/V (10 x 69 MB) and k-bar (10 x 101 MB) far exceed the 256 MB last-level cache, so no
+    # step finds its data left behind by an earlier one
+    ap.add_argument("--rotations", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")

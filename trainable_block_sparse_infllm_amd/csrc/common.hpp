@@ -89,6 +89,15 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// 16-byte load marked nontemporal: for data read once per kernel (the k-bar
+// table in decode scoring), so it does not displace reusable lines in the
+// caches.
+__device__ __forceinline__ uint4 ldg16_nt(const void* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return uint4{x[0], x[1], x[2], x[3]};
+}
+
 // Guarded loads without branches. A guarded load reads either the real
 // location or a device-global constant holding the neutral value (zeros, -inf)
 // and uses the result unconditionally: the choice is made on the address, so a

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(64) void score_lse_kernel(const uint16_t* __restric
   for (int m = 0; m < kKpb; ++m)
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds)
-      kf[m][ds] = as_bf16x8(ldg16(kbar + kbar_off<D>(bg, m, 2 * ds + hl, j0 + r32, nblk)));
+      kf[m][ds] = as_bf16x8(ldg16_nt(kbar + kbar_off<D>(bg, m, 2 * ds + hl, j0 + r32, nblk)));
   // A operand: row row0 + r32 -> (node, head)
   bf16x8 qa[DS];
   {
