@@ -253,74 +253,107 @@ def summarize_pmc(fetch_db: str, write_db: str, copy_bytes: int) -> dict:
 
 
 # ------------------------------------------------------------------ timing helpers
+def dist(samples) -> dict:
+    """Median, 10th and 90th percentile and mean of a list of times."""
+    a = np.asarray(samples, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "mean": float(a.mean()), "n": int(a.size)}
+
+
+def scaled(d: dict, f: float, nd: int = 3) -> dict:
+    return {k: (round(v * f, nd) if k != "n" else v) for k, v in d.items()}
+
+
 def timed_loop(fns_per_step, steps, warmup, torch):
-    """Run warmup steps, then `steps` timed steps; events between stages give per-stage times."""
+    """warmup untimed steps, then `steps` timed steps with an event between every two launches
+    (all on the current stream). Returns per-stage and per-step samples in ms."""
     nst = len(fns_per_step(0))
     for s in range(warmup):
         for f in fns_per_step(s):
             f()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(steps)]
-    t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
     for s in range(steps):
         fs = fns_per_step(s)
         ev[s][0].record()
         for i, f in enumerate(fs):
             f()
             ev[s][i + 1].record()
-    end.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    stage_ms = [float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)])) for i in range(nst)]
-    return total_ms / steps, stage_ms, wall
+    stage = [[ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)] for i in range(nst)]
+    step = [ev[s][0].elapsed_time(ev[s][nst]) for s in range(steps)]
+    return stage, step
 
 
-def graph_loop(fns_per_step, nsets, steps, warmup, torch):
-    """Capture nsets consecutive steps (one per input set) in one HIP graph; time its replays."""
+def capture(fns_per_step, first, count, torch):
+    """One HIP graph holding steps first .. first+count-1 (captured after one eager pass)."""
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        for s in range(nsets):
+        for s in range(first, first + count):
             for f in fns_per_step(s):
                 f()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
-        for s in range(nsets):
+        for s in range(first, first + count):
             for f in fns_per_step(s):
                 f()
-    reps = max(1, (steps + nsets - 1) // nsets)
-    for _ in range(max(1, warmup // nsets)):
-        g.replay()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(reps):
-        g.replay()
-    end.record()
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / (reps * nsets)
+    return g
 
 
-# ------------------------------------------------------------------ decode leg
+def graph_loop(fns_per_step, nsets, steps, warmup, torch):
+    """Exactly `steps` consecutive steps (step s on input set s % nsets) replayed from HIP graphs
+    of nsets steps (plus one graph for the remainder), after `warmup` steps' worth of replays.
+    Returns (mean ms per step over the timed region, per-step ms samples from each full replay)."""
+    g = capture(fns_per_step, 0, nsets, torch)
+    rem = steps % nsets
+    g_rem = capture(fns_per_step, 0, rem, torch) if rem else None
+    for _ in range(max(1, (warmup + nsets - 1) // nsets)):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = steps // nsets
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 2)]
+    ev[0].record()
+    for r in range(reps):
+        g.replay()
+        ev[r + 1].record()
+    if g_rem is not None:
+        g_rem.replay()
+    ev[reps + 1].record()
+    torch.cuda.synchronize()
+    total = ev[0].elapsed_time(ev[reps + 1])
+    per_step = [ev[r].elapsed_time(ev[r + 1]) / nsets for r in range(reps)]
+    return total / steps, per_step
+
+
+def dev_bf16(a, torch):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def make_cfg(lib, w):
+    return lib.make_cfg(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, top_k=w.top_k,
+                        dense_threshold=w.dense_threshold)
+
+
+def rotated(d, torch, ops, cfg, n):
+    """n independent device copies of (K, V, k̄) so the 256 MB last-level cache cannot serve a
+    step from the previous one."""
+    k0, v0 = dev_bf16(d["k"], torch), dev_bf16(d["v"], torch)
+    kb0 = ops.pool_kernels(cfg, k0, d["kv_cap"], d["kv_len"])
+    return [(k0, v0, kb0)] + [(k0.clone(), v0.clone(), kb0.clone()) for _ in range(n - 1)]
+
+
+# ------------------------------------------------------------------ decode (the headline)
 def bench_decode(w, steps, warmup, rotations, torch, lib, ops, synth):
     log(f"decode: generating {w.name} inputs")
     t = time.perf_counter()
     d = synth.generate(w, seed=0, threads=16)
     log(f"decode: generated in {time.perf_counter() - t:.1f}s; uploading {rotations} rotation(s)")
-    cfg = lib.make_cfg(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, top_k=w.top_k,
-                       dense_threshold=w.dense_threshold)
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
-    q = dev(d["q"])
-    k0, v0 = dev(d["k"]), dev(d["v"])
-    kbar0 = ops.pool_kernels(cfg, k0, d["kv_cap"], d["kv_len"])
-    sets = [(k0, v0, kbar0)] + [(k0.clone(), v0.clone(), kbar0.clone()) for _ in range(rotations - 1)]
+    cfg = make_cfg(lib, w)
+    q = dev_bf16(d["q"], torch)
+    sets = rotated(d, torch, ops, cfg, rotations)
     del d
     kv_cap, kv_len, n_q = w.kv_cap, w.kv_len, 1
     nblk = ops.nblk(kv_cap)
@@ -329,23 +362,25 @@ def bench_decode(w, steps, warmup, rotations, torch, lib, ops, synth):
     out = torch.empty((w.batch, w.n_q_heads, n_q, w.head_dim), dtype=torch.bfloat16, device="cuda")
     nbytes = lib.infllmv2_decode_workspace_bytes(cfg, n_q, kv_len)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
     def step(s):
         # stream None: the binding uses torch's current stream (the capture stream inside a graph)
         k, v, kbar = sets[s % len(sets)]
-        # scores over the whole kernel table, then top-K selection and sparse attention in one
-        # entry point (the selection runs inside the attention kernel)
         return [
             lambda: lib.infllmv2_score_blocks(cfg, q, n_q, kv_len - 1, 0, kbar, kv_cap, scores, None),
             lambda: lib.infllmv2_sparse_attn_decode_scores(cfg, q, k, v, kv_cap, kv_len, scores, idx, out, None,
                                                            ws, nbytes, None),
         ]
-    log(f"decode: timing {steps} eager steps after {warmup} warmup (per-stage events)")
-    ms, stage_ms, _ = timed_loop(step, steps, warmup, torch)
-    log("decode: capturing one graph of rotation steps and timing its replays")
-    g_ms = graph_loop(step, len(sets), steps, warmup, torch)
+    stage_names = ["score_blocks", "sparse_attn_decode_scores"]
+    log(f"decode: {steps} eager steps after {warmup} warmup (an event between launches)")
+    stage, step_eager = timed_loop(step, steps, warmup, torch)
+    log("decode: one graph of consecutive steps over the rotated sets, replayed")
+    g_ms, g_samples = graph_loop(step, len(sets), steps, warmup, torch)
+    log("decode: 100 graph replays for the per-step distribution")
+    _, g_dist = graph_loop(step, len(sets), 100 * len(sets), len(sets), torch)
 
-    # the decode loop with per-sequence lengths: append one token per sequence (pooling the
-    # block it completes), then scores, selection and attention at the new lengths
+    # decode loop with per-sequence lengths: append one token per sequence (pooling the block it
+    # completes), then scores, selection and attention at the new lengths
     lens = [kv_len - 1 - 4096 * b for b in range(w.batch)]
     lens_old = torch.tensor(lens, dtype=torch.int64, device="cuda")
     lens_new = lens_old + 1
@@ -353,6 +388,7 @@ def bench_decode(w, steps, warmup, rotations, torch, lib, ops, synth):
     v_new = torch.randn_like(k_new)
     nbv = lib.infllmv2_decode_varlen_workspace_bytes(cfg, kv_len)
     wsv = torch.empty(nbv, dtype=torch.uint8, device="cuda")
+
     def vstep(s):
         k, v, kbar = sets[s % len(sets)]
         return [
@@ -361,14 +397,17 @@ def bench_decode(w, steps, warmup, rotations, torch, lib, ops, synth):
             lambda: lib.infllmv2_sparse_attn_decode_varlen(cfg, q, k, v, kv_cap, lens_new, kv_len, scores, idx,
                                                            out, None, wsv, nbv, None),
         ]
-    log("decode loop (variable lengths): eager per-stage timing, then one graph of rotation steps")
-    _, vstage_ms, _ = timed_loop(vstep, steps, warmup, torch)
-    v_ms = graph_loop(vstep, len(sets), steps, warmup, torch)
-    varlen = dict(ms=v_ms, stage_ms=vstage_ms, lens=lens, bytes=decode_loop_bytes(w, [L + 1 for L in lens]))
+    log("decode loop (variable lengths): eager stages, then graph replays")
+    vstage, _ = timed_loop(vstep, steps, warmup, torch)
+    v_ms, _ = graph_loop(vstep, len(sets), steps, warmup, torch)
+    varlen = dict(ms=v_ms, stage=dict(zip(["append_kv", "score_blocks_varlen", "sparse_attn_decode_varlen"],
+                                          [dist(x) for x in vstage])),
+                  lens=lens, bytes=decode_loop_bytes(w, [L + 1 for L in lens]))
 
     # the same step with the LSE-normalized scores deciding the top-K
     nbl = lib.infllmv2_score_lse_workspace_bytes(cfg, n_q, kv_cap)
     wsl = torch.empty(nbl, dtype=torch.uint8, device="cuda")
+
     def lstep(s):
         k, v, kbar = sets[s % len(sets)]
         return [
@@ -377,55 +416,52 @@ def bench_decode(w, steps, warmup, rotations, torch, lib, ops, synth):
             lambda: lib.infllmv2_sparse_attn_decode_scores(cfg, q, k, v, kv_cap, kv_len, scores, idx, out, None,
                                                            ws, nbytes, None),
         ]
-    log("decode with LSE-normalized selection: eager per-stage timing, then one graph of rotation steps")
-    _, lstage_ms, _ = timed_loop(lstep, steps, warmup, torch)
-    l_ms = graph_loop(lstep, len(sets), steps, warmup, torch)
-    # the LSE scores add a write and a read of the per-head block values and tile partials
-    lse_extra = 2 * nbl
-    lsel = dict(ms=l_ms, stage_ms=lstage_ms, extra_bytes=lse_extra)
-    return dict(ms=g_ms, eager_ms=ms, stage_ms=stage_ms, bytes=decode_bytes(w), varlen=varlen, lse=lsel)
+    log("decode with LSE-normalized selection: eager stages, then graph replays")
+    lstage, _ = timed_loop(lstep, steps, warmup, torch)
+    l_ms, _ = graph_loop(lstep, len(sets), steps, warmup, torch)
+    lsel = dict(ms=l_ms, stage=dict(zip(["score_blocks_lse", "sparse_attn_decode_scores"],
+                                        [dist(x) for x in lstage])),
+                extra_bytes=2 * nbl)   # the per-head block values and tile partials, written and read
+    return dict(ms=g_ms, step_samples=g_samples, step_dist=dist(g_dist), eager_step=dist(step_eager),
+                stage=dict(zip(stage_names, [dist(x) for x in stage])), bytes=decode_bytes(w),
+                varlen=varlen, lse=lsel)
 
 
-# ------------------------------------------------------------------ prefill leg
-def bench_prefill(w, steps, warmup, torch, lib, ops, synth):
-    log(f"prefill: generating {w.name} inputs")
+# ------------------------------------------------------------------ prefill legs
+def prefill_inputs(w, torch, lib, ops, synth):
     d = synth.generate(w, seed=0, threads=16)
-    cfg = lib.make_cfg(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, top_k=w.top_k,
-                       dense_threshold=w.dense_threshold)
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
-    q, k, v = dev(d["q"]), dev(d["k"]), dev(d["v"])
+    cfg = make_cfg(lib, w)
+    q, k, v = dev_bf16(d["q"], torch), dev_bf16(d["k"], torch), dev_bf16(d["v"], torch)
     T, kv_cap = w.seq_len, d["kv_cap"]
-    del d
     kbar = torch.zeros(ops.kbar_shape(w.batch, w.n_kv_heads, kv_cap, w.head_dim), dtype=torch.bfloat16,
                        device="cuda")
     idx = torch.empty((w.batch, w.n_kv_heads, T, w.top_k), dtype=torch.int32, device="cuda")
     out = torch.empty((w.batch, w.n_q_heads, T, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    return cfg, q, k, v, kbar, idx, out, T, kv_cap
+
+
+def bench_prefill(w, steps, warmup, torch, lib, ops, synth):
+    log(f"prefill: generating {w.name} inputs")
+    cfg, q, k, v, kbar, idx, out, T, kv_cap = prefill_inputs(w, torch, lib, ops, synth)
+
     def step(s):
         return [
             lambda: lib.infllmv2_pool_kernels(cfg, k, kv_cap, T, 0, kbar, None),
             lambda: lib.infllmv2_topk_blocks(cfg, None, q, kbar, T, 0, 0, kv_cap, idx, None),
             lambda: lib.infllmv2_sparse_attn_prefill(cfg, q, T, k, v, kv_cap, T, idx, out, None, None),
         ]
-    log(f"prefill: timing {steps} steps after {warmup} warmup")
-    ms, stage_ms, _ = timed_loop(step, steps, warmup, torch)
-    return dict(ms=ms, stage_ms=stage_ms, flops=prefill_flops(w))
+    log(f"prefill {w.name}: {steps} timed steps after {warmup} warmup")
+    stage, st = timed_loop(step, steps, warmup, torch)
+    return dict(step=dist(st), stage=dict(zip(["pool_kernels", "topk_blocks_fused", "sparse_attn_prefill"],
+                                              [dist(x) for x in stage])), flops=prefill_flops(w))
 
 
 def bench_prefill_backward(w, steps, warmup, torch, lib, ops, synth):
     """Gradients of the sparse prefill (dq, dk, dv) for one upstream gradient dO, from the forward's
     own selection, output and log-sum-exp, as one training step's attention backward."""
     log(f"backward: generating {w.name} inputs and running the forward once (untimed)")
-    d = synth.generate(w, seed=0, threads=16)
-    cfg = lib.make_cfg(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, top_k=w.top_k,
-                       dense_threshold=w.dense_threshold)
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
-    q, k, v = dev(d["q"]), dev(d["k"]), dev(d["v"])
-    T, kv_cap = w.seq_len, d["kv_cap"]
-    del d
+    cfg, q, k, v, kbar, idx, out, T, kv_cap = prefill_inputs(w, torch, lib, ops, synth)
     B, Hq, Hkv, D = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
-    kbar = torch.zeros(ops.kbar_shape(B, Hkv, kv_cap, D), dtype=torch.bfloat16, device="cuda")
-    idx = torch.empty((B, Hkv, T, w.top_k), dtype=torch.int32, device="cuda")
-    out = torch.empty((B, Hq, T, D), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
     lib.infllmv2_pool_kernels(cfg, k, kv_cap, T, 0, kbar, None)
     lib.infllmv2_topk_blocks(cfg, None, q, kbar, T, 0, 0, kv_cap, idx, None)
@@ -437,103 +473,75 @@ def bench_prefill_backward(w, steps, warmup, torch, lib, ops, synth):
     dv = torch.zeros_like(dk)
     nbytes = lib.infllmv2_prefill_backward_workspace_bytes(cfg, T, T)
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+
     def step(s):
         return [lambda: lib.infllmv2_sparse_attn_prefill_backward(cfg, q, T, k, v, kv_cap, T, idx, out, lse,
                                                                   dout, dq, dk, dv, ws, nbytes, None)]
-    log(f"backward: timing {steps} steps after {warmup} warmup")
-    ms, _, _ = timed_loop(step, steps, warmup, torch)
-    return dict(ms=ms, flops=backward_flops(w), workspace_bytes=nbytes)
+    log(f"backward: {steps} timed steps after {warmup} warmup")
+    _, st = timed_loop(step, steps, warmup, torch)
+    return dict(step=dist(st), flops=backward_flops(w), workspace_bytes=nbytes)
 
 
 def bench_window(w, window, steps, warmup, torch, lib, ops, synth):
     """The draft model's attention: sliding-window causal attention over the whole prompt."""
     log(f"window: generating {w.name} inputs")
-    d = synth.generate(w, seed=0, threads=16)
-    cfg = lib.make_cfg(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, top_k=w.top_k,
-                       dense_threshold=w.dense_threshold)
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
-    q, k, v = dev(d["q"]), dev(d["k"]), dev(d["v"])
-    T, kv_cap = w.seq_len, d["kv_cap"]
-    del d
-    out = torch.empty((w.batch, w.n_q_heads, T, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    cfg, q, k, v, _, _, out, T, kv_cap = prefill_inputs(w, torch, lib, ops, synth)
+
     def step(s):
         return [lambda: lib.infllmv2_sliding_window_attn(cfg, q, T, k, v, kv_cap, T, window, out, None,
                                                          None)]
-    log(f"window: timing {steps} steps after {warmup} warmup")
-    ms, _, _ = timed_loop(step, steps, warmup, torch)
-    return dict(ms=ms, flops=window_flops(w, window))
+    log(f"window: {steps} timed steps after {warmup} warmup")
+    _, st = timed_loop(step, steps, warmup, torch)
+    return dict(step=dist(st), flops=window_flops(w, window))
 
 
-# ------------------------------------------------------------------ the other configurations
-def _rotated(d, torch, ops, cfg, w, n):
-    """n independent device copies of (K, V, k̄) so the 256 MB last-level cache cannot serve a
-    step from the previous one."""
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
-    k0, v0 = dev(d["k"]), dev(d["v"])
-    kb0 = ops.pool_kernels(cfg, k0, d["kv_cap"], d["kv_len"])
-    return [(k0, v0, kb0)] + [(k0.clone(), v0.clone(), kb0.clone()) for _ in range(n - 1)]
-
-
-def bench_configs(steps, warmup, torch, lib, ops, synth):
-    """Throughput of the remaining synthetic configurations next to their roofline: the 2K tiny
-    prefill (D64), the 32K single-sequence decode step and the 128K tree verification step."""
-    res = {}
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
-    # tiny prefill: kernels -> fused score/top-K -> attention
-    w = synth.WORKLOADS["tiny_prefill_2k"]
-    log(f"configs: {w.name}")
-    d = synth.generate(w, seed=0)
-    cfg = lib.make_cfg(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, top_k=w.top_k,
-                       dense_threshold=w.dense_threshold)
-    q, k, v = dev(d["q"]), dev(d["k"]), dev(d["v"])
-    T, cap = w.seq_len, d["kv_cap"]
-    kbar = torch.zeros(ops.kbar_shape(w.batch, w.n_kv_heads, cap, w.head_dim), dtype=torch.bfloat16,
-                       device="cuda")
-    idx = torch.empty((w.batch, w.n_kv_heads, T, w.top_k), dtype=torch.int32, device="cuda")
-    out = torch.empty_like(q)
-    def pstep(s):
-        return [lambda: lib.infllmv2_pool_kernels(cfg, k, cap, T, 0, kbar, None),
-                lambda: lib.infllmv2_topk_blocks(cfg, None, q, kbar, T, 0, 0, cap, idx, None),
-                lambda: lib.infllmv2_sparse_attn_prefill(cfg, q, T, k, v, cap, T, idx, out, None, None)]
-    ms, _, _ = timed_loop(pstep, steps, warmup, torch)
-    f = prefill_flops(w)["total"]
-    res[w.name] = {"ms_per_step": round(ms, 4), "tflops": round(f / (ms * 1e-3) / 1e12, 3),
-                   "algorithmic_gflop": round(f / 1e9, 3), "bound": "latency (parity-scale config)"}
-    # single-sequence 32K decode step
-    w = synth.WORKLOADS["decode_32k"]
-    log(f"configs: {w.name}")
+# ------------------------------------------------------------------ single-sequence decode and tree
+def bench_decode_one(w, steps, warmup, torch, lib, ops, synth):
+    """The 32K single-sequence decode step (scores, then selection and attention)."""
+    log(f"{w.name}: generating inputs")
     d = synth.generate(w, seed=0, threads=16)
-    cfg = lib.make_cfg(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, top_k=w.top_k,
-                       dense_threshold=w.dense_threshold)
-    sets = _rotated(d, torch, ops, cfg, w, 4)
-    q = dev(d["q"])
+    cfg = make_cfg(lib, w)
+    sets = rotated(d, torch, ops, cfg, 4)
+    q = dev_bf16(d["q"], torch)
     cap, L = d["kv_cap"], d["kv_len"]
     scores = torch.empty((w.batch, w.n_kv_heads, 1, ops.nblk(cap)), dtype=torch.float32, device="cuda")
     idx = torch.empty((w.batch, w.n_kv_heads, 1, w.top_k), dtype=torch.int32, device="cuda")
     out = torch.empty_like(q)
     nb = lib.infllmv2_decode_workspace_bytes(cfg, 1, L)
     ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+
     def dstep(s):
         k, v, kb = sets[s % len(sets)]
         return [lambda: lib.infllmv2_score_blocks(cfg, q, 1, L - 1, 0, kb, cap, scores, None),
                 lambda: lib.infllmv2_sparse_attn_decode_scores(cfg, q, k, v, cap, L, scores, idx, out, None, ws,
                                                                nb, None)]
-    g_ms = graph_loop(dstep, len(sets), steps, warmup, torch)
+    log(f"{w.name}: eager stages, then graph replays")
+    stage, _ = timed_loop(dstep, steps, warmup, torch)
+    g_ms, g_samples = graph_loop(dstep, len(sets), steps, warmup, torch)
     b = decode_bytes(w)["total"]
-    res[w.name] = {"us_per_step": round(g_ms * 1e3, 2), "tok_s": round(w.batch / (g_ms * 1e-3), 1),
-                   "algorithmic_bytes": b, "achieved_gbs": round(b / (g_ms * 1e-3) / 1e9, 1),
-                   "frac_hbm": round(b / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                   "bound": "latency (one sequence: 8 (b, g) rows)"}
-    del sets
-    # 128K tree verification: every node's top-K over the prefix, attention to its blocks, the
-    # prefix tail and its tree ancestors
-    w = synth.WORKLOADS["tree_128k"]
-    log(f"configs: {w.name}")
+    return dict(ms=g_ms, step_dist=dist(g_samples), bytes=b,
+                stage=dict(zip(["score_blocks", "sparse_attn_decode_scores"], [dist(x) for x in stage])))
+
+
+def tree_union(w, idx_host, P):
+    """Per KV group: the blocks any node of the tree attends in the prefix (selected blocks and the
+    prefix tail's block)."""
+    C = P // 64
+    out = []
+    for g in range(w.n_kv_heads):
+        blocks = set(int(j) for j in idx_host[0, g].ravel() if 0 <= j < C) | {C}
+        out.append(len(blocks))
+    return out
+
+
+def bench_tree(w, steps, warmup, torch, lib, ops, synth):
+    """128K tree verification: every node's top-K over the prefix, attention to its blocks, the
+    prefix tail and its tree ancestors."""
+    log(f"{w.name}: generating inputs")
     d = synth.generate(w, seed=0, threads=16)
-    cfg = lib.make_cfg(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, top_k=w.top_k,
-                       dense_threshold=w.dense_threshold)
-    sets = _rotated(d, torch, ops, cfg, w, 2)
-    q = dev(d["q"])
+    cfg = make_cfg(lib, w)
+    sets = rotated(d, torch, ops, cfg, 2)
+    q = dev_bf16(d["q"], torch)
     n_q, cap, L = d["n_q"], d["kv_cap"], d["kv_len"]
     P = L - n_q
     tmask = torch.from_numpy(d["tree_mask"].view(np.int64)).cuda()
@@ -542,30 +550,38 @@ def bench_configs(steps, warmup, torch, lib, ops, synth):
     out = torch.empty_like(q)
     nb = lib.infllmv2_decode_workspace_bytes(cfg, n_q, L)
     ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+
     def tstep(s):
         k, v, kb = sets[s % len(sets)]
         return [lambda: lib.infllmv2_score_blocks(cfg, q, n_q, P, 1, kb, cap, scores, None),
                 lambda: lib.infllmv2_topk_blocks(cfg, scores, None, None, n_q, P, 1, cap, idx, None),
                 lambda: lib.infllmv2_sparse_attn_decode(cfg, q, n_q, k, v, cap, L, idx, tmask, out, None, ws, nb,
                                                         None)]
-    g_ms = graph_loop(tstep, len(sets), steps, warmup, torch)
+    log(f"{w.name}: eager stages, then graph replays")
+    stage, _ = timed_loop(tstep, steps, warmup, torch)
+    g_ms, g_samples = graph_loop(tstep, len(sets), steps, warmup, torch)
     torch.cuda.synchronize()
-    # bytes: the k̄ scan of the prefix candidates, plus K and V of the union of the nodes' blocks
-    # (selected blocks, the prefix tail's block) and the tree rows, plus q and out
-    ih = idx.cpu().numpy()
+    U = tree_union(w, idx.cpu().numpy(), P)
     C = P // 64
-    kv = 0
-    for g in range(w.n_kv_heads):
-        blocks = set(int(j) for j in ih[0, g].ravel() if 0 <= j < C) | {C}
-        kv += len(blocks) * 64 * w.head_dim * 2 * 2
+    kv = sum(U) * 64 * w.head_dim * 2 * 2
     kbar_b = w.n_kv_heads * C * 3 * w.head_dim * 2
     tree_b = w.n_kv_heads * n_q * w.head_dim * 2 * 2 + w.n_q_heads * n_q * w.head_dim * 2 * 2
-    b = kbar_b + kv + tree_b
-    res[w.name] = {"us_per_step": round(g_ms * 1e3, 2), "tree_tokens_s": round(n_q / (g_ms * 1e-3), 1),
-                   "algorithmic_bytes": b, "achieved_gbs": round(b / (g_ms * 1e-3) / 1e9, 1),
-                   "frac_hbm": round(b / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                   "bound": "HBM and latency (16 nodes, one sequence)"}
-    return res
+    return dict(ms=g_ms, step_dist=dist(g_samples), bytes=kbar_b + kv + tree_b, union=U,
+                stage=dict(zip(["score_blocks", "topk_blocks", "sparse_attn_decode"], [dist(x) for x in stage])))
+
+
+def bench_tiny(w, steps, warmup, torch, lib, ops, synth):
+    log(f"{w.name}: generating inputs")
+    cfg, q, k, v, kbar, idx, out, T, cap = prefill_inputs(w, torch, lib, ops, synth)
+
+    def pstep(s):
+        return [lambda: lib.infllmv2_pool_kernels(cfg, k, cap, T, 0, kbar, None),
+                lambda: lib.infllmv2_topk_blocks(cfg, None, q, kbar, T, 0, 0, cap, idx, None),
+                lambda: lib.infllmv2_sparse_attn_prefill(cfg, q, T, k, v, cap, T, idx, out, None, None)]
+    stage, st = timed_loop(pstep, steps, warmup, torch)
+    return dict(step=dist(st), flops=prefill_flops(w),
+                stage=dict(zip(["pool_kernels", "topk_blocks_fused", "sparse_attn_prefill"],
+                               [dist(x) for x in stage])))
 
 
 def device_context(torch):
@@ -600,42 +616,106 @@ def device_context(torch):
     return {"copy_gbs_read_plus_write": round(copy_gbs, 1), "gemm_bf16_8192_tflops": round(gemm, 1)}
 
 
-# ------------------------------------------------------------------ CPU baseline (oracle)
-def cpu_baseline_decode(w, budget_s, synth):
-    import oracle as orc
-    log("cpu baseline: generating inputs and the oracle's k̄ (untimed)")
-    d = synth.generate(w, seed=0, threads=16)
-    kbar = orc.pool(d["k"], d["kv_len"])
+# ------------------------------------------------------------------ CPU baselines (the oracle)
+def host_info(orc) -> dict:
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
+    return {"nproc": affinity, "cpu_count": os.cpu_count(), "cpu_model": model,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"), "oracle_threads": orc.num_threads()}
+
+
+def _repeat(fn, budget_s):
     n, t0 = 0, time.perf_counter()
     while True:
-        orc.sparse_forward(d["q"], d["k"], d["v"], kv_len=d["kv_len"], q_pos0=d["kv_len"] - 1,
-                           n_kv_heads=w.n_kv_heads, top_k=w.top_k, dense_threshold=w.dense_threshold,
-                           kbar=kbar)
+        fn()
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
-            break
-    return dict(value=w.batch * n / el, unit="tok/s", cores=orc.num_threads(), kind="oracle",
-                sample=f"{n} full decode steps of {w.name} ({w.batch} sequences, all "
+            return n, el
+
+
+def cpu_decode(w, budget_s, synth, orc):
+    """Full decode steps (every sequence and KV group; k̄ precomputed, as on the GPU)."""
+    d = synth.generate(w, seed=0, threads=16)
+    kbar = orc.pool(d["k"], d["kv_len"])
+    n, el = _repeat(lambda: orc.sparse_forward(d["q"], d["k"], d["v"], kv_len=d["kv_len"], q_pos0=d["kv_len"] - 1,
+                                               n_kv_heads=w.n_kv_heads, top_k=w.top_k,
+                                               dense_threshold=w.dense_threshold, kbar=kbar), budget_s)
+    return dict(value=round(w.batch * n / el, 2), unit="tok/s", cores=orc.num_threads(), kind="oracle",
+                sample=f"{n} full decode steps of {w.name} ({w.batch} sequence(s), all "
                        f"{w.batch * w.n_kv_heads} KV-group rows; k̄ precomputed as on the GPU), {el:.1f}s")
 
 
+def cpu_tree(w, budget_s, synth, orc):
+    d = synth.generate(w, seed=0, threads=16)
+    kbar = orc.pool(d["k"], d["kv_len"])
+    P = d["kv_len"] - d["n_q"]
+    n, el = _repeat(lambda: orc.sparse_forward(d["q"], d["k"], d["v"], kv_len=d["kv_len"], q_pos0=P,
+                                               n_kv_heads=w.n_kv_heads, top_k=w.top_k,
+                                               dense_threshold=w.dense_threshold, tree_mask=d["tree_mask"],
+                                               kbar=kbar), budget_s)
+    return dict(value=round(d["n_q"] * n / el, 2), unit="tree tokens/s", cores=orc.num_threads(), kind="oracle",
+                sample=f"{n} full verification steps of {w.name} ({d['n_q']} nodes x {w.n_kv_heads} KV groups; "
+                       f"k̄ precomputed), {el:.1f}s")
+
+
+def cpu_prefill(w, budget_s, synth, orc, tiles=None):
+    """Pooling, scoring, selection and attention of the oracle; the whole prompt, or (tiles) every
+    row of some 32-token tiles at spread depths, in GFLOP/s of the rows' algorithmic flops."""
+    d = synth.generate(w, seed=0, threads=16)
+    T = w.seq_len
+    if tiles is None:
+        toks = np.arange(T)
+        rows = None
+        what = f"the whole {T}-token prompt"
+    else:
+        toks = np.array([32 * t + i for t in tiles for i in range(32) if 32 * t + i < T])
+        rows = np.array([(b, g, t) for b in range(w.batch) for g in range(w.n_kv_heads) for t in toks], np.int32)
+        what = f"{len(toks)} tokens (every row of {len(tiles)} 32-token tiles at depths spread over the prompt)"
+    D, Hq = w.head_dim, w.n_q_heads
+    C = toks // 64
+    dense = (toks + 1) < w.dense_threshold if w.dense_threshold > 0 else np.zeros(len(toks), bool)
+    keys = np.where(dense, toks + 1, 64 * np.minimum(C, w.top_k) + toks % 64 + 1)
+    flops = float((4 * D * Hq * keys).sum() + (2 * D * Hq * 3 * C[C > w.top_k]).sum()) * w.batch
+
+    def run():
+        kbar = orc.pool(d["k"], d["kv_len"])
+        orc.sparse_forward(d["q"], d["k"], d["v"], kv_len=d["kv_len"], q_pos0=0, n_kv_heads=w.n_kv_heads,
+                           top_k=w.top_k, dense_threshold=w.dense_threshold, group_rows=rows, kbar=kbar)
+    n, el = _repeat(run, budget_s)
+    return dict(value=round(flops * n / el / 1e9, 3), unit="GFLOP/s", cores=orc.num_threads(), kind="oracle",
+                sample=f"{n} run(s) of pooling + scoring + selection + attention for {what} of {w.name} "
+                       f"({flops / 1e9:.2f} GFLOP algorithmic per run), {el:.1f}s")
+
+
 # ------------------------------------------------------------------ main
+LEGS = ["decode", "prefill", "backward", "window", "tiny", "decode32k", "tree", "context"]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     # independent K, V and k-bar sets cycled through by the decode graph: ten steps' selected
     # K/V (10 x 69 MB) and k-bar (10 x 101 MB) far exceed the 256 MB last-level cache, so no
     # step finds its data left behind by an earlier one
     ap.add_argument("--rotations", type=int, default=10)
+    ap.add_argument("--legs", default=",".join(LEGS),
+                    help="comma-separated subset of " + ",".join(LEGS) + " (a trace of one leg alone)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--no-backward", action="store_true")
-    ap.add_argument("--no-window", action="store_true")
-    ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter calibration)")
     ap.add_argument("--summarize-trace", metavar="DB",
@@ -673,6 +753,11 @@ def main():
         print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
+    legs = [x for x in args.legs.split(",") if x]
+    bad = [x for x in legs if x not in LEGS]
+    if bad:
+        print(f"unknown legs {bad}; choose from {LEGS}", file=sys.stderr)
+        sys.exit(2)
 
     import torch
     import synth
@@ -682,113 +767,179 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     lib.lib()
-
-    wd = synth.WORKLOADS["decode_128k_b8"]
-    dec = bench_decode(wd, args.steps, args.warmup, args.rotations, torch, lib, ops, synth)
-    tok_s = wd.batch / (dec["ms"] * 1e-3)
-    names = ["score_blocks", "sparse_attn_decode_scores"]
-    stage = dict(zip(names, dec["stage_ms"]))
-    b = dec["bytes"]
-    score_gbs = b["score"] / (stage["score_blocks"] * 1e-3) / 1e9
-    attn_gbs = b["attn"] / (stage["sparse_attn_decode_scores"] * 1e-3) / 1e9
-    step_gbs = b["total"] / (dec["ms"] * 1e-3) / 1e9
-    dominant = "score_blocks" if stage["score_blocks"] >= stage["sparse_attn_decode_scores"] \
-        else "sparse_attn_decode_scores"
-    dom_gbs = score_gbs if dominant == "score_blocks" else attn_gbs
-    dom_bytes = b["score"] if dominant == "score_blocks" else b["attn"]
+    K, W = args.steps, args.warmup
+    cpu = not args.no_cpu_baseline
+    if cpu:
+        import oracle as orc
+    Wk = synth.WORKLOADS
+    wd = Wk["decode_128k_b8"]
     result = {
         "metric": "128K sparse-attn decode tok/s + prefill TFLOP/s; % HBM/MFMA roofline",
-        "value": round(tok_s, 1),
-        "unit": "tok/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(dec["ms"], 5),
-        "timing": "one HIP graph of consecutive decode steps over the rotated input sets, replayed; "
-                  "per-stage times from eager steps with events between launches",
-        "eager_ms_per_step": round(dec["eager_ms"], 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
+        "value": None, "unit": "tok/s", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": None,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wd.name, "batch": wd.batch, "kv_len": wd.kv_len, "q_heads": wd.n_q_heads,
                    "kv_heads": wd.n_kv_heads, "head_dim": wd.head_dim, "top_k": wd.top_k,
                    "block": 64, "kernel_window": 32, "kernel_stride": 16, "rotations": args.rotations},
-        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(dominant),
-                     "algorithmic_bytes_per_launch": dom_bytes},
-        "step_hbm": {"algorithmic_bytes": b["total"], "achieved_gbs": round(step_gbs, 1),
-                     "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
-        "stages_ms": {k: round(v, 5) for k, v in stage.items()},
     }
-    ls = dec["lse"]
-    lb = b["total"] + ls["extra_bytes"]
-    result["decode_lse_selection"] = {
-        "workload": f"{wd.name}, top-K from LSE-normalized scores",
-        "tok_s": round(wd.batch / (ls["ms"] * 1e-3), 1), "ms_per_step": round(ls["ms"], 5),
-        "stages_ms": {k: round(v, 5) for k, v in zip(["score_blocks_lse", "sparse_attn_decode_scores"],
-                                                     ls["stage_ms"])},
-        "step_hbm": {"algorithmic_bytes": lb, "achieved_gbs": round(lb / (ls["ms"] * 1e-3) / 1e9, 1),
-                     "frac": round(lb / (ls["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-    }
-    vl = dec["varlen"]
-    vb = vl["bytes"]
-    result["decode_loop_varlen"] = {
-        "workload": f"{wd.name} with per-sequence lengths 131071 - 4096 b, one appended token each",
-        "tok_s": round(wd.batch / (vl["ms"] * 1e-3), 1), "ms_per_step": round(vl["ms"], 5),
-        "stages_ms": {k: round(v, 5) for k, v in zip(["append_kv", "score_blocks_varlen",
-                                                       "sparse_attn_decode_varlen"], vl["stage_ms"])},
-        "step_hbm": {"algorithmic_bytes": vb["total"],
-                     "achieved_gbs": round(vb["total"] / (vl["ms"] * 1e-3) / 1e9, 1),
-                     "frac": round(vb["total"] / (vl["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-    }
-    if not args.no_prefill:
-        wp = synth.WORKLOADS["prefill_32k"]
-        pre = bench_prefill(wp, max(3, args.steps // 5), max(1, args.warmup // 5), torch, lib, ops, synth)
+    configs = {}
+    if cpu:
+        result["host"] = host_info(orc)
+
+    if "decode" in legs:
+        dec = bench_decode(wd, K, W, args.rotations, torch, lib, ops, synth)
+        b = dec["bytes"]
+        st = dec["stage"]
+        step_gbs = b["total"] / (dec["ms"] * 1e-3) / 1e9
+        # dominant launch: the entry point with the longer median event time; its algorithmic bytes
+        # over that time
+        per = {"score_blocks": (st["score_blocks"]["median"], b["score"]),
+               "sparse_attn_decode_scores": (st["sparse_attn_decode_scores"]["median"], b["attn"])}
+        dom = max(per, key=lambda x: per[x][0])
+        dom_ms, dom_bytes = per[dom]
+        dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
+        result.update({
+            "value": round(wd.batch / (dec["ms"] * 1e-3), 1),
+            "ms_per_step": round(dec["ms"], 5),
+            "timing": f"exactly {K} consecutive decode steps replayed from HIP graphs of {args.rotations} steps "
+                      f"(one per rotated input set) after {W} warmup steps; per-stage times from eager steps "
+                      "with events between launches",
+            "step_us": scaled(dec["step_dist"], 1e3),
+            "eager_step_us": scaled(dec["eager_step"], 1e3),
+            "stages_us": {k: scaled(v, 1e3) for k, v in st.items()},
+            "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic(dom), "algorithmic_bytes_per_launch": dom_bytes,
+                         "launch_us_median": round(dom_ms * 1e3, 3),
+                         "timing": "median of the launch's event-timed duration over the eager steps"},
+            "step_hbm": {"algorithmic_bytes": b["total"], "achieved_gbs": round(step_gbs, 1),
+                         "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
+        })
+        ls = dec["lse"]
+        lb = b["total"] + ls["extra_bytes"]
+        result["decode_lse_selection"] = {
+            "workload": f"{wd.name}, top-K from LSE-normalized scores",
+            "tok_s": round(wd.batch / (ls["ms"] * 1e-3), 1), "ms_per_step": round(ls["ms"], 5),
+            "stages_us": {k: scaled(v, 1e3) for k, v in ls["stage"].items()},
+            "step_hbm": {"algorithmic_bytes": lb, "achieved_gbs": round(lb / (ls["ms"] * 1e-3) / 1e9, 1),
+                         "frac": round(lb / (ls["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        }
+        vl = dec["varlen"]
+        vb = vl["bytes"]
+        result["decode_loop_varlen"] = {
+            "workload": f"{wd.name} with per-sequence lengths 131071 - 4096 b, one appended token each",
+            "tok_s": round(wd.batch / (vl["ms"] * 1e-3), 1), "ms_per_step": round(vl["ms"], 5),
+            "stages_us": {k: scaled(v, 1e3) for k, v in vl["stage"].items()},
+            "step_hbm": {"algorithmic_bytes": vb["total"],
+                         "achieved_gbs": round(vb["total"] / (vl["ms"] * 1e-3) / 1e9, 1),
+                         "frac": round(vb["total"] / (vl["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        }
+        configs[wd.name] = {"us_per_step": round(dec["ms"] * 1e3, 2), "tok_s": result["value"],
+                            "frac_hbm": result["step_hbm"]["frac"]}
+        if cpu:
+            log("cpu baseline: the oracle's decode step for decode_128k_b8")
+            result["cpu_baseline"] = cpu_decode(wd, args.cpu_seconds, synth, orc)
+            configs[wd.name]["cpu_baseline"] = result["cpu_baseline"]
+
+    if "prefill" in legs:
+        wp = Wk["prefill_32k"]
+        pre = bench_prefill(wp, K, W, torch, lib, ops, synth)
         f = pre["flops"]
-        pst = dict(zip(["pool_kernels", "topk_blocks_fused", "sparse_attn_prefill"], pre["stage_ms"]))
-        tf = f["total"] / (pre["ms"] * 1e-3) / 1e12
-        attn_tf = f["attn"] / (pst["sparse_attn_prefill"] * 1e-3) / 1e12
+        ms = pre["step"]["mean"]
+        tf = f["total"] / (ms * 1e-3) / 1e12
+        attn_ms = pre["stage"]["sparse_attn_prefill"]["median"]
+        attn_tf = f["attn"] / (attn_ms * 1e-3) / 1e12
         result["prefill"] = {
-            "workload": wp.name, "tflops": round(tf, 2), "ms_per_step": round(pre["ms"], 4),
+            "workload": wp.name, "tflops": round(tf, 2), "ms_per_step": round(ms, 4),
+            "step_ms": scaled(pre["step"], 1, 4),
             "frac_mfma": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_gflop": round(f["total"] / 1e9, 2),
-            "stages_ms": {k: round(v, 4) for k, v in pst.items()},
+            "stages_ms": {k: scaled(v, 1, 4) for k, v in pre["stage"].items()},
             "roofline": {"bound": "mfma", "kernel": "sparse_attn_prefill", "achieved": round(attn_tf, 2),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "algorithmic_gflop_per_launch": round(f["attn"] / 1e9, 2),
+                         "launch_ms_median": round(attn_ms, 4),
                          "traffic": measured_traffic("sparse_attn_prefill")},
         }
-    if not args.no_prefill and not args.no_backward:
-        wp = synth.WORKLOADS["prefill_32k"]
-        bw = bench_prefill_backward(wp, max(3, args.steps // 5), max(1, args.warmup // 5), torch, lib, ops,
-                                    synth)
-        btf = bw["flops"] / (bw["ms"] * 1e-3) / 1e12
+        configs[wp.name] = {"ms_per_step": round(ms, 4), "tflops": round(tf, 2),
+                            "frac_mfma": result["prefill"]["frac_mfma"]}
+        if cpu:
+            log("cpu baseline: the oracle on whole tiles of prefill_32k")
+            configs[wp.name]["cpu_baseline"] = cpu_prefill(wp, 6.0, synth, orc, tiles=[0, 100, 400, 700, 1023])
+
+    if "backward" in legs:
+        wp = Wk["prefill_32k"]
+        bw = bench_prefill_backward(wp, K, W, torch, lib, ops, synth)
+        ms = bw["step"]["median"]
+        btf = bw["flops"] / (ms * 1e-3) / 1e12
         result["prefill_backward"] = {
-            "workload": wp.name, "ms_per_step": round(bw["ms"], 4), "algorithmic_gflop": round(bw["flops"] / 1e9, 2),
-            "workspace_bytes": bw["workspace_bytes"],
+            "workload": wp.name, "ms_per_step": round(bw["step"]["mean"], 4), "step_ms": scaled(bw["step"], 1, 4),
+            "algorithmic_gflop": round(bw["flops"] / 1e9, 2), "workspace_bytes": bw["workspace_bytes"],
             "roofline": {"bound": "mfma", "kernel": "sparse_attn_prefill_backward", "achieved": round(btf, 2),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(btf / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic("sparse_attn_prefill_backward")},
         }
-    if not args.no_prefill and not args.no_window:
-        wp = synth.WORKLOADS["prefill_32k"]
-        sw = bench_window(wp, WINDOW, max(3, args.steps // 5), max(1, args.warmup // 5), torch, lib, ops,
-                          synth)
-        wtf = sw["flops"] / (sw["ms"] * 1e-3) / 1e12
+
+    if "window" in legs:
+        wp = Wk["prefill_32k"]
+        sw = bench_window(wp, WINDOW, K, W, torch, lib, ops, synth)
+        ms = sw["step"]["median"]
+        wtf = sw["flops"] / (ms * 1e-3) / 1e12
         result["sliding_window"] = {
-            "workload": f"{wp.name}, window {WINDOW}", "ms_per_step": round(sw["ms"], 4),
-            "algorithmic_gflop": round(sw["flops"] / 1e9, 2),
+            "workload": f"{wp.name}, window {WINDOW}", "ms_per_step": round(sw["step"]["mean"], 4),
+            "step_ms": scaled(sw["step"], 1, 4), "algorithmic_gflop": round(sw["flops"] / 1e9, 2),
             "roofline": {"bound": "mfma", "kernel": "sliding_window_attn", "achieved": round(wtf, 2),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(wtf / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic("sliding_window_attn")},
         }
-    if not args.no_configs:
-        result["configs"] = bench_configs(max(20, args.steps // 2), max(3, args.warmup // 2), torch, lib, ops,
-                                          synth)
+
+    if "tiny" in legs:
+        w = Wk["tiny_prefill_2k"]
+        r = bench_tiny(w, K, W, torch, lib, ops, synth)
+        f = r["flops"]["total"]
+        ms = r["step"]["median"]
+        configs[w.name] = {"ms_per_step": scaled(r["step"], 1, 4), "tflops": round(f / (ms * 1e-3) / 1e12, 3),
+                           "algorithmic_gflop": round(f / 1e9, 3), "bound": "latency (parity-scale config)",
+                           "stages_ms": {k: scaled(v, 1, 4) for k, v in r["stage"].items()}}
+        if cpu:
+            log("cpu baseline: the oracle on tiny_prefill_2k")
+            configs[w.name]["cpu_baseline"] = cpu_prefill(w, 3.0, synth, orc)
+
+    if "decode32k" in legs:
+        w = Wk["decode_32k"]
+        r = bench_decode_one(w, K, W, torch, lib, ops, synth)
+        b = r["bytes"]
+        configs[w.name] = {"us_per_step": round(r["ms"] * 1e3, 2), "step_us": scaled(r["step_dist"], 1e3),
+                           "tok_s": round(w.batch / (r["ms"] * 1e-3), 1), "algorithmic_bytes": b,
+                           "achieved_gbs": round(b / (r["ms"] * 1e-3) / 1e9, 1),
+                           "frac_hbm": round(b / (r["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "stages_us": {k: scaled(v, 1e3) for k, v in r["stage"].items()},
+                           "bound": "latency (one sequence: 8 (b, g) rows)"}
+        if cpu:
+            log("cpu baseline: the oracle on decode_32k")
+            configs[w.name]["cpu_baseline"] = cpu_decode(w, 3.0, synth, orc)
+
+    if "tree" in legs:
+        w = Wk["tree_128k"]
+        r = bench_tree(w, K, W, torch, lib, ops, synth)
+        b = r["bytes"]
+        U = r["union"]
+        configs[w.name] = {"us_per_step": round(r["ms"] * 1e3, 2), "step_us": scaled(r["step_dist"], 1e3),
+                           "tree_tokens_s": round(w.n_tree / (r["ms"] * 1e-3), 1),
+                           "union_blocks_per_group": U, "union_blocks_mean": round(float(np.mean(U)), 2),
+                           "algorithmic_bytes": b, "achieved_gbs": round(b / (r["ms"] * 1e-3) / 1e9, 1),
+                           "frac_hbm": round(b / (r["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "stages_us": {k: scaled(v, 1e3) for k, v in r["stage"].items()},
+                           "bound": "HBM and latency (16 nodes, one sequence)"}
+        if cpu:
+            log("cpu baseline: the oracle on tree_128k")
+            configs[w.name]["cpu_baseline"] = cpu_tree(w, 3.0, synth, orc)
+
+    if configs:
+        result["configs"] = configs
+    if "context" in legs:
         result["device_context"] = device_context(torch)
         result["pages_claims"] = {
             "note": "context, not targets: the pages report no absolute throughput for this path",
@@ -807,10 +958,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         result["copy_calibration_bytes"] = n
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_decode(wd, args.cpu_seconds, synth)
-    else:
-        result["cpu_baseline"] = None
+    result.setdefault("cpu_baseline", None)
     print(json.dumps(result), flush=True)
 
 

@@ -259,7 +259,8 @@ INFLLMV2_API int infllmv2_append_kv(const infllmv2_cfg* cfg, const void* k_new, 
  * (the scoring of infllmv2_score_blocks): sequence b's token sits at position
  * kv_lens[b] - 1 (device int64 [B], each >= 1), so its candidates are the
  * complete blocks j < (kv_lens[b] - 1)/64. q [B][Hq][1][D]; scores
- * [B][Hkv][1][kv_cap/64] fp32, -inf past each sequence's candidates. */
+ * [B][Hkv][1][nblk] fp32 with nblk = ceil(kv_cap / 64), -inf past each
+ * sequence's candidates. */
 INFLLMV2_API int infllmv2_score_blocks_varlen(const infllmv2_cfg* cfg, const void* q,
                                  const int64_t* kv_lens, const void* kbar, int64_t kv_cap,
                                  float* scores, void* stream);

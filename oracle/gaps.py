@@ -1,4 +1,6 @@
-"""Open top-K score gaps in generated inputs (test infrastructure; calls only the oracle).
+"""Open top-K score gaps in generated inputs.
+
+TEST INFRASTRUCTURE ONLY (tests, the smoke check): it calls only the oracle.
 
 Selection is compared bit-exactly, so every compared row must have a clear
 boundary: when a row has more candidates than K, the K-th and (K+1)-th best

@@ -187,3 +187,38 @@ def test_valid_call_without_gpu_reports_hip_error(t):
         pytest.skip("a GPU is present")
     rc, msg = call(t, "infllmv2_pool_kernels", cfg_ok(t), A, 64, 64, 0, B, None)
     assert rc == -4 and "HIP error" in msg
+
+
+# kv_cap need not be a multiple of 64: the tables hold nblk = ceil(kv_cap / 64) blocks and the
+# kernels bound every read at kv_len, so such a cache is accepted and the call reaches the device
+# check (here, without a GPU, a HIP error), never INVALID_ARGUMENT.
+KV_CAP_RAGGED = [
+    ("infllmv2_pool_kernels", (A, 100, 100, 0, B, None)),
+    ("infllmv2_score_blocks", (A, 1, 99, 0, B, 100, A, None)),
+    ("infllmv2_topk_blocks", (A, None, None, 1, 99, 0, 100, B, None)),
+    ("infllmv2_sparse_attn_prefill", (A, 64, A, A, 100, 100, B, A, None, None)),
+    ("infllmv2_sparse_attn_decode_scores", (A, A, A, 100, 100, A, None, B, None, 0x100000, 1 << 30, None)),
+    ("infllmv2_dense_attn", (A, 1, A, A, 100, 100, 1, B, None, None)),
+    ("infllmv2_score_blocks_varlen", (A, A, A, 100, A, None)),
+]
+
+
+@pytest.mark.parametrize("name,args", KV_CAP_RAGGED)
+def test_kv_cap_not_multiple_of_64_is_accepted(t, name, args):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    rc, msg = call(t, name, cfg_ok(t), *args)
+    assert rc == -4 and "HIP error" in msg, msg
+
+
+def test_fused_topk_accepts_4096_candidates_for_every_group_size(t):
+    """One or two query heads per group with up to 4096 candidates fit the fused path (fewer tokens per
+    workgroup): the call passes every argument check."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    for hq, hkv in [(2, 2), (4, 2), (8, 2), (32, 8)]:
+        cfg = cfg_ok(t, n_q_heads=hq, n_kv_heads=hkv, head_dim=64)
+        rc, msg = call(t, "infllmv2_topk_blocks", cfg, None, A, B, 16, 64 * 4096, 0, 64 * 4097, A, None)
+        assert rc == -4 and "HIP error" in msg, (hq, hkv, msg)

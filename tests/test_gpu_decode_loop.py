@@ -15,7 +15,7 @@ import torch
 import oracle as orc
 import synth
 from trainable_block_sparse_infllm_amd import ops
-from gaps import open_gaps
+from oracle.gaps import open_gaps
 from gpu_util import LSE_ABS, assert_close_rows, cfg_of, dev_bf16, host_f64, kbar_rows, note
 
 pytestmark = pytest.mark.gpu

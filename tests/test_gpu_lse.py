@@ -14,7 +14,7 @@ import torch
 import oracle as orc
 import synth
 from trainable_block_sparse_infllm_amd import ops
-from gaps import open_gaps
+from oracle.gaps import open_gaps
 from gpu_util import LSE_ABS, assert_close_rows, cfg_of, dev_bf16, dev_i32, host_f64, note
 
 pytestmark = pytest.mark.gpu

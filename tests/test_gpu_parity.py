@@ -13,7 +13,7 @@ import oracle as orc
 import synth
 import trainable_block_sparse_infllm_amd as lib
 from trainable_block_sparse_infllm_amd import ops
-from gaps import open_gaps
+from oracle.gaps import open_gaps
 from gpu_util import (LSE_ABS, assert_close_rows, cfg_of, check_idx_rows, dev_bf16, dev_i32, dev_u64, kbar_rows,
                       host_f64, host_u16, note)
 
@@ -145,14 +145,21 @@ def test_prefill_attention_chunk_with_oracle_indices(n_q, kv_len, thr):
     assert np.abs(host_f64(lse)[hr[:, 0], hr[:, 1], hr[:, 2]] - ref["lse"]).max() <= LSE_ABS
 
 
-def test_prefill_32k_full_size_sampled_rows():
+# Whole 32-token tiles of the 32K prefill compared row by row (every token of the tile, all
+# query heads of every KV group): the attention kernel's tile for GQA 4 is 32 tokens and the
+# fused top-K kernel's 16, so each listed tile covers whole workgroups of both. Depths spread
+# over the sequence; tile 31 (tokens 992-1023) holds the dense-threshold boundary (row 1022
+# dense, 1023 sparse), tiles 32 and 33 the first fully sparse rows, tile 1023 the last token.
+PREFILL_32K_TILES = [0, 1, 31, 32, 33, 64, 127, 200, 255, 256, 400, 511, 512, 700, 900, 1023]
+
+
+def test_prefill_32k_full_size_whole_tiles():
     """The full prefill workload in the benchmark's launch configuration; the
-    oracle checks sampled rows (every KV group, block edges, the dense
-    threshold boundary, the last token) and all rows are checked for validity."""
+    oracle checks every row of 16 whole 32-token tiles per KV group (block
+    edges, the dense threshold boundary, the last token), and every selection
+    row of the call is checked for validity."""
     w = P0
-    rng = np.random.default_rng(11)
-    toks = sorted(set([0, 1, 63, 64, 65, 1022, 1023, 1024, 4095, 4096, 16383, 32766, 32767]
-                      + rng.integers(0, w.seq_len, 48).tolist()))
+    toks = [32 * tile + t for tile in PREFILL_32K_TILES for t in range(32)]
     rows = np.array([(0, g, t) for g in range(w.n_kv_heads) for t in toks], dtype=np.int32)
     d, ref, res = run_prefill(w, seed=0, group_rows=rows)
     gidx = res["idx"].cpu().numpy().reshape(-1, w.top_k)

@@ -3,7 +3,7 @@ import numpy as np
 import torch
 
 import synth
-from gaps import open_gaps, boundary_gaps
+from oracle.gaps import open_gaps, boundary_gaps
 
 SMALL_DECODE = synth.WORKLOADS["decode_32k"].scaled(name="t_dec", n_q_heads=8, n_kv_heads=2, seq_len=4096,
                                                      top_k=8, n_plant=8)

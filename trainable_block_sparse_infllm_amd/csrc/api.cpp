@@ -220,6 +220,8 @@ int infllmv2_topk_blocks(const infllmv2_cfg* cfg, const float* scores, const voi
   const int64_t pos_last = is_tree ? q_pos0 : q_pos0 + n_q - 1;
   if (std::min(pos_last / 64, nblk_of(kv_cap)) > 4096)
     return fail(INFLLMV2_UNSUPPORTED, fn, "more than 4096 candidate blocks per row");
+  if (!scores && !infllmv2::topk_fused_ok(d, std::min(pos_last / 64, nblk_of(kv_cap))))
+    return fail(INFLLMV2_UNSUPPORTED, fn, "fused scoring: the score rows do not fit LDS");
   TRY(check_device(fn));
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (scores)

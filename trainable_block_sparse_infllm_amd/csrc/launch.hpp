@@ -40,6 +40,8 @@ hipError_t launch_scores_lse(const Dims& d, const uint16_t* q, int n_q, int64_t 
 hipError_t launch_topk_from_scores(const Dims& d, const float* scores, int n_q, int64_t q_pos0,
                                    int is_tree, int64_t nblk, int32_t* idx, hipStream_t s);
 
+// Whether the fused score + top-K path runs rows with cmax candidates.
+bool topk_fused_ok(const Dims& d, int64_t cmax);
 hipError_t launch_topk_fused(const Dims& d, const uint16_t* q, const uint16_t* kbar, int n_q,
                              int64_t q_pos0, int is_tree, int64_t nblk, int32_t* idx, hipStream_t s);
 

@@ -5,6 +5,8 @@
 //
 // Two producers feed it: a score tensor (decode, trees), or scores computed
 // in the same workgroup with MFMA and kept in LDS (prefill; never stored).
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "topk_select.hpp"
@@ -40,17 +42,19 @@ __global__ __launch_bounds__(256) void topk_scores_kernel(const float* __restric
 }
 
 // ---------------------------------------------------------- fused prefill path
-// Workgroup: 4 wavefronts, 16*NT query columns = TQ = 16*NT/G tokens of one
-// (b, g). Waves split the 16-block chunks of the k̄ table (MFMA, max over the
-// 3 kernel slots, head sum by shuffles) and park the scores in LDS
-// sc[TQ][64*KPL]; then each wave selects the rows of TQ/4 tokens.
+// Workgroup: 4 wavefronts, 16*NT query columns holding TQ <= 16*NT/G tokens of
+// one (b, g) (TQ is smaller only when TQ score rows of 64*KPL candidates would
+// not fit LDS; the columns of tokens >= TQ are idle). Waves split the 16-block
+// chunks of the k̄ table (MFMA, max over the 3 kernel slots, head sum by
+// shuffles) and park the scores in LDS sc[TQ][64*KPL]; then each wave selects
+// the rows of TQ/4 tokens.
 template <int D, int NT, int KPL>
 __global__ __launch_bounds__(256) void topk_fused_kernel(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ kbar,
                                                          int32_t* __restrict__ idx, int Hq, int Hkv,
                                                          int G, int n_q, int64_t q_pos0,
                                                          int is_tree, int64_t nblk, int K,
-                                                         int ntile) {
+                                                         int ntile, int TQ) {
   constexpr int KS = D / 32;
   constexpr int LDSC = KPL * kWave;
   extern __shared__ float sc[];
@@ -61,7 +65,6 @@ __global__ __launch_bounds__(256) void topk_fused_kernel(const uint16_t* __restr
   __syncthreads();
   const int l = lane_id();
   const int r16 = l % 16, kg = l / 16;
-  const int TQ = 16 * NT / G;
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   const int tile = item % ntile;
   const int bg = item / ntile;
@@ -119,7 +122,7 @@ __global__ __launch_bounds__(256) void topk_fused_kernel(const uint16_t* __restr
           best[nt][i] = v;
         }
         const int c = nt * 16 + r16;
-        if (c % G == 0) {
+        if (c % G == 0 && c / G < TQ) {
           float* dst = sc + (c / G) * LDSC;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -153,6 +156,36 @@ static int pick_kpl(int64_t cmax) {
   return kpl;
 }
 
+namespace {
+
+constexpr int kTopkFusedLds = 152 * 1024;   // the score tile's LDS budget (160 KB per CU on gfx950, less the static arrays)
+
+struct TopkFusedPlan {
+  int kpl, nt, tq;
+};
+
+// Columns per workgroup: the largest of 64/32/16 whose score tile (TQ tokens
+// x 64*KPL candidates, fp32) fits the LDS budget; when even 16 columns' tokens
+// do not fit (one query head per group and more than 2048 candidates), fewer
+// tokens, each with its full score row, leaving the other columns idle.
+TopkFusedPlan topk_fused_plan(const Dims& d, int64_t cmax) {
+  TopkFusedPlan p;
+  p.kpl = pick_kpl(cmax);
+  const int64_t row = int64_t(p.kpl) * kWave * 4;
+  p.nt = 4;
+  while (p.nt > 1 && int64_t(16 * p.nt / d.G) * row > kTopkFusedLds) p.nt >>= 1;
+  p.tq = std::min<int>(16 * p.nt / d.G, int(kTopkFusedLds / row));
+  if (16 * p.nt < d.G) p.tq = 0;
+  return p;
+}
+
+}  // namespace
+
+bool topk_fused_ok(const Dims& d, int64_t cmax) {
+  if (cmax > 64 * 64) return false;
+  return topk_fused_plan(d, cmax).tq >= 1;
+}
+
 hipError_t launch_topk_from_scores(const Dims& d, const float* scores, int n_q, int64_t q_pos0,
                                    int is_tree, int64_t nblk, int32_t* idx, hipStream_t s) {
   const int64_t rows = int64_t(d.B) * d.Hkv * n_q;
@@ -180,20 +213,21 @@ hipError_t launch_topk_fused(const Dims& d, const uint16_t* q, const uint16_t* k
   if (cmax > nblk) cmax = nblk;
   if (topk_prefill128_ok(d, cmax))
     return launch_topk_prefill128(d, q, kbar, n_q, q_pos0, is_tree, nblk, cmax, idx, s);
-  const int kpl = pick_kpl(cmax);
-  // Columns per workgroup: largest of 64/32/16 whose score tile fits 64 KB of LDS.
-  int nt = 4;
-  while (nt > 1 && int64_t(16 * nt / d.G) * kpl * kWave * 4 > 65536) nt >>= 1;
-  if (16 * nt < d.G) return hipErrorInvalidValue;
-  const int tq = 16 * nt / d.G;
+  const TopkFusedPlan p = topk_fused_plan(d, cmax);
+  if (p.tq < 1) return hipErrorInvalidValue;
+  const int kpl = p.kpl, nt = p.nt, tq = p.tq;
   const int ntile = (n_q + tq - 1) / tq;
   const size_t lds = size_t(tq) * kpl * kWave * sizeof(float);
-  if (lds > 65536) return hipErrorInvalidValue;
   const dim3 grid(unsigned(int64_t(d.B) * d.Hkv * ntile));
 #define FUSED_CASE(DD, NN, P)                                                                   \
   if (d.D == DD && nt == NN && kpl == P) {                                                      \
-    topk_fused_kernel<DD, NN, P><<<grid, 256, lds, s>>>(q, kbar, idx, d.Hq, d.Hkv, d.G, n_q,   \
-                                                        q_pos0, is_tree, nblk, d.K, ntile);     \
+    auto kern = topk_fused_kernel<DD, NN, P>;                                                   \
+    static const hipError_t attr = hipFuncSetAttribute(                                         \
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,        \
+        kTopkFusedLds);                                                                         \
+    if (attr != hipSuccess) return attr;                                                        \
+    kern<<<grid, 256, lds, s>>>(q, kbar, idx, d.Hq, d.Hkv, d.G, n_q, q_pos0, is_tree, nblk,    \
+                                d.K, ntile, tq);                                                \
     return hipGetLastError();                                                                   \
   }
 #define FUSED_D(DD, NN) \

@@ -82,7 +82,7 @@ def decode(cfg, q, k_cache, v_cache, kbar, kv_len, *, tree_mask=None, ws: Worksp
     B, Hq, n_q, D = q.shape
     kv_cap = k_cache.shape[2]
     is_tree = tree_mask is not None
-    q_pos0 = kv_len - n_q if is_tree else kv_len - n_q
+    q_pos0 = kv_len - n_q        # a tree's nodes all score against the prefix P = kv_len - n_q
     scores = torch.empty((B, cfg.n_kv_heads, n_q, nblk(kv_cap)), dtype=torch.float32, device=q.device)
     capi.infllmv2_score_blocks(cfg, q, n_q, q_pos0, is_tree, kbar, kv_cap, scores, stream)
     idx = torch.empty((B, cfg.n_kv_heads, n_q, cfg.top_k), dtype=torch.int32, device=q.device)
