@@ -174,6 +174,23 @@ INFLLMV2_API int infllmv2_sparse_attn_decode_scores(const infllmv2_cfg* cfg, con
                                        void* out, float* lse, void* workspace,
                                        size_t workspace_bytes, void* stream);
 
+/* infllmv2_sparse_attn_decode_scores without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the split partials live in
+ * a static device array of 16 MiB per GPU, allocated with the library's code
+ * object and held until the process ends. This call allocates nothing and
+ * calls no allocating routine. Same arguments, rules and results as
+ * infllmv2_sparse_attn_decode_scores; a shape whose workspace
+ * (infllmv2_decode_workspace_bytes with n_q = 1) exceeds 16 MiB returns
+ * INFLLMV2_UNSUPPORTED. Every call on one GPU shares that GPU's array: calls
+ * that overlap in time on one GPU (different streams or threads) race and
+ * must be serialized by the caller. */
+INFLLMV2_API int infllmv2_sparse_attn_decode_scores_noalloc(const infllmv2_cfg* cfg, const void* q,
+                                               const void* k_cache, const void* v_cache,
+                                               int64_t kv_cap, int64_t kv_len, const float* scores,
+                                               int32_t* idx_out, void* out, float* lse,
+                                               void* stream);
+
 /* Bytes of workspace infllmv2_sparse_attn_prefill_backward needs for these
  * shapes (0 if the configuration is invalid). */
 INFLLMV2_API size_t infllmv2_prefill_backward_workspace_bytes(const infllmv2_cfg* cfg, int32_t n_q,

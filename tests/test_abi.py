@@ -222,3 +222,20 @@ def test_fused_topk_accepts_4096_candidates_for_every_group_size(t):
         cfg = cfg_ok(t, n_q_heads=hq, n_kv_heads=hkv, head_dim=64)
         rc, msg = call(t, "infllmv2_topk_blocks", cfg, None, A, B, 16, 64 * 4096, 0, 64 * 4097, A, None)
         assert rc == -4 and "HIP error" in msg, (hq, hkv, msg)
+
+
+def test_noalloc_decode_rejects_scratch_above_its_maximum(t):
+    """The allocation-free decode checks the workspace the shape needs against its static scratch
+    (16 MiB) before any HIP call."""
+    cfg = cfg_ok(t, batch=256, n_q_heads=256, n_kv_heads=64, top_k=64)
+    need = t.infllmv2_decode_workspace_bytes(cfg, 1, 131072)
+    assert need > 16 << 20
+    rc, msg = call(t, "infllmv2_sparse_attn_decode_scores_noalloc", cfg, A, A, A, 131072, 131072, A, None, B,
+                   None, None)
+    assert rc == -2 and "static scratch" in msg, msg
+
+
+def test_package_binds_every_export(t):
+    """Each exported C function has a Python binding of the same name on the package."""
+    for name in t.EXPORTS:
+        assert callable(getattr(t, name)), name

@@ -8,7 +8,8 @@ from .capi import (  # noqa: F401
     EXPORTS, InfLLMv2Error, infllmv2_cfg, make_cfg, lib, LIB_PATH,
     infllmv2_pool_kernels, infllmv2_score_blocks, infllmv2_topk_blocks,
     infllmv2_sparse_attn_prefill, infllmv2_decode_workspace_bytes,
-    infllmv2_sparse_attn_decode, infllmv2_sparse_attn_decode_scores, infllmv2_dense_attn,
+    infllmv2_sparse_attn_decode, infllmv2_sparse_attn_decode_scores,
+    infllmv2_sparse_attn_decode_scores_noalloc, infllmv2_dense_attn,
     infllmv2_prefill_backward_workspace_bytes, infllmv2_sparse_attn_prefill_backward,
     infllmv2_sliding_window_attn, infllmv2_append_kv, infllmv2_score_blocks_varlen,
     infllmv2_decode_varlen_workspace_bytes, infllmv2_sparse_attn_decode_varlen,

@@ -18,7 +18,8 @@ OK, INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP_ERROR = 0, -1, -2, -
 EXPORTS = [
     "infllmv2_pool_kernels", "infllmv2_score_blocks", "infllmv2_topk_blocks",
     "infllmv2_sparse_attn_prefill", "infllmv2_decode_workspace_bytes",
-    "infllmv2_sparse_attn_decode", "infllmv2_sparse_attn_decode_scores", "infllmv2_dense_attn",
+    "infllmv2_sparse_attn_decode", "infllmv2_sparse_attn_decode_scores",
+    "infllmv2_sparse_attn_decode_scores_noalloc", "infllmv2_dense_attn",
     "infllmv2_prefill_backward_workspace_bytes", "infllmv2_sparse_attn_prefill_backward",
     "infllmv2_sliding_window_attn", "infllmv2_append_kv", "infllmv2_score_blocks_varlen",
     "infllmv2_decode_varlen_workspace_bytes", "infllmv2_sparse_attn_decode_varlen",
@@ -69,6 +70,7 @@ def lib():
             "infllmv2_decode_workspace_bytes": (sz, [cfg, i32, i64]),
             "infllmv2_sparse_attn_decode": (i32, [cfg, P, i32, P, P, i64, i64, P, P, P, P, P, sz, P]),
             "infllmv2_sparse_attn_decode_scores": (i32, [cfg, P, P, P, i64, i64, P, P, P, P, P, sz, P]),
+            "infllmv2_sparse_attn_decode_scores_noalloc": (i32, [cfg, P, P, P, i64, i64, P, P, P, P, P]),
             "infllmv2_dense_attn": (i32, [cfg, P, i32, P, P, i64, i64, i32, P, P, P]),
             "infllmv2_sliding_window_attn": (i32, [cfg, P, i32, P, P, i64, i64, i64, P, P, P]),
             "infllmv2_append_kv": (i32, [cfg, P, P, i32, P, P, i64, P, i64, P, P]),
@@ -152,6 +154,13 @@ def infllmv2_sparse_attn_decode_scores(cfg, q, k_cache, v_cache, kv_cap, kv_len,
     _check(lib().infllmv2_sparse_attn_decode_scores(C.byref(cfg), _p(q), _p(k_cache), _p(v_cache), kv_cap,
                                                     kv_len, _p(scores), _p(idx_out), _p(out), _p(lse),
                                                     _p(workspace), workspace_bytes, _s(stream)))
+
+
+def infllmv2_sparse_attn_decode_scores_noalloc(cfg, q, k_cache, v_cache, kv_cap, kv_len, scores, idx_out, out,
+                                               lse, stream=None):
+    _check(lib().infllmv2_sparse_attn_decode_scores_noalloc(C.byref(cfg), _p(q), _p(k_cache), _p(v_cache),
+                                                            kv_cap, kv_len, _p(scores), _p(idx_out), _p(out),
+                                                            _p(lse), _s(stream)))
 
 
 def infllmv2_dense_attn(cfg, q, n_q, k, v, kv_cap, kv_len, causal, out, lse=None, stream=None):

@@ -27,6 +27,7 @@
 // splits of the group repeat the same selection) and the entries follow. This
 // saves the separate selection kernel and its round trip.
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -574,6 +575,32 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
 
 size_t decode_workspace_bytes(const Dims& d, int n_q, int64_t kv_len) {
   return decode_layout(d, n_q, kv_len).total;
+}
+
+// Scratch memory of the allocation-free single-token decode entry point: the
+// split partials it would otherwise keep in a caller's workspace. One copy per
+// GPU, allocated by the loader with the code object and held until the
+// process ends. Host code never passes this array's name to a kernel (on the
+// host it only stands for the symbol): the device address comes from
+// hipGetSymbolAddress, once per device.
+static __device__ __align__(256) char scratch[kDecodeNoAllocScratchBytes];
+
+hipError_t decode_noalloc_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 size_t decode_varlen_workspace_bytes(const Dims& d, int64_t kv_len_max) {

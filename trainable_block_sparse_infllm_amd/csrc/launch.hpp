@@ -81,6 +81,12 @@ hipError_t launch_decode(const Dims& d, const uint16_t* q, int n_q, const uint16
                          int32_t* idx_out = nullptr, const int64_t* kv_lens = nullptr);
 size_t decode_varlen_workspace_bytes(const Dims& d, int64_t kv_len_max);
 
+// The allocation-free single-token decode keeps its workspace in a static
+// device array of this size (one per GPU); decode_noalloc_scratch() gives the
+// current device's address of it (looked up once per device).
+constexpr size_t kDecodeNoAllocScratchBytes = size_t(16) << 20;
+hipError_t decode_noalloc_scratch(void** ptr);
+
 // Backward of the head_dim-128 sparse prefill (mode 0): dq, dk, dv (fp32).
 bool prefill_backward_ok(const Dims& d, int64_t kv_len);
 size_t prefill_backward_workspace_bytes(const Dims& d, int n_q, int64_t kv_len);
