@@ -378,6 +378,26 @@ def bench_decode(w, steps, warmup, rotations, torch, lib, ops, synth):
     g_ms, g_samples = graph_loop(step, len(sets), steps, warmup, torch)
     log("decode: 100 graph replays for the per-step distribution")
     _, g_dist = graph_loop(step, len(sets), 100 * len(sets), len(sets), torch)
+    return dict(ms=g_ms, step_samples=g_samples, step_dist=dist(g_dist), eager_step=dist(step_eager),
+                stage=dict(zip(stage_names, [dist(x) for x in stage])), bytes=decode_bytes(w))
+
+
+def bench_decode_variants(w, steps, warmup, rotations, torch, lib, ops, synth):
+    """The decode-loop step with per-sequence lengths and the step with LSE-normalized selection, on
+    the 128K batch-8 caches (rotated as for the headline step)."""
+    log(f"decode variants: generating {w.name} inputs")
+    d = synth.generate(w, seed=0, threads=16)
+    cfg = make_cfg(lib, w)
+    q = dev_bf16(d["q"], torch)
+    sets = rotated(d, torch, ops, cfg, rotations)
+    del d
+    kv_cap, kv_len, n_q = w.kv_cap, w.kv_len, 1
+    nblk = ops.nblk(kv_cap)
+    scores = torch.empty((w.batch, w.n_kv_heads, n_q, nblk), dtype=torch.float32, device="cuda")
+    idx = torch.empty((w.batch, w.n_kv_heads, n_q, w.top_k), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.batch, w.n_q_heads, n_q, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    nbytes = lib.infllmv2_decode_workspace_bytes(cfg, n_q, kv_len)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
 
     # decode loop with per-sequence lengths: append one token per sequence (pooling the block it
     # completes), then scores, selection and attention at the new lengths
@@ -422,9 +442,7 @@ def bench_decode(w, steps, warmup, rotations, torch, lib, ops, synth):
     lsel = dict(ms=l_ms, stage=dict(zip(["score_blocks_lse", "sparse_attn_decode_scores"],
                                         [dist(x) for x in lstage])),
                 extra_bytes=2 * nbl)   # the per-head block values and tile partials, written and read
-    return dict(ms=g_ms, step_samples=g_samples, step_dist=dist(g_dist), eager_step=dist(step_eager),
-                stage=dict(zip(stage_names, [dist(x) for x in stage])), bytes=decode_bytes(w),
-                varlen=varlen, lse=lsel)
+    return dict(varlen=varlen, lse=lsel)
 
 
 # ------------------------------------------------------------------ prefill legs
@@ -700,7 +718,7 @@ def cpu_prefill(w, budget_s, synth, orc, tiles=None):
 
 
 # ------------------------------------------------------------------ main
-LEGS = ["decode", "prefill", "backward", "window", "tiny", "decode32k", "tree", "context"]
+LEGS = ["decode", "decode_variants", "prefill", "backward", "window", "tiny", "decode32k", "tree", "context"]
 
 
 def main():
@@ -798,6 +816,10 @@ def main():
         dom = max(per, key=lambda x: per[x][0])
         dom_ms, dom_bytes = per[dom]
         dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
+        per_launch = {k: {"median_us": round(v[0] * 1e3, 3), "algorithmic_bytes": v[1],
+                          "achieved_gbs": round(v[1] / (v[0] * 1e-3) / 1e9, 1),
+                          "frac": round(v[1] / (v[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "kernels": list(ENTRY_KERNELS[k][0])} for k, v in per.items()}
         result.update({
             "value": round(wd.batch / (dec["ms"] * 1e-3), 1),
             "ms_per_step": round(dec["ms"], 5),
@@ -814,7 +836,18 @@ def main():
                          "timing": "median of the launch's event-timed duration over the eager steps"},
             "step_hbm": {"algorithmic_bytes": b["total"], "achieved_gbs": round(step_gbs, 1),
                          "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
+            "launches": per_launch,
         })
+        configs[wd.name] = {"us_per_step": round(dec["ms"] * 1e3, 2), "tok_s": result["value"],
+                            "frac_hbm": result["step_hbm"]["frac"]}
+        if cpu:
+            log("cpu baseline: the oracle's decode step for decode_128k_b8")
+            result["cpu_baseline"] = cpu_decode(wd, args.cpu_seconds, synth, orc)
+            configs[wd.name]["cpu_baseline"] = result["cpu_baseline"]
+
+    if "decode_variants" in legs:
+        dec = bench_decode_variants(wd, K, W, args.rotations, torch, lib, ops, synth)
+        b = decode_bytes(wd)
         ls = dec["lse"]
         lb = b["total"] + ls["extra_bytes"]
         result["decode_lse_selection"] = {
@@ -834,12 +867,6 @@ def main():
                          "achieved_gbs": round(vb["total"] / (vl["ms"] * 1e-3) / 1e9, 1),
                          "frac": round(vb["total"] / (vl["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         }
-        configs[wd.name] = {"us_per_step": round(dec["ms"] * 1e3, 2), "tok_s": result["value"],
-                            "frac_hbm": result["step_hbm"]["frac"]}
-        if cpu:
-            log("cpu baseline: the oracle's decode step for decode_128k_b8")
-            result["cpu_baseline"] = cpu_decode(wd, args.cpu_seconds, synth, orc)
-            configs[wd.name]["cpu_baseline"] = result["cpu_baseline"]
 
     if "prefill" in legs:
         wp = Wk["prefill_32k"]
