@@ -179,7 +179,7 @@ __device__ __forceinline__ void load_v_tile(const uint16_t* vbase, int64_t key0,
     const int sw = D == 128 ? vswz(r) : ((r >> 2) & 3) << 1;
     const void* src = key < kv_len ? static_cast<const void*>(vbase + key * D + ((piece ^ sw) << 3))
                                    : static_cast<const void*>(kZeroPiece);
-    load_lds16(src, vt + x * RPI * D);
+    load_lds16_nt(src, vt + x * RPI * D);       // each selected block is read once per step
   }
 }
 
@@ -346,7 +346,8 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
       const int64_t key = key0 + kt * 16 + r16;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        kf[kt][ks] = as_bf16x8(ldg16_if(key < kv_len, kbase + key * D + ks * 32 + kg * 8));
+        kf[kt][ks] = as_bf16x8(ldg16_nt(key < kv_len ? static_cast<const void*>(kbase + key * D + ks * 32 + kg * 8)
+                                                     : static_cast<const void*>(kZeroPiece)));
     }
 
     bool sub_on[NSTD], row_on[NSTD];
@@ -522,7 +523,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
     int Hq, int Hkv, int G, int n_q, int nsplit, int sb, int n_e1, int rows, int64_t nrows) {
   constexpr int CPL = D / kWave;
   const int l = lane_id();
-  const int64_t rid = int64_t(blockIdx.x) * 4 + threadIdx.x / kWave;   // (b, h, i)
+  // (b, h, i); workgroups renumbered like the split kernel's, so a row's partials
+  // are read on the XCD whose L2 holds them
+  const int64_t rid = int64_t(xcd_remap(blockIdx.x, gridDim.x)) * 4 + threadIdx.x / kWave;
   if (rid >= nrows) return;
   const int i = int(rid % n_q);
   const int h = int((rid / n_q) % Hq);

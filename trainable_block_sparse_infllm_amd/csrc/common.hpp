@@ -156,6 +156,12 @@ __device__ __forceinline__ void load_lds16(const void* gsrc, void* lds_base) {
   __builtin_amdgcn_global_load_lds((gas_void*)gsrc, (las_void*)lds_base, 16, 0, 0);
 }
 
+// The same copy marked nontemporal (cache policy NT): for data read once per
+// kernel, so it does not displace reusable lines.
+__device__ __forceinline__ void load_lds16_nt(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((gas_void*)gsrc, (las_void*)lds_base, 16, 0, 2);
+}
+
 // s_waitcnt vmcnt(0): every vector-memory load of this wave, including the
 // direct-to-LDS ones the compiler does not track, has completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
