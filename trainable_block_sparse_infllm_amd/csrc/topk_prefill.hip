@@ -14,10 +14,12 @@
 //      32x32x16 bf16 MFMA (A = Q rows, B = kbar^T). An accumulator column is
 //      one block, so the max over the 3 kernels of a block is elementwise and
 //      the head sum of a token stays within a lane (G <= 4) or a lane pair.
-//      The next chunk's kbar fragments are loaded while one is computed.
-//      Scores go to LDS, sc[token][block];
-//   2. selection: one wavefront per token, with the exact wavefront top-K of
-//      topk_select.hpp over the scores in LDS.
+//      The next step's kbar fragments are loaded while one is computed.
+//      Order-preserving keys of the scores go to LDS, sc[token][block];
+//   2. selection: for K <= 16, four tokens per wavefront, one per 16-lane row
+//      (rows16_topk of topk_select.hpp); a row it leaves unresolved (ties at
+//      the threshold, many survivors) and every row for larger K take the
+//      exact one-row routine over the whole wavefront (wave_topk).
 #include "common.hpp"
 #include "launch.hpp"
 #include "topk_select.hpp"
@@ -27,13 +29,7 @@ namespace infllmv2 {
 namespace {
 
 constexpr int kDK = 128;
-
-__device__ __forceinline__ f32x16 max16(const f32x16& a, const f32x16& b) {
-  f32x16 r;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) r[e] = fmaxf(a[e], b[e]);
-  return r;
-}
+constexpr int kQPrefetchAhead = 64;   // items ahead whose Q rows a workgroup loads into L2
 
 __device__ __forceinline__ float pair_sum(float x) {   // lanes l and l ^ 32
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -42,132 +38,235 @@ __device__ __forceinline__ float pair_sum(float x) {   // lanes l and l ^ 32
 
 }  // namespace
 
-template <int G, int KPL>
+template <int G, int KPL, bool ROWSEL>
 __global__ __launch_bounds__(256, 2) void topk_prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kbar, int32_t* __restrict__ idx,
     int Hq, int Hkv, int n_q, int64_t q_pos0, int is_tree, int64_t nblk, int K, int ntile, int scs) {
-  constexpr int TQ = 64 / G;     // tokens per workgroup
+  constexpr int TQ = 64 / G;     // tokens per work item
   constexpr int TPS = 32 / G;    // tokens per 32-row sub-tile
   constexpr int DS = kDK / 16;   // k-steps
+  constexpr int SLAB = kKpb * kDK * 32;   // k-bar elements of one 32-block tile (3 kernels)
 
   extern __shared__ __align__(16) char smem[];
-  float* sc = reinterpret_cast<float*>(smem);    // [TQ][scs]
+  // [TQ][scs] order-preserving keys of the scores (ordered_key_nz: every sum
+  // starts from +0 or ends with + 0, so none is -0)
+  uint32_t* sc = reinterpret_cast<uint32_t*>(smem);
   __shared__ uint32_t scratch[4][2 * kWave];
+  __shared__ uint2 rbuf[ROWSEL ? 4 : 1][4][32];
+  __shared__ int32_t obuf[ROWSEL ? 4 : 1][4][16];
 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int l = lane_id();
   const int r32 = l % 32, hl = l / 32;
-  const int item = xcd_remap(blockIdx.x, gridDim.x);
-  const int tile = item % ntile;
-  const int bg = item / ntile;
-  const int b = bg / Hkv, g = bg % Hkv;
-  const int tok0 = tile * TQ;
-  const int ntok = min(TQ, n_q - tok0);
-  const int64_t pos_last = is_tree ? q_pos0 : q_pos0 + tok0 + ntok - 1;
-  const int64_t Cmax = min(pos_last / kBlock, nblk);
 
-  // ---------------------------------------------------------------- 1. scores
-  if (Cmax > K) {
-    // A operand: row 32*st + r32 of the tile (token row / G, head row % G),
-    // k-slots 8*hl .. 8*hl+7 of each 16-wide d step.
-    bf16x8 qa[2][DS];
+  const int it = xcd_remap(blockIdx.x, gridDim.x);
+
+  struct Item {
+    int bg, b, g, tok0, ntok;
+    int64_t Cmax;
+  };
+  auto item_of = [&](int i) {
+    Item c;
+    const int tile = i % ntile;
+    c.bg = i / ntile;
+    c.b = c.bg / Hkv;
+    c.g = c.bg % Hkv;
+    c.tok0 = tile * TQ;
+    c.ntok = min(TQ, n_q - c.tok0);
+    const int64_t pos_last = is_tree ? q_pos0 : q_pos0 + c.tok0 + c.ntok - 1;
+    c.Cmax = min(pos_last / kBlock, nblk);
+    return c;
+  };
+  // This wavefront's chunks of 32 blocks are w, w + 4, ...: its i-th is chunk
+  // w + 4i; nmine of them.
+  auto nmine_of = [&](const Item& c) { return (int((c.Cmax + 31) / 32) - w + 3) / 4; };
+
+  // A operand: row 32*st + r32 of the item (token row / G, head row % G),
+  // k-slots 8*hl .. 8*hl+7 of each 16-wide d step.
+  auto load_q = [&](const Item& c, bf16x8 (&qa)[2][DS]) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int row = 32 * st + r32;
       const int t = row / G;
-      const int h = g * G + row % G;
-      const uint16_t* qrow = q + ((int64_t(b) * Hq + h) * n_q + tok0 + (t < ntok ? t : 0)) * kDK + 8 * hl;
+      const int h = c.g * G + row % G;
+      const uint16_t* qrow = q + ((int64_t(c.b) * Hq + h) * n_q + c.tok0 + (t < c.ntok ? t : 0)) * kDK + 8 * hl;
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) qa[st][ds] = as_bf16x8(ldg16_if(t < ntok, qrow + 16 * ds));
+      for (int ds = 0; ds < DS; ++ds) qa[st][ds] = as_bf16x8(ldg16_if(t < c.ntok, qrow + 16 * ds));
     }
-    const int nchunk = int((Cmax + 31) / 32);
-    // This wavefront's chunks are w, w + 4, ...; step s is (chunk w + 4*(s/3),
-    // kernel s%3). B operand of a step: block 32*chunk + r32, d = 16*ds + 8*hl ..,
-    // i.e. piece 2*ds + hl: 32 consecutive blocks of one piece are contiguous.
-    const int nsteps = kKpb * ((nchunk - w + 3) / 4);
-    auto load_step = [&](int s, bf16x8 (&dst)[DS]) {
-      const int64_t blk = int64_t(w + 4 * (s / kKpb)) * 32 + r32;
-      const bool ok = blk < Cmax;
-      const int64_t jb = ok ? blk : 0;
+  };
+  // A step is (chunk, kernel m); its B operand, lane l: block 32*chunk + r32,
+  // d = 16*ds + 8*hl .., i.e. piece 2*ds + hl of the k-bar tile (layout
+  // [bg][tile][m][piece][32][8]): a wave-uniform base plus a per-lane offset.
+  // A prefetch past the last step is clamped to the last chunk; blocks past
+  // Cmax in the last chunk are in the table (whole tiles of 32) and their
+  // scores are never selected.
+  auto load_step = [&](const Item& c, int nm, int i, int m, bf16x8 (&dst)[DS]) {
+    const int ch = w + 4 * min(i, nm - 1);
+    const uint16_t* p = kbar + int64_t(c.bg) * ((nblk + 31) >> 5) * SLAB +
+                        (int64_t(ch) * kKpb + m) * (kDK * 32) + (hl * 32 + r32) * 8;
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds)
-        dst[ds] = as_bf16x8(ldg16_if(ok, kbar + kbar_off<kDK>(bg, s % kKpb, 2 * ds + hl, jb, nblk)));
-    };
-    // Accumulator register r of lane l: tile row 32*st + 8*(r/4) + 4*hl + r%4,
-    // block 32*chunk + r32. Max over the kernels; after the last, head sums
-    // and the store.
-    f32x16 best[2];
-    auto compute_step = [&](int s, const bf16x8 (&kf)[DS]) {
-      const int m = s % kKpb;
-      const int blk = (w + 4 * (s / kKpb)) * 32 + r32;
+    for (int ds = 0; ds < DS; ++ds) dst[ds] = as_bf16x8(ldg16(p + ds * 512));
+  };
+
+  bf16x8 qa[2][DS], kfa[DS], kfb[DS];
+  const Item cur = item_of(it);
+  if (cur.Cmax > K) {
+    load_q(cur, qa);
+    if (nmine_of(cur) > 0) load_step(cur, nmine_of(cur), 0, 0, kfa);
+  }
+  {
+    // ------------------------------------------------------------ 1. scores
+    // (the item's Q rows and its first k-bar step are already in flight)
+    const int nmine = nmine_of(cur);
+    if (cur.Cmax > K && nmine > 0) {
+      // Accumulator register r of lane l: item row 32*st + 8*(r/4) + 4*hl +
+      // r%4, block 32*chunk + r32. Max over the kernels; after the last, head
+      // sums and the store.
+      f32x16 best[2];
+      auto compute_step = [&](int i, int m, const bf16x8 (&kf)[DS]) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        f32x16 acc;
+        for (int st = 0; st < 2; ++st) {
+          f32x16 acc;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+          for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 #pragma unroll
-        for (int ds = 0; ds < DS; ++ds) acc = mfma32(qa[st][ds], kf[ds], acc);
-        best[st] = m == 0 ? acc : max16(best[st], acc);
-      }
-      if (m != kKpb - 1) return;
+          for (int ds = 0; ds < DS; ++ds) acc = mfma32(qa[st][ds], kf[ds], acc);
+          if (m == 0) {
+            best[st] = acc;
+          } else {
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        if constexpr (G <= 4) {
+            for (int e = 0; e < 16; ++e) best[st][e] = fmax_nq(best[st][e], acc[e]);
+          }
+        }
+        if (m != kKpb - 1) return;
+        // Token row of register group a (and head pair u): st*TPS + 8a/G + u,
+        // plus 4*hl/G for G <= 4; this lane's column 32*chunk + r32.
+        const uint32_t srow = uint32_t(G <= 4 ? (4 * hl / G) * scs + r32 : r32) + uint32_t((w + 4 * i) * 32);
 #pragma unroll
-          for (int a = 0; a < 4; ++a)
+        for (int st = 0; st < 2; ++st) {
+          if constexpr (G <= 4) {
 #pragma unroll
-            for (int u = 0; u < 4 / G; ++u) {
-              float sum = 0.f;
+            for (int a = 0; a < 4; ++a)
 #pragma unroll
-              for (int v = 0; v < G; ++v) sum += best[st][4 * a + G * u + v];
-              const int tk = st * TPS + (8 * a + 4 * hl + G * u) / G;
-              sc[tk * scs + blk] = sum;
-            }
-        } else {
-          float s4[4];
+              for (int u = 0; u < 4 / G; ++u) {
+                float sum = 0.f;
 #pragma unroll
-          for (int a = 0; a < 4; ++a)
-            s4[a] = pair_sum(best[st][4 * a] + best[st][4 * a + 1] + best[st][4 * a + 2] + best[st][4 * a + 3]);
-          if (hl == 0) {
-            if constexpr (G == 8) {
+                for (int v = 0; v < G; ++v) sum += best[st][4 * a + G * u + v];
+                sc[srow + (st * TPS + 8 * a / G + u) * scs] = ordered_key_nz(sum);
+              }
+          } else {
+            float s4[4];
 #pragma unroll
-              for (int a = 0; a < 4; ++a) sc[(st * TPS + a) * scs + blk] = s4[a];
-            } else {
+            for (int a = 0; a < 4; ++a)
+              s4[a] = pair_sum(best[st][4 * a] + best[st][4 * a + 1] + best[st][4 * a + 2] + best[st][4 * a + 3]);
+            if (hl == 0) {
+              if constexpr (G == 8) {
 #pragma unroll
-              for (int a = 0; a < 2; ++a) sc[(st * TPS + a) * scs + blk] = s4[2 * a] + s4[2 * a + 1];
+                for (int a = 0; a < 4; ++a) sc[srow + (st * TPS + a) * scs] = ordered_key_nz(s4[a] + 0.f);
+              } else {
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+                  sc[srow + (st * TPS + a) * scs] = ordered_key_nz(s4[2 * a] + s4[2 * a + 1] + 0.f);
+              }
             }
           }
         }
+      };
+
+      // The next step's fragments load while one step computes; two chunks
+      // (six steps) per iteration keep the two fragment buffers in place.
+      for (int i = 0; i < nmine; i += 2) {
+        load_step(cur, nmine, i, 1, kfb);
+        compute_step(i, 0, kfa);
+        load_step(cur, nmine, i, 2, kfa);
+        compute_step(i, 1, kfb);
+        load_step(cur, nmine, i + 1, 0, kfb);
+        compute_step(i, 2, kfa);
+        if (i + 1 >= nmine) break;
+        load_step(cur, nmine, i + 1, 1, kfa);
+        compute_step(i + 1, 0, kfb);
+        load_step(cur, nmine, i + 1, 2, kfb);
+        compute_step(i + 1, 1, kfa);
+        load_step(cur, nmine, i + 2, 0, kfa);
+        compute_step(i + 1, 2, kfb);
       }
-    };
-
-    // The next step's fragments load while one step computes. The loads are
-    // issued unconditionally (a step past the end maps to blocks >= Cmax and
-    // reads zeros): behind a branch, the wait placed before the current
-    // step's MFMAs would also cover the prefetch.
-    bf16x8 kfa[DS], kfb[DS];
-    load_step(0, kfa);
-    for (int s = 0; s < nsteps; s += 2) {
-      load_step(s + 1, kfb);
-      compute_step(s, kfa);
-      if (s + 1 >= nsteps) break;
-      load_step(s + 2, kfa);
-      compute_step(s + 1, kfb);
     }
-  }
-  __syncthreads();
+    // Warm the L2 with the Q rows of the item that a workgroup of this XCD
+    // starts about one wave of workgroups later (the grid numbering gives each
+    // XCD a contiguous item range, and 256 CUs x 2 resident workgroups are 64
+    // per XCD): the lines arrive during this item's selection, and that item's
+    // own Q loads, otherwise a full HBM latency at its start, then hit. One
+    // dword per 128-byte line: item row (64*w + l) / 2, half (64*w + l) % 2.
+    uint32_t pf = 0u;
+    if (w < 2) {
+      const int pit = it + kQPrefetchAhead;
+      const Item pc = item_of(pit < int(gridDim.x) ? pit : it);
+      const int k = w * kWave + l;
+      const int row = k / 2, t = row / G;
+      pf = *reinterpret_cast<const uint32_t*>(
+          q + ((int64_t(pc.b) * Hq + pc.g * G + row % G) * n_q + pc.tok0 + (t < pc.ntok ? t : 0)) * kDK + (k % 2) * 64);
+    }
+    lds_barrier();    // the item's scores are in LDS
 
-  // ---------------------------------------------------------------- 2. selection
-  for (int t = w; t < ntok; t += 4) {
-    const int64_t pos = is_tree ? q_pos0 : q_pos0 + tok0 + t;
-    const int C = int(min(pos / kBlock, nblk));
-    uint32_t key[KPL];
+    // ---------------------------------------------------------- 2. selection
+    const int64_t Cmax = cur.Cmax;
+    const int tok0 = cur.tok0, ntok = cur.ntok, bg = cur.bg;
+    if constexpr (ROWSEL) {
+      // Four tokens per wavefront and pass, one per 16-lane row
+      // (rows16_topk); rows it leaves unresolved go to the exact one-row
+      // routine with the whole wavefront.
+      const int rq = l >> 4, rl = l & 15;
+      const int ng = int((Cmax + 63) / 64);
+      for (int tb = 4 * w; tb < ntok; tb += 16) {
+        const int t = tb + rq;
+        const bool act = t < ntok;
+        const int64_t pos = is_tree ? q_pos0 : q_pos0 + tok0 + (act ? t : tb);
+        const int C = act ? int(min(pos / kBlock, nblk)) : 0;
+        uint32_t* row = sc + (act ? t : tb) * scs;
+        // Entries C .. 64*ng - 1 (later blocks, or never written) read as
+        // key 0. The tokens of one item are < 64 positions apart, so
+        // C >= Cmax - 1 and there are at most 64 of them.
+        if (act && Cmax > K) {
 #pragma unroll
-    for (int r = 0; r < KPL; ++r) {
-      const int j = r * kWave + l;
-      key[r] = (C > K && j < C) ? ordered_key(sc[t * scs + j]) : 0u;
+          for (int u = 0; u < 4; ++u) {
+            const int j = C + rl + 16 * u;
+            if (j < 64 * ng) row[j] = 0u;
+          }
+        }
+        int32_t* out = act ? idx + (int64_t(bg) * n_q + tok0 + t) * K : nullptr;
+        const bool ok = rows16_topk<KPL>(row, ng, C, K, out, rbuf[w][rq], obuf[w][rq]);
+        uint64_t bad = ballot64(!ok && rl == 0);
+        while (bad) {
+          const int qq = __builtin_ctzll(bad) / 16;
+          bad &= bad - 1;
+          const int tt = tb + qq;
+          const int64_t pp = is_tree ? q_pos0 : q_pos0 + tok0 + tt;
+          const int Ct = int(min(pp / kBlock, nblk));
+          uint32_t key[KPL];
+#pragma unroll
+          for (int r = 0; r < KPL; ++r) {
+            const int j = r * kWave + l;
+            key[r] = j < Ct ? sc[tt * scs + j] : 0u;
+          }
+          wave_topk<KPL>(key, Ct, K, idx + (int64_t(bg) * n_q + tok0 + tt) * K, scratch[w]);
+        }
+      }
+    } else {
+      for (int t = w; t < ntok; t += 4) {
+        const int64_t pos = is_tree ? q_pos0 : q_pos0 + tok0 + t;
+        const int C = int(min(pos / kBlock, nblk));
+        uint32_t key[KPL];
+#pragma unroll
+        for (int r = 0; r < KPL; ++r) {
+          const int j = r * kWave + l;
+          key[r] = (C > K && j < C) ? sc[t * scs + j] : 0u;
+        }
+        wave_topk<KPL>(key, C, K, idx + (int64_t(bg) * n_q + tok0 + t) * K, scratch[w]);
+      }
     }
-    wave_topk<KPL>(key, C, K, idx + (int64_t(bg) * n_q + tok0 + t) * K, scratch[w]);
+    // The prefetched dword is not used; an empty asm consumes it so that the
+    // load stays (the wave ends only after it has returned).
+    asm volatile("" ::"v"(pf));
   }
 }
 
@@ -197,13 +296,13 @@ bool topk_prefill128_ok(const Dims& d, int64_t cmax) {
   return topk_prefill_plan(d, cmax).lds <= 64 * 1024;
 }
 
-template <int G, int KPL>
+template <int G, int KPL, bool ROWSEL>
 static hipError_t launch_topk_prefill_t(const Dims& d, const uint16_t* q, const uint16_t* kbar,
                                         int n_q, int64_t q_pos0, int is_tree, int64_t nblk,
                                         int scs, int32_t* idx, hipStream_t s) {
   constexpr int TQ = 64 / G;
   const int ntile = (n_q + TQ - 1) / TQ;
-  auto kern = topk_prefill_kernel<G, KPL>;
+  auto kern = topk_prefill_kernel<G, KPL, ROWSEL>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      64 * 1024);
@@ -219,11 +318,14 @@ static hipError_t launch_topk_prefill_g(const Dims& d, const uint16_t* q, const 
                                         int n_q, int64_t q_pos0, int is_tree, int64_t nblk,
                                         int64_t cmax, int32_t* idx, hipStream_t s) {
   const TopkPrefillPlan p = topk_prefill_plan(d, cmax);
+  const bool rowsel = d.K <= 16;
+#define TP_CASE(P)                                                                                  \
+  case P:                                                                                           \
+    return rowsel ? launch_topk_prefill_t<G, P, true>(d, q, kbar, n_q, q_pos0, is_tree, nblk, p.scs, idx, s) \
+                  : launch_topk_prefill_t<G, P, false>(d, q, kbar, n_q, q_pos0, is_tree, nblk, p.scs, idx, s);
   switch (p.kpl) {
-    case 1: return launch_topk_prefill_t<G, 1>(d, q, kbar, n_q, q_pos0, is_tree, nblk, p.scs, idx, s);
-    case 2: return launch_topk_prefill_t<G, 2>(d, q, kbar, n_q, q_pos0, is_tree, nblk, p.scs, idx, s);
-    case 4: return launch_topk_prefill_t<G, 4>(d, q, kbar, n_q, q_pos0, is_tree, nblk, p.scs, idx, s);
-    case 8: return launch_topk_prefill_t<G, 8>(d, q, kbar, n_q, q_pos0, is_tree, nblk, p.scs, idx, s);
+    TP_CASE(1) TP_CASE(2) TP_CASE(4) TP_CASE(8)
+#undef TP_CASE
     default: return hipErrorInvalidValue;
   }
 }

@@ -413,4 +413,183 @@ __device__ __forceinline__ void wg_topk8(const float* __restrict__ row, int64_t 
   wave_topk_lc<SKPL>(all, n, K, out, scratch);
 }
 
+// ------------------------------------------------------- one row per 16 lanes
+// Top-K (K <= 16) of four score rows at once, one per 16-lane row of the
+// wavefront (row q = lanes 16q .. 16q+15). Every cross-lane step stays inside
+// a 16-lane row (DPP), so the four rows share each instruction.
+//
+// The rows hold order-preserving score keys, 0 past the row's candidates.
+// Lane r of a row holds candidates 64g + 4r + e (g < ng, e < 4): a 16-byte LDS
+// read per group, and every lane holds candidates as soon as n >= 64.
+//   1. bound: each lane keeps its two largest keys; the K-th largest T0 of
+//      those 32 is a lower bound of the row's K-th largest key (K distinct
+//      candidates are >= T0), so every chosen candidate, and every candidate
+//      tied with the K-th, is >= T0. (With fewer than K candidates among them,
+//      T0 is 0 and every candidate survives.)
+//   2. survivors (usually 16-24): compacted into 32 LDS slots per row;
+//   3. threshold: the K-th largest key T among the survivors (two 16-lane
+//      bitonic sorts and their elementwise max = the 16 largest of 32);
+//   4. emit: when exactly K survivors are >= T the row's choice is these,
+//      written ascending after one more 16-lane sort of their indices.
+// A row with more than 32 survivors, or with more survivors equal to T than
+// the K-th place can take (ties that the lower index must break), is left
+// unresolved for the exact one-row routine (wave_topk).
+//
+// Row of 16 lanes: the value of lane l ^ J (J < 16) of the same row.
+template <int J>
+__device__ __forceinline__ uint32_t row_xor(uint32_t v, int rl) {
+  if constexpr (J == 8) {
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x128, 0xF, 0xF, false));  // row_ror:8
+  } else {
+    return xor_lane<J>(v, rl);
+  }
+}
+
+// Bitonic stage inside a 16-lane row; runs of KS lanes end descending when
+// `desc` (ascending otherwise) at KS = 16, alternating below.
+template <int KS, int J>
+__device__ __forceinline__ uint32_t row_cex(uint32_t v, int rl, bool desc) {
+  const uint32_t p = row_xor<J>(v, rl);
+  const bool lower = (rl & J) == 0;
+  const bool d = ((rl & KS) == 0) == desc;
+  return lower == d ? max(v, p) : min(v, p);
+}
+
+__device__ __forceinline__ uint32_t row_sort16(uint32_t v, int rl, bool desc) {
+  v = row_cex<2, 1>(v, rl, desc);
+  v = row_cex<4, 2>(v, rl, desc);   v = row_cex<4, 1>(v, rl, desc);
+  v = row_cex<8, 4>(v, rl, desc);   v = row_cex<8, 2>(v, rl, desc);   v = row_cex<8, 1>(v, rl, desc);
+  v = row_cex<16, 8>(v, rl, desc);  v = row_cex<16, 4>(v, rl, desc);  v = row_cex<16, 2>(v, rl, desc);
+  v = row_cex<16, 1>(v, rl, desc);
+  return v;
+}
+
+// A bitonic 16-lane row -> descending.
+__device__ __forceinline__ uint32_t row_merge16_desc(uint32_t v, int rl) {
+  v = row_cex<16, 8>(v, rl, true);  v = row_cex<16, 4>(v, rl, true);
+  v = row_cex<16, 2>(v, rl, true);  v = row_cex<16, 1>(v, rl, true);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t row_min16(uint32_t v, int rl) {
+  v = min(v, row_xor<1>(v, rl));
+  v = min(v, row_xor<2>(v, rl));
+  v = min(v, row_xor<4>(v, rl));
+  return min(v, row_xor<8>(v, rl));
+}
+
+__device__ __forceinline__ uint32_t row_sum16(uint32_t v, int rl) {
+  v += row_xor<1>(v, rl);
+  v += row_xor<2>(v, rl);
+  v += row_xor<4>(v, rl);
+  return v + row_xor<8>(v, rl);
+}
+
+__device__ __forceinline__ uint32_t row_incl_scan16(uint32_t v) {
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x111, 0xF, 0xF, true));   // row_shr:1
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x112, 0xF, 0xF, true));   // row_shr:2
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x114, 0xF, 0xF, true));   // row_shr:4
+  v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x118, 0xF, 0xF, true));   // row_shr:8
+  return v;
+}
+
+// Lane rl = i of this lane's row.
+__device__ __forceinline__ uint32_t row_lane(uint32_t v, int l, int i) {
+  return uint32_t(__shfl(int(v), (l & 48) | i));
+}
+
+// max / median of fp32 without the NaN quieting fmaxf carries (scores are
+// never NaN): v_max_f32.
+__device__ __forceinline__ float fmax_nq(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, INFINITY); }
+
+// Order-preserving key of a score that is not -0 (a sum that started from +0):
+// larger float -> larger key, -inf -> 0x007FFFFF, so key 0 is below every score.
+__device__ __forceinline__ uint32_t ordered_key_nz(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return u ^ (uint32_t(int32_t(u) >> 31) | 0x80000000u);
+}
+
+__device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
+  return max(min(a, b), min(max(a, b), c));
+}
+
+// `row`: this lane's row of score keys (ordered_key) in LDS, 16-byte aligned,
+// 64*ng entries, those j >= n holding 0. `n`: candidates of the row;
+// 1 <= K <= 16 (wave-uniform). `out`: the row's K outputs, or null for a row
+// that writes nothing. `buf` (32 pairs) and `obuf` (16 ints): LDS private to
+// the row. Every lane of the wavefront calls it; returns whether this lane's
+// row is resolved (rows with n <= K always are: all taken, -1 padded).
+template <int NG>
+__device__ __forceinline__ bool rows16_topk(const uint32_t* __restrict__ row, int ng, int n, int K,
+                                            int32_t* __restrict__ out, uint2* buf, int32_t* obuf) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const int l = lane_id();
+  const int rl = l & 15;
+  // 1. per-lane two largest, then the bound T0
+  u32x4 v[NG];
+  uint32_t m1 = 0u, m2 = 0u;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    v[g] = g < ng ? *reinterpret_cast<const u32x4*>(row + 64 * g + 4 * rl) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      m2 = umed3(m1, m2, v[g][e]);
+      m1 = max(m1, v[g][e]);
+    }
+  }
+  const uint32_t a = row_sort16(m1, rl, true);
+  const uint32_t b = row_sort16(m2, rl, false);
+  const uint32_t c = max(a, b);                  // the 16 largest of the 32, bitonic
+  uint32_t t0 = K < 16 ? row_lane(row_merge16_desc(c, rl), l, K - 1) : row_min16(c, rl);
+  t0 = max(t0, 1u);                              // padding (key 0) never survives
+
+  // 2. survivors
+  uint32_t mask = 0u;
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mask |= (v[g][e] >= t0 ? 1u : 0u) << (4 * g + e);
+  const uint32_t cnt = __popc(mask);
+  const uint32_t incl = row_incl_scan16(cnt);
+  const uint32_t total = row_lane(incl, l, 15);
+  const bool trivial = n <= K;
+  if (trivial || total > 32u) mask = 0u;
+  uint32_t pos = incl - cnt;
+  while (ballot64(mask != 0u)) {
+    if (mask != 0u) {
+      const int bit = __builtin_ctz(mask);
+      const int j = (bit >> 2) * 64 + 4 * rl + (bit & 3);
+      buf[pos] = make_uint2(row[j], uint32_t(j));
+      ++pos;
+      mask &= mask - 1u;
+    }
+  }
+
+  // 3. threshold among the survivors (keys of empty slots are 0, below all)
+  const bool va = uint32_t(rl) < total, vb = uint32_t(rl) + 16u < total;
+  const uint2 ea = va ? buf[rl] : make_uint2(0u, 0u);
+  const uint2 eb = vb ? buf[rl + 16] : make_uint2(0u, 0u);
+  const uint32_t sa = row_sort16(ea.x, rl, true);
+  const uint32_t sb = row_sort16(eb.x, rl, false);
+  const uint32_t c2 = max(sa, sb);
+  const uint32_t T = K < 16 ? row_lane(row_merge16_desc(c2, rl), l, K - 1) : row_min16(c2, rl);
+  const uint32_t ta = ea.x >= T ? 1u : 0u, tb = eb.x >= T ? 1u : 0u;
+  const uint32_t nge = row_sum16(ta + tb, rl);
+  const bool resolved = trivial || (total <= 32u && nge == uint32_t(K));
+
+  // 4. emit ascending
+  const uint32_t tin = row_incl_scan16(ta + tb);
+  const uint32_t p = tin - ta - tb;
+  if (resolved && !trivial) {
+    if (ta) obuf[p] = int32_t(ea.y);
+    if (tb) obuf[p + ta] = int32_t(eb.y);
+  }
+  const uint32_t o = row_sort16(rl < K ? uint32_t(obuf[rl]) : 0x7FFFFFFFu, rl, false);
+  if (out != nullptr && rl < K) {
+    if (trivial) out[rl] = rl < n ? rl : -1;
+    else if (resolved) out[rl] = int32_t(o);
+  }
+  return resolved;
+}
+
 }  // namespace infllmv2
