@@ -480,30 +480,53 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
           make_float4(oacc[s][dt][0], oacc[s][dt][1], oacc[s][dt][2], oacc[s][dt][3]);
   }
   __syncthreads();
-  // Merge the wavefronts by log-sum-exp; thread t takes (row, column) pairs.
+  // Merge the wavefronts by log-sum-exp. A thread takes 4-column units (row
+  // wr, columns c .. c+3) and issues all of a unit's LDS reads (every
+  // wavefront's (m, l) and O values) before it uses any of them; the sums run
+  // over the wavefronts in order.
+  constexpr int MAXW = NSTD == 1 ? kMaxWaves : kMaxWaves2;
+  constexpr int U4 = D / 4;
   const bool final = nsplit == 1;
-  for (int e = threadIdx.x; e < WR * D; e += blockDim.x) {
-    const int wr = e / D, c = e % D;
+  for (int unit = threadIdx.x; unit < WR * U4; unit += blockDim.x) {
+    const int wr = unit / U4, c = (unit % U4) * 4;
     const int row = row0 + wr;
     if (row >= rows) continue;
+    float2 ml[MAXW];
+    f32x4 ov[MAXW];
+#pragma unroll
+    for (int x = 0; x < MAXW; ++x) {
+      if (x < nwv) {
+        ml[x] = s_ml[x][wr];
+        ov[x] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(dsm + x * kBlock * D) + wr * D + c);
+      }
+    }
     float M = -INFINITY;
-    for (int x = 0; x < nwv; ++x) M = fmaxf(M, s_ml[x][wr].x);
-    float Lsum = 0.f, acc = 0.f;
-    for (int x = 0; x < nwv; ++x) {
-      const float2 ml = s_ml[x][wr];
-      const float wgt = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
-      Lsum += wgt * ml.y;
-      acc += wgt * reinterpret_cast<const float*>(dsm + x * kBlock * D)[wr * D + c];
+#pragma unroll
+    for (int x = 0; x < MAXW; ++x)
+      if (x < nwv) M = fmaxf(M, ml[x].x);
+    float Lsum = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int x = 0; x < MAXW; ++x) {
+      if (x < nwv) {
+        const float wgt = ml[x].x == -INFINITY ? 0.f : exp2f(ml[x].x - M);
+        Lsum += wgt * ml[x].y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += wgt * ov[x][i];
+      }
     }
     if (final) {
       const int node = row / G, hh = row % G;
       const int64_t rid = (int64_t(b) * Hq + g * G + hh) * n_q + node;
-      out[rid * D + c] = f2bf(Lsum > 0.f ? acc / Lsum : 0.f);
+      uint2 uu;
+      uu.x = uint32_t(f2bf(Lsum > 0.f ? acc[0] / Lsum : 0.f)) | (uint32_t(f2bf(Lsum > 0.f ? acc[1] / Lsum : 0.f)) << 16);
+      uu.y = uint32_t(f2bf(Lsum > 0.f ? acc[2] / Lsum : 0.f)) | (uint32_t(f2bf(Lsum > 0.f ? acc[3] / Lsum : 0.f)) << 16);
+      *reinterpret_cast<uint2*>(out + rid * D + c) = uu;
       if (lse && c == 0) lse[rid] = (M + log2f(Lsum)) * 0.69314718055994531f;
     } else {
       // partials: ml[bg][split][row] = (m, l); o[bg][split][row][d] (unnormalized)
       const int64_t pr = (int64_t(bg) * nsplit + split) * rows + row;
-      part_o[pr * D + c] = acc;
+      *reinterpret_cast<f32x4*>(part_o + pr * D + c) = acc;
       if (c == 0) {
         part_ml[pr * 2 + 0] = M;
         part_ml[pr * 2 + 1] = Lsum;
