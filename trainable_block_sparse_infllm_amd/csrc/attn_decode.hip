@@ -210,7 +210,7 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
     const int32_t* __restrict__ u_count, float* __restrict__ part_ml, float* __restrict__ part_o,
     uint16_t* __restrict__ out, float* __restrict__ lse, int Hq, int Hkv, int G, int n_q,
     int64_t kv_cap, int64_t kv_len, int K, int dense_thr, int is_tree, int sb, int nsplit,
-    int max_e, int rows, float scale_log2, const float* __restrict__ scores, int64_t nblk,
+    int nsg, int max_e, int rows, float scale_log2, const float* __restrict__ scores, int64_t nblk,
     int32_t* __restrict__ idx_out, const int64_t* __restrict__ kv_lens) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
@@ -222,9 +222,12 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
   uint16_t* vt = dsm + w * kBlock * D;
   const int l = lane_id();
   const int r16 = l % 16, kg = l / 16;
+  // The grid holds nsg splits per (b, g) (nsg < nsplit only for multi-row
+  // calls, whose union size is known on the device alone); a workgroup takes
+  // splits split0, split0 + nsg, ... while they hold union entries.
   const int item = xcd_remap(blockIdx.x, gridDim.x);
-  const int split = item % nsplit;
-  const int bg = item / nsplit;
+  const int split0 = item % nsg;
+  const int bg = item / nsg;
   const int b = bg / Hkv, g = bg % Hkv;
   const int row0 = blockIdx.y * 16 * NSTD;
   // per-sequence length (single-token rows), kept within 1 .. the bound the
@@ -244,13 +247,11 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
   } else {
     n_e = u_count[bg];
   }
-  const int u0 = split * sb;
-  const int u1 = min(u0 + sb, n_e);
   // A multi-row call sizes its splits for the largest possible union, and its
   // combine reads only the splits that hold entries (u_count): a split past
   // the union has nothing to write. (Single-token rows keep every split: their
   // combine reads all of them.)
-  if (n_q > 1 && nsplit > 1 && u0 >= n_e) return;
+  if (n_q > 1 && nsplit > 1 && split0 * sb >= n_e) return;
 
   // block list of a single-token row selected here from its scores
   __shared__ int32_t s_sel[SKPL > 0 ? 64 : 1];
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
       wave_topk_lc<SKPL>(val, C, K, s_sel, s_scr);
     }
     lds_barrier();
-    if (w == 0 && split == 0 && idx_out)
+    if (w == 0 && split0 == 0 && idx_out)
       for (int t = l; t < K; t += kWave) idx_out[int64_t(bg) * K + t] = s_sel[t];
   }
 
@@ -314,224 +315,233 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
     }
   }
 
-  f32x4 oacc[NSTD][DT];
-  float m_run[NSTD], l_run[NSTD];
-#pragma unroll
-  for (int s = 0; s < NSTD; ++s) {
-    m_run[s] = -INFINITY;
-    l_run[s] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[s][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  for (int u = u0 + w; u < u1; u += nwv) {
-    int64_t j;
-    uint64_t nmask;
-    if (n_q == 1) {
-      j = dense1 ? u : (u < K ? (SKPL > 0 ? s_sel[u] : idx[int64_t(bg) * K + u]) : own1);
-      if (!dense1 && u < K && (j < 0 || j >= own1)) continue;
-      nmask = 1ull;
-    } else {
-      j = u_blk[int64_t(bg) * max_e + u];
-      nmask = u_mask[int64_t(bg) * max_e + u];
-    }
-    const int64_t key0 = j * kBlock;
-
-    wait_lds();                                    // previous block's V reads are done
-    load_v_tile<D>(vbase, key0, kv_len, vt);       // V -> LDS, no registers
-    // K fragments straight from HBM: lane feeds key 16*kt + r16, d = 32*ks + 8*kg .. +7
-    bf16x8 kf[4][KS];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int64_t key = key0 + kt * 16 + r16;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kf[kt][ks] = as_bf16x8(ldg16_nt(key < kv_len ? static_cast<const void*>(kbase + key * D + ks * 32 + kg * 8)
-                                                     : static_cast<const void*>(kZeroPiece)));
-    }
-
-    bool sub_on[NSTD], row_on[NSTD];
+  // (Only two-sub-tile instances loop: a loop around the single-sub-tile
+  // kernels, which run nine wavefronts at 168 registers, makes them spill.)
+  constexpr bool kLoop = NSTD > 1;
+  for (int split = split0;; split += nsg) {
+    const int u0 = split * sb;
+    const int u1 = min(u0 + sb, n_e);
+    f32x4 oacc[NSTD][DT];
+    float m_run[NSTD], l_run[NSTD];
 #pragma unroll
     for (int s = 0; s < NSTD; ++s) {
-      row_on[s] = node_of[s] >= 0 && ((nmask >> node_of[s]) & 1ull);
-      sub_on[s] = ballot64(row_on[s]) != 0ull;
-    }
-    f32x4 sacc[NSTD][4];
+      m_run[s] = -INFINITY;
+      l_run[s] = 0.f;
 #pragma unroll
-    for (int s = 0; s < NSTD; ++s) {
-      if (!sub_on[s]) continue;
+      for (int dt = 0; dt < DT; ++dt) oacc[s][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    for (int u = u0 + w; u < u1; u += nwv) {
+      int64_t j;
+      uint64_t nmask;
+      if (n_q == 1) {
+        j = dense1 ? u : (u < K ? (SKPL > 0 ? s_sel[u] : idx[int64_t(bg) * K + u]) : own1);
+        if (!dense1 && u < K && (j < 0 || j >= own1)) continue;
+        nmask = 1ull;
+      } else {
+        j = u_blk[int64_t(bg) * max_e + u];
+        nmask = u_mask[int64_t(bg) * max_e + u];
+      }
+      const int64_t key0 = j * kBlock;
+
+      wait_lds();                                    // previous block's V reads are done
+      load_v_tile<D>(vbase, key0, kv_len, vt);       // V -> LDS, no registers
+      // K fragments straight from HBM: lane feeds key 16*kt + r16, d = 32*ks + 8*kg .. +7
+      bf16x8 kf[4][KS];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+        const int64_t key = key0 + kt * 16 + r16;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) a = mfma16(kf[kt][ks], qf[s][ks], a);
-        sacc[s][kt] = a;
+        for (int ks = 0; ks < KS; ++ks)
+          kf[kt][ks] = as_bf16x8(ldg16_nt(key < kv_len ? static_cast<const void*>(kbase + key * D + ks * 32 + kg * 8)
+                                                       : static_cast<const void*>(kZeroPiece)));
+      }
+
+      bool sub_on[NSTD], row_on[NSTD];
+#pragma unroll
+      for (int s = 0; s < NSTD; ++s) {
+        row_on[s] = node_of[s] >= 0 && ((nmask >> node_of[s]) & 1ull);
+        sub_on[s] = ballot64(row_on[s]) != 0ull;
+      }
+      f32x4 sacc[NSTD][4];
+#pragma unroll
+      for (int s = 0; s < NSTD; ++s) {
+        if (!sub_on[s]) continue;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) a = mfma16(kf[kt][ks], qf[s][ks], a);
+          sacc[s][kt] = a;
+        }
+      }
+      bf16x8 pf[NSTD][2];
+#pragma unroll
+      for (int s = 0; s < NSTD; ++s) {
+        if (!sub_on[s]) continue;
+        const int node = node_of[s];
+        const int64_t p_row = P + (node < 0 ? 0 : node);
+        float mb = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t key = key0 + kt * 16 + kg * 4 + i;
+            bool ok;
+            if (is_tree)
+              ok = key < P || (key < kv_len && ((tmask[s] >> (key - P)) & 1ull));
+            else
+              ok = key <= p_row;
+            const float x = (row_on[s] && ok) ? sacc[s][kt][i] * scale_log2 : -INFINITY;
+            sacc[s][kt][i] = x;
+            mb = fmaxf(mb, x);
+          }
+        mb = rows4_max(mb);
+        const float m_new = fmaxf(m_run[s], mb);
+        const bool none = m_new == -INFINITY;
+        const float alpha = none ? 1.f : exp2f(m_run[s] - m_new);
+        const float neg_m = none ? 0.f : -m_new;    // masked keys: exp2(-inf) = 0
+        float ps = 0.f;
+        float pv[4][4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float e = __builtin_amdgcn_exp2f(sacc[s][kt][i] + neg_m);
+            pv[kt][i] = e;
+            ps += e;
+          }
+        ps = rows4_sum(ps);
+        l_run[s] = l_run[s] * alpha + ps;
+        m_run[s] = m_new;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) oacc[s][dt][i] *= alpha;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          uint4 uu;
+          uu.x = cvt_pk_bf16(pv[2 * k2][0], pv[2 * k2][1]);
+          uu.y = cvt_pk_bf16(pv[2 * k2][2], pv[2 * k2][3]);
+          uu.z = cvt_pk_bf16(pv[2 * k2 + 1][0], pv[2 * k2 + 1][1]);
+          uu.w = cvt_pk_bf16(pv[2 * k2 + 1][2], pv[2 * k2 + 1][3]);
+          pf[s][k2] = as_bf16x8(uu);
+        }
+      }
+      wait_vmem();                                   // the V tile has landed in LDS
+      if constexpr (D == 128) {
+        // byte offset of lane (r16, kg)'s chunk for d tile 0, rows 4*kg + r16/4
+        const int v_row = 4 * kg + r16 / 4;
+        const int v_lane = v_row * (D * 2) + ((((r16 % 4) >> 1) ^ vswz(v_row)) << 4) + 8 * (r16 & 1);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const int off = k2 * 32 * D * 2 + (v_lane ^ (dt << 5));
+            const bf16x8 vf = read_vt_tr(vt, off, off + 16 * D * 2);
+#pragma unroll
+            for (int s = 0; s < NSTD; ++s) {
+              if (!sub_on[s]) continue;
+              oacc[s][dt] = mfma16(vf, pf[s][k2], oacc[s][dt]);
+            }
+          }
+        }
+      } else {
+        const uint16_t* vlane = vt + 4 * kg * D + r16;  // key 4*kg, column r16 (swizzle applied per dt)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const uint16_t* vcol = vlane + ((dt ^ kg) << 4);
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            // key slots (kg, jj): key = 32*k2 + 16*(jj/4) + 4*kg + jj%4, matching pf's packing
+            uint32_t w4[4];
+#pragma unroll
+            for (int hp = 0; hp < 4; ++hp) {
+              const int koff = 32 * k2 + 16 * (hp / 2) + 2 * (hp % 2);   // jj = 2*hp
+              const uint32_t lo = vcol[koff * D];
+              const uint32_t hi = vcol[(koff + 1) * D];
+              w4[hp] = lo | (hi << 16);
+            }
+            const bf16x8 vf = as_bf16x8(uint4{w4[0], w4[1], w4[2], w4[3]});
+#pragma unroll
+            for (int s = 0; s < NSTD; ++s) {
+              if (!sub_on[s]) continue;
+              oacc[s][dt] = mfma16(vf, pf[s][k2], oacc[s][dt]);
+            }
+          }
+        }
       }
     }
-    bf16x8 pf[NSTD][2];
+
+    // This wavefront's partial -> LDS: (m, l) per row, O (unnormalized, zeros
+    // for rows that saw no key) in the wavefront's V tile, [row][D] fp32.
+    wait_lds();
+    float* o_s = reinterpret_cast<float*>(vt);
 #pragma unroll
     for (int s = 0; s < NSTD; ++s) {
-      if (!sub_on[s]) continue;
-      const int node = node_of[s];
-      const int64_t p_row = P + (node < 0 ? 0 : node);
-      float mb = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t key = key0 + kt * 16 + kg * 4 + i;
-          bool ok;
-          if (is_tree)
-            ok = key < P || (key < kv_len && ((tmask[s] >> (key - P)) & 1ull));
-          else
-            ok = key <= p_row;
-          const float x = (row_on[s] && ok) ? sacc[s][kt][i] * scale_log2 : -INFINITY;
-          sacc[s][kt][i] = x;
-          mb = fmaxf(mb, x);
-        }
-      mb = rows4_max(mb);
-      const float m_new = fmaxf(m_run[s], mb);
-      const bool none = m_new == -INFINITY;
-      const float alpha = none ? 1.f : exp2f(m_run[s] - m_new);
-      const float neg_m = none ? 0.f : -m_new;    // masked keys: exp2(-inf) = 0
-      float ps = 0.f;
-      float pv[4][4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(sacc[s][kt][i] + neg_m);
-          pv[kt][i] = e;
-          ps += e;
-        }
-      ps = rows4_sum(ps);
-      l_run[s] = l_run[s] * alpha + ps;
-      m_run[s] = m_new;
+      const int wr = s * 16 + r16;
+      if (kg == 0) s_ml[w][wr] = make_float2(m_run[s], l_run[s]);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) oacc[s][dt][i] *= alpha;
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        uint4 uu;
-        uu.x = cvt_pk_bf16(pv[2 * k2][0], pv[2 * k2][1]);
-        uu.y = cvt_pk_bf16(pv[2 * k2][2], pv[2 * k2][3]);
-        uu.z = cvt_pk_bf16(pv[2 * k2 + 1][0], pv[2 * k2 + 1][1]);
-        uu.w = cvt_pk_bf16(pv[2 * k2 + 1][2], pv[2 * k2 + 1][3]);
-        pf[s][k2] = as_bf16x8(uu);
-      }
+        *reinterpret_cast<float4*>(o_s + wr * D + dt * 16 + kg * 4) =
+            make_float4(oacc[s][dt][0], oacc[s][dt][1], oacc[s][dt][2], oacc[s][dt][3]);
     }
-    wait_vmem();                                   // the V tile has landed in LDS
-    if constexpr (D == 128) {
-      // byte offset of lane (r16, kg)'s chunk for d tile 0, rows 4*kg + r16/4
-      const int v_row = 4 * kg + r16 / 4;
-      const int v_lane = v_row * (D * 2) + ((((r16 % 4) >> 1) ^ vswz(v_row)) << 4) + 8 * (r16 & 1);
+    __syncthreads();
+    // Merge the wavefronts by log-sum-exp. A thread takes 4-column units (row
+    // wr, columns c .. c+3) and issues all of a unit's LDS reads (every
+    // wavefront's (m, l) and O values) before it uses any of them; the sums run
+    // over the wavefronts in order.
+    constexpr int MAXW = NSTD == 1 ? kMaxWaves : kMaxWaves2;
+    constexpr int U4 = D / 4;
+    const bool final = nsplit == 1;
+    for (int unit = threadIdx.x; unit < WR * U4; unit += blockDim.x) {
+      const int wr = unit / U4, c = (unit % U4) * 4;
+      const int row = row0 + wr;
+      if (row >= rows) continue;
+      float2 ml[MAXW];
+      f32x4 ov[MAXW];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const int off = k2 * 32 * D * 2 + (v_lane ^ (dt << 5));
-          const bf16x8 vf = read_vt_tr(vt, off, off + 16 * D * 2);
-#pragma unroll
-          for (int s = 0; s < NSTD; ++s) {
-            if (!sub_on[s]) continue;
-            oacc[s][dt] = mfma16(vf, pf[s][k2], oacc[s][dt]);
-          }
+      for (int x = 0; x < MAXW; ++x) {
+        if (x < nwv) {
+          ml[x] = s_ml[x][wr];
+          ov[x] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(dsm + x * kBlock * D) + wr * D + c);
         }
       }
-    } else {
-      const uint16_t* vlane = vt + 4 * kg * D + r16;  // key 4*kg, column r16 (swizzle applied per dt)
+      float M = -INFINITY;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const uint16_t* vcol = vlane + ((dt ^ kg) << 4);
+      for (int x = 0; x < MAXW; ++x)
+        if (x < nwv) M = fmaxf(M, ml[x].x);
+      float Lsum = 0.f;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          // key slots (kg, jj): key = 32*k2 + 16*(jj/4) + 4*kg + jj%4, matching pf's packing
-          uint32_t w4[4];
+      for (int x = 0; x < MAXW; ++x) {
+        if (x < nwv) {
+          const float wgt = ml[x].x == -INFINITY ? 0.f : exp2f(ml[x].x - M);
+          Lsum += wgt * ml[x].y;
 #pragma unroll
-          for (int hp = 0; hp < 4; ++hp) {
-            const int koff = 32 * k2 + 16 * (hp / 2) + 2 * (hp % 2);   // jj = 2*hp
-            const uint32_t lo = vcol[koff * D];
-            const uint32_t hi = vcol[(koff + 1) * D];
-            w4[hp] = lo | (hi << 16);
-          }
-          const bf16x8 vf = as_bf16x8(uint4{w4[0], w4[1], w4[2], w4[3]});
-#pragma unroll
-          for (int s = 0; s < NSTD; ++s) {
-            if (!sub_on[s]) continue;
-            oacc[s][dt] = mfma16(vf, pf[s][k2], oacc[s][dt]);
-          }
+          for (int i = 0; i < 4; ++i) acc[i] += wgt * ov[x][i];
+        }
+      }
+      if (final) {
+        const int node = row / G, hh = row % G;
+        const int64_t rid = (int64_t(b) * Hq + g * G + hh) * n_q + node;
+        uint2 uu;
+        uu.x = uint32_t(f2bf(Lsum > 0.f ? acc[0] / Lsum : 0.f)) | (uint32_t(f2bf(Lsum > 0.f ? acc[1] / Lsum : 0.f)) << 16);
+        uu.y = uint32_t(f2bf(Lsum > 0.f ? acc[2] / Lsum : 0.f)) | (uint32_t(f2bf(Lsum > 0.f ? acc[3] / Lsum : 0.f)) << 16);
+        *reinterpret_cast<uint2*>(out + rid * D + c) = uu;
+        if (lse && c == 0) lse[rid] = (M + log2f(Lsum)) * 0.69314718055994531f;
+      } else {
+        // partials: ml[bg][split][row] = (m, l); o[bg][split][row][d] (unnormalized)
+        const int64_t pr = (int64_t(bg) * nsplit + split) * rows + row;
+        *reinterpret_cast<f32x4*>(part_o + pr * D + c) = acc;
+        if (c == 0) {
+          part_ml[pr * 2 + 0] = M;
+          part_ml[pr * 2 + 1] = Lsum;
         }
       }
     }
-  }
-
-  // This wavefront's partial -> LDS: (m, l) per row, O (unnormalized, zeros
-  // for rows that saw no key) in the wavefront's V tile, [row][D] fp32.
-  wait_lds();
-  float* o_s = reinterpret_cast<float*>(vt);
-#pragma unroll
-  for (int s = 0; s < NSTD; ++s) {
-    const int wr = s * 16 + r16;
-    if (kg == 0) s_ml[w][wr] = make_float2(m_run[s], l_run[s]);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<float4*>(o_s + wr * D + dt * 16 + kg * 4) =
-          make_float4(oacc[s][dt][0], oacc[s][dt][1], oacc[s][dt][2], oacc[s][dt][3]);
-  }
-  __syncthreads();
-  // Merge the wavefronts by log-sum-exp. A thread takes 4-column units (row
-  // wr, columns c .. c+3) and issues all of a unit's LDS reads (every
-  // wavefront's (m, l) and O values) before it uses any of them; the sums run
-  // over the wavefronts in order.
-  constexpr int MAXW = NSTD == 1 ? kMaxWaves : kMaxWaves2;
-  constexpr int U4 = D / 4;
-  const bool final = nsplit == 1;
-  for (int unit = threadIdx.x; unit < WR * U4; unit += blockDim.x) {
-    const int wr = unit / U4, c = (unit % U4) * 4;
-    const int row = row0 + wr;
-    if (row >= rows) continue;
-    float2 ml[MAXW];
-    f32x4 ov[MAXW];
-#pragma unroll
-    for (int x = 0; x < MAXW; ++x) {
-      if (x < nwv) {
-        ml[x] = s_ml[x][wr];
-        ov[x] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(dsm + x * kBlock * D) + wr * D + c);
-      }
-    }
-    float M = -INFINITY;
-#pragma unroll
-    for (int x = 0; x < MAXW; ++x)
-      if (x < nwv) M = fmaxf(M, ml[x].x);
-    float Lsum = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int x = 0; x < MAXW; ++x) {
-      if (x < nwv) {
-        const float wgt = ml[x].x == -INFINITY ? 0.f : exp2f(ml[x].x - M);
-        Lsum += wgt * ml[x].y;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += wgt * ov[x][i];
-      }
-    }
-    if (final) {
-      const int node = row / G, hh = row % G;
-      const int64_t rid = (int64_t(b) * Hq + g * G + hh) * n_q + node;
-      uint2 uu;
-      uu.x = uint32_t(f2bf(Lsum > 0.f ? acc[0] / Lsum : 0.f)) | (uint32_t(f2bf(Lsum > 0.f ? acc[1] / Lsum : 0.f)) << 16);
-      uu.y = uint32_t(f2bf(Lsum > 0.f ? acc[2] / Lsum : 0.f)) | (uint32_t(f2bf(Lsum > 0.f ? acc[3] / Lsum : 0.f)) << 16);
-      *reinterpret_cast<uint2*>(out + rid * D + c) = uu;
-      if (lse && c == 0) lse[rid] = (M + log2f(Lsum)) * 0.69314718055994531f;
-    } else {
-      // partials: ml[bg][split][row] = (m, l); o[bg][split][row][d] (unnormalized)
-      const int64_t pr = (int64_t(bg) * nsplit + split) * rows + row;
-      *reinterpret_cast<f32x4*>(part_o + pr * D + c) = acc;
-      if (c == 0) {
-        part_ml[pr * 2 + 0] = M;
-        part_ml[pr * 2 + 1] = Lsum;
-      }
-    }
+    if (!kLoop || split + nsg >= nsplit || (split + nsg) * sb >= n_e) break;
+    __syncthreads();                              // the next split reuses the LDS
   }
 }
 
@@ -663,7 +673,17 @@ hipError_t launch_decode(const Dims& d, const uint16_t* q, int n_q, const uint16
   const int nstd_total = (rows + 15) / 16;
   const int nstd = nstd_total >= 2 ? 2 : nstd_total;
   const unsigned ygroups = unsigned((nstd_total + nstd - 1) / nstd);
-  const dim3 grid(unsigned(L.bgs * L.nsplit), ygroups);
+  // Multi-row calls of two sub-tiles: splits for a union of about 2(K+1)
+  // blocks plus the rows' own blocks (a tree's nodes mostly agree) or, for
+  // dense rows, the whole range; a larger union is walked by the same
+  // workgroups in turn. (Single-token calls keep every split: their combine
+  // reads all of them, entries or not.)
+  int nsg = int(L.nsplit);
+  if (n_q > 1 && nstd > 1 && !(d.dense_thr > 0 && kv_len - n_q + 1 < d.dense_thr)) {
+    const int64_t e_typ = 2 * (int64_t(d.K) + 1) + (n_q + kBlock - 1) / kBlock + 1;
+    nsg = int(std::min<int64_t>(L.nsplit, (e_typ + sb - 1) / sb));
+  }
+  const dim3 grid(unsigned(L.bgs * nsg), ygroups);
   const float sl2 = d.scale * 1.4426950408889634f;
   const int n_e1 = int(L.max_e);
   const int64_t nblk = (kv_cap + kBlock - 1) / kBlock;
@@ -682,7 +702,7 @@ hipError_t launch_decode(const Dims& d, const uint16_t* q, int n_q, const uint16
     if (attr != hipSuccess) return attr;                                                          \
     kern<<<grid, 64 * sb, size_t(sb) * kBlock * DD * 2, s>>>(                                     \
         q, k, v, idx, tree_mask, u_blk, u_mask, u_count, part_ml, part_o, out, lse, d.Hq, d.Hkv,  \
-        d.G, n_q, kv_cap, kv_len, d.K, d.dense_thr, is_tree, sb, int(L.nsplit), int(L.max_e),     \
+        d.G, n_q, kv_cap, kv_len, d.K, d.dense_thr, is_tree, sb, int(L.nsplit), nsg, int(L.max_e), \
         int(L.rows), sl2, scores, nblk, idx_out, kv_lens);                                        \
   } else
 #define SPLIT_SEL(DD)                                                                             \
