@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void decode_union_kernel(
     int32_t* __restrict__ u_blk, uint64_t* __restrict__ u_mask, int32_t* __restrict__ u_count,
     int Hkv, int n_q, int K, int64_t kv_len, int is_tree, int dense_thr, int64_t max_e) {
   extern __shared__ uint64_t nm[];          // [last_blk + 1] row masks per block
-  __shared__ int s_cnt[256];
+  __shared__ int s_cnt[4];
   const int bg = blockIdx.x;
   const int b = bg / Hkv;
   const int tid = threadIdx.x;
@@ -127,20 +127,23 @@ __global__ __launch_bounds__(256) void decode_union_kernel(
       atomicOr(reinterpret_cast<unsigned long long*>(&nm[j]), all);
   }
   __syncthreads();
-  // ascending compaction: thread t scans blocks [t*per, (t+1)*per)
+  // ascending compaction: thread t scans blocks [t*per, (t+1)*per); offsets
+  // from a DPP scan within each wavefront and the four wavefront totals
   const int per = (nb + 255) / 256;
   const int lo = min(nb, tid * per), hi = min(nb, lo + per);
   int c = 0;
   for (int j = lo; j < hi; ++j) c += nm[j] != 0ull;
-  s_cnt[tid] = c;
+  const int incl = int(wave_incl_scan_dpp(uint32_t(c)));
+  const int wv = tid / kWave;
+  if (lane_id() == kWave - 1) s_cnt[wv] = incl;
   __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {      // inclusive scan
-    const int x = tid >= o ? s_cnt[tid - o] : 0;
-    __syncthreads();
-    s_cnt[tid] += x;
-    __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    before += x < wv ? s_cnt[x] : 0;
+    total += s_cnt[x];
   }
-  int pos = s_cnt[tid] - c;
+  int pos = before + incl - c;
   for (int j = lo; j < hi; ++j) {
     if (nm[j] != 0ull && pos < max_e) {
       u_blk[int64_t(bg) * max_e + pos] = j;
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(256) void decode_union_kernel(
       ++pos;
     }
   }
-  if (tid == 255) u_count[bg] = min<int64_t>(s_cnt[255], max_e);
+  if (tid == 255) u_count[bg] = min<int64_t>(total, max_e);
 }
 
 // ------------------------------------------------------------------ split
