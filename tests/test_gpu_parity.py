@@ -287,6 +287,23 @@ def test_tree_end_to_end(case):
     run_decode(TREE_CASES[case])
 
 
+def test_tree_union_beyond_the_typical_size():
+    """A tree whose nodes mostly pick different blocks (nothing planted): the
+    union of a group exceeds the typical size the attention grid is sized for
+    (about 2(K+1) blocks plus the rows' own), so its workgroups walk further
+    splits in turn."""
+    w = T0.scaled(name="t_wide", seq_len=16384, top_k=8, n_plant=0, dense_threshold=0)
+    d, ref, _ = run_decode(w, seed=3)
+    n_q, kv_len = d["n_q"], d["kv_len"]
+    P = kv_len - n_q
+    local = (kv_len - 1) // 64 - P // 64 + 1
+    union = max(len({int(j) for j in ref["idx"][b, g].ravel() if j >= 0}) + local
+                for b in range(w.batch) for g in range(w.n_kv_heads))
+    sb = 4                                  # union entries per split for two 16-row sub-tiles
+    typical = sb * -(-(2 * (w.top_k + 1) + -(-n_q // 64) + 1) // sb)
+    assert union > typical, (union, typical)
+
+
 def _decode_scores_matches_split_path(w, seed=0):
     """The fused entry (selection inside the attention kernel) reproduces the
     separate top-K + attention entry points bit for bit."""
