@@ -108,11 +108,14 @@ __global__ __launch_bounds__(256, 2) void topk_prefill_kernel(
     for (int ds = 0; ds < DS; ++ds) dst[ds] = as_bf16x8(ldg16(p + ds * 512));
   };
 
-  bf16x8 qa[2][DS], kfa[DS], kfb[DS];
+  bf16x8 qa[2][DS], kf0[DS], kf1[DS], kf2[DS];
   const Item cur = item_of(it);
   if (cur.Cmax > K) {
     load_q(cur, qa);
-    if (nmine_of(cur) > 0) load_step(cur, nmine_of(cur), 0, 0, kfa);
+    if (nmine_of(cur) > 0) {
+      load_step(cur, nmine_of(cur), 0, 0, kf0);
+      load_step(cur, nmine_of(cur), 0, 1, kf1);
+    }
   }
   {
     // ------------------------------------------------------------ 1. scores
@@ -173,22 +176,15 @@ __global__ __launch_bounds__(256, 2) void topk_prefill_kernel(
         }
       };
 
-      // The next step's fragments load while one step computes; two chunks
-      // (six steps) per iteration keep the two fragment buffers in place.
-      for (int i = 0; i < nmine; i += 2) {
-        load_step(cur, nmine, i, 1, kfb);
-        compute_step(i, 0, kfa);
-        load_step(cur, nmine, i, 2, kfa);
-        compute_step(i, 1, kfb);
-        load_step(cur, nmine, i + 1, 0, kfb);
-        compute_step(i, 2, kfa);
-        if (i + 1 >= nmine) break;
-        load_step(cur, nmine, i + 1, 1, kfa);
-        compute_step(i + 1, 0, kfb);
-        load_step(cur, nmine, i + 1, 2, kfb);
-        compute_step(i + 1, 1, kfa);
-        load_step(cur, nmine, i + 2, 0, kfa);
-        compute_step(i + 1, 2, kfb);
+      // Fragments load two steps ahead of their MFMAs; the three buffers
+      // follow the three kernel slots of a chunk, so they stay in place.
+      for (int i = 0; i < nmine; ++i) {
+        load_step(cur, nmine, i, 2, kf2);
+        compute_step(i, 0, kf0);
+        load_step(cur, nmine, i + 1, 0, kf0);   // past the last chunk: clamped, unused
+        compute_step(i, 1, kf1);
+        load_step(cur, nmine, i + 1, 1, kf1);
+        compute_step(i, 2, kf2);
       }
     }
     // Warm the L2 with the Q rows of the item that a workgroup of this XCD
