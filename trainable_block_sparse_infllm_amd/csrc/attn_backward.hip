@@ -168,19 +168,10 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void bw
   const uint16_t* kbase = k + int64_t(bg) * kv_cap * kD;
   const uint16_t* vbase = v + int64_t(bg) * kv_cap * kD;
 
-  // This lane's row: token tok0 + w*TPS + r32/G, head g*G + r32%G. Q^T and
-  // dO^T fragments (B operands, k-slots 8*hl .. of each 16-wide d step).
+  // This lane's row: token tok0 + w*TPS + r32/G, head g*G + r32%G.
   const int my_t = tok0 + w * TPS + r32 / G;
   const int h = g * G + r32 % G;
   const int64_t rid = (int64_t(b) * Hq + h) * n_q + (my_t < n_q ? my_t : 0);
-  bf16x8 qf[DS], df[DS];
-#pragma unroll
-  for (int ds = 0; ds < DS; ++ds) {
-    qf[ds] = as_bf16x8(ldg16_if(my_t < n_q, q + rid * kD + ds * 16 + hl * 8));
-    df[ds] = as_bf16x8(ldg16_if(my_t < n_q, dout + rid * kD + ds * 16 + hl * 8));
-  }
-  const float row_lse2 = my_t < n_q ? lse2[rid] : 0.f;
-  const float row_delta = my_t < n_q ? delta[rid] : 0.f;
 
   int U;
   if (tile_dense)
@@ -202,6 +193,18 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void bw
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(vbase), 0, int(nrec), 0x00020000);
   if (U > 0) issue_stage<NW>(ring, rk, rv, int64_t(blk_of(0)) * kBlock, w, l);
+  // Q^T and dO^T fragments (B operands, k-slots 8*hl .. of each 16-wide d
+  // step) and the row's lse and Delta, loaded after the union is built
+  // (waiting for its index loads would also wait for these, the counter being
+  // in order) and together with the first ring stage.
+  bf16x8 qf[DS], df[DS];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) {
+    qf[ds] = as_bf16x8(ldg16_if(my_t < n_q, q + rid * kD + ds * 16 + hl * 8));
+    df[ds] = as_bf16x8(ldg16_if(my_t < n_q, dout + rid * kD + ds * 16 + hl * 8));
+  }
+  const float row_lse2 = my_t < n_q ? lse2[rid] : 0.f;
+  const float row_delta = my_t < n_q ? delta[rid] : 0.f;
 
   f32x16 dqacc[DT];
 #pragma unroll

@@ -99,17 +99,8 @@ __device__ __forceinline__ void prefill_attn_body(
   const uint16_t* kbase = k + int64_t(bg) * kv_cap * kD;
   const uint16_t* vbase = v + int64_t(bg) * kv_cap * kD;
 
-  // This lane's query row: token tok0 + w*TPS + r32/G, head g*G + r32%G. Its
-  // Q^T fragments (B operand, k-slots 8*hl .. 8*hl+7 of each 16-wide d step)
-  // are loaded first so their latency overlaps the union construction.
+  // This lane's query row: token tok0 + w*TPS + r32/G, head g*G + r32%G.
   const int my_t = tok0 + w * TPS + r32 / G;
-  bf16x8 qf[DS];
-  {
-    const int h = g * G + r32 % G;
-    const uint16_t* qrow = q + ((int64_t(b) * Hq + h) * n_q + (my_t < n_q ? my_t : 0)) * kD;
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) qf[ds] = as_bf16x8(ldg16_if(my_t < n_q, qrow + ds * 16 + hl * 8));
-  }
 
   auto range_mask_t = [&](int64_t j) -> uint64_t {
     return range_mask(j, mode, base, dend, ntok, window);
@@ -140,6 +131,17 @@ __device__ __forceinline__ void prefill_attn_body(
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(vbase), 0, int(nrec), 0x00020000);
   if (U > 0) issue_stage<NW>(ring, rk, rv, blk_of(0) * kBlock, w, l);
+  // Q^T fragments (B operand, k-slots 8*hl .. 8*hl+7 of each 16-wide d step),
+  // loaded after the union is built (waiting for its index loads would also
+  // wait for these, the counter being in order) and together with the first
+  // ring stage, whose wait covers them.
+  bf16x8 qf[DS];
+  {
+    const int h = g * G + r32 % G;
+    const uint16_t* qrow = q + ((int64_t(b) * Hq + h) * n_q + (my_t < n_q ? my_t : 0)) * kD;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) qf[ds] = as_bf16x8(ldg16_if(my_t < n_q, qrow + ds * 16 + hl * 8));
+  }
 
   f32x16 oacc[DT];
 #pragma unroll

@@ -162,20 +162,25 @@ __device__ __forceinline__ int build_union(const int32_t* __restrict__ idx, int6
   const int l = lane_id();
   const int nwords = int(own_hi / 32) + 1;    // <= 256, checked on the host
   const int64_t rlo = dend > 0 ? 0 : own_lo;  // range part: [rlo, own_hi]
-  for (int i = tid; i < nwords; i += NT)
-    bitmap[i] = uint32_t(range_bits(rlo - int64_t(i) * 32, own_hi + 1 - int64_t(i) * 32, 32));
-  __syncthreads();
-  // four index loads per thread are issued before any of them is used, so
-  // their latencies overlap
+  // Four index loads per thread are issued before any of them is used, so
+  // their latencies overlap; the first four go out before the bitmap is set
+  // up, so their latency also covers that work and its barrier.
   const int nsel = ntok * K;
-  for (int e0 = tid; e0 < nsel; e0 += 4 * NT) {
-    int jv[4];
+  auto load4 = [&](int e0, int (&jv)[4]) {
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int e = e0 + x * NT;
       const int t = e / K;
       jv[x] = (e < nsel && t >= dend) ? idx[(bg * n_q + tok0 + t) * K + e % K] : -1;
     }
+  };
+  int jv[4];
+  load4(tid, jv);
+  for (int i = tid; i < nwords; i += NT)
+    bitmap[i] = uint32_t(range_bits(rlo - int64_t(i) * 32, own_hi + 1 - int64_t(i) * 32, 32));
+  __syncthreads();
+  for (int e0 = tid; e0 < nsel; e0 += 4 * NT) {
+    if (e0 != tid) load4(e0, jv);
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int e = e0 + x * NT;
