@@ -169,8 +169,7 @@ __global__ __launch_bounds__(256) void decode_union_kernel(
 __device__ __forceinline__ int vswz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
 template <int D>
-__device__ __forceinline__ void load_v_tile(const uint16_t* vbase, int64_t key0, int64_t kv_len,
-                                            uint16_t* vt) {
+__device__ __forceinline__ void load_v_tile(__amdgpu_buffer_rsrc_t rv, uint16_t* vt) {
   constexpr int PPR = D / 8;                 // 16-byte pieces per row
   constexpr int RPI = kWave / PPR;           // rows per 1 KB instruction
   const int l = lane_id();
@@ -178,12 +177,23 @@ __device__ __forceinline__ void load_v_tile(const uint16_t* vbase, int64_t key0,
   for (int x = 0; x < kBlock / RPI; ++x) {
     const int r = x * RPI + l / PPR;
     const int piece = l % PPR;
-    const int64_t key = key0 + r;
     const int sw = D == 128 ? vswz(r) : ((r >> 2) & 3) << 1;
-    const void* src = key < kv_len ? static_cast<const void*>(vbase + key * D + ((piece ^ sw) << 3))
-                                   : static_cast<const void*>(kZeroPiece);
-    load_lds16_nt(src, vt + x * RPI * D);       // each selected block is read once per step
+    // nontemporal (cache policy 2): each selected block is read once per step
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (las_void*)(vt + x * RPI * D), 16,
+                                             uint32_t(r * D * 2 + ((piece ^ sw) << 4)), 0, 0, 2);
   }
+}
+
+// The rows of block j (keys 64j .. 64j+63) below kv_len as a buffer resource:
+// loads through it take 32-bit offsets below 16 KB whatever the context
+// length, and rows past kv_len read zeros.
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint16_t* base, int64_t key0,
+                                                             int64_t kv_len) {
+  const int64_t live = kv_len - key0;
+  const int rows = int(live < 0 ? 0 : (live > kBlock ? kBlock : live));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + key0 * D), 0, rows * D * 2,
+                                           0x00020000);
 }
 
 typedef short dv4i16 __attribute__((ext_vector_type(4)));
@@ -345,20 +355,32 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
         j = u_blk[int64_t(bg) * max_e + u];
         nmask = u_mask[int64_t(bg) * max_e + u];
       }
-      const int64_t key0 = j * kBlock;
+      const int64_t key0 = int64_t(uniform_u64(uint64_t(j))) * kBlock;
 
-      wait_lds();                                    // previous block's V reads are done
-      load_v_tile<D>(vbase, key0, kv_len, vt);       // V -> LDS, no registers
-      // K fragments straight from HBM: lane feeds key 16*kt + r16, d = 32*ks + 8*kg .. +7
+      // K fragments straight from HBM (lane feeds key 16*kt + r16, d = 32*ks +
+      // 8*kg .. +7; nontemporal), issued before the V tile: the products with
+      // K wait for the K loads alone (the vector-memory counter is in order),
+      // while V still arrives. A wave-uniform base at the block and 32-bit
+      // lane offsets; rows are clamped into the cache (scores of keys past
+      // kv_len are replaced by -inf in the softmax, whatever K holds there).
       bf16x8 kf[4][KS];
+      {
+        const uint16_t* kblk = kbase + key0 * D;
+        const int rmax = int(min<int64_t>(kBlock - 1, kv_cap - 1 - key0));
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const int64_t key = key0 + kt * 16 + r16;
+        for (int kt = 0; kt < 4; ++kt) {
+          const int row = min(kt * 16 + r16, rmax);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          kf[kt][ks] = as_bf16x8(ldg16_nt(key < kv_len ? static_cast<const void*>(kbase + key * D + ks * 32 + kg * 8)
-                                                       : static_cast<const void*>(kZeroPiece)));
+          for (int ks = 0; ks < KS; ++ks)
+            kf[kt][ks] = as_bf16x8(ldg16_nt(kblk + row * D + ks * 32 + kg * 8));
+        }
       }
+      // Every K load issues before the V tile's and before any product (left
+      // free, the scheduler sinks them to their uses, one round trip each).
+      __builtin_amdgcn_sched_barrier(0);
+      wait_lds();                                    // previous block's V reads are done
+      load_v_tile<D>(block_rsrc<D>(vbase, key0, kv_len), vt);   // V -> LDS, no registers
+      __builtin_amdgcn_sched_barrier(0);
 
       bool sub_on[NSTD], row_on[NSTD];
 #pragma unroll
@@ -366,10 +388,12 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
         row_on[s] = node_of[s] >= 0 && ((nmask >> node_of[s]) & 1ull);
         sub_on[s] = ballot64(row_on[s]) != 0ull;
       }
+      // S for every sub-tile, needed or not: with the products behind the
+      // sub-tile test, the compiler moves the K loads into that branch and
+      // issues them one at a time next to their uses.
       f32x4 sacc[NSTD][4];
 #pragma unroll
       for (int s = 0; s < NSTD; ++s) {
-        if (!sub_on[s]) continue;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
           f32x4 a = {0.f, 0.f, 0.f, 0.f};
