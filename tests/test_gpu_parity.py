@@ -71,6 +71,8 @@ TREE_CASES = {
                               n_tree=5, tree_depth=3),
     "single_node": T0.scaled(name="t_one", n_q_heads=8, n_kv_heads=2, seq_len=2000, top_k=4, n_plant=4,
                              n_tree=1, tree_depth=1, dense_threshold=0),
+    # 160 (node, head) rows: the scoring kernel's two-tile wavefronts and a partial last row tile
+    "p2048_n40_d128": T0.scaled(name="t_n40", seq_len=2048, top_k=8, n_plant=8, n_tree=40, tree_depth=6),
 }
 
 
