@@ -169,17 +169,29 @@ def test_prefill_32k_full_size_whole_tiles():
     check_idx_rows(gidx, C, w.top_k)
 
 
-def test_topk_from_fp32_scores_is_exact_with_ties():
+# (table length, first row's candidate count, K, value stored past each row's candidates):
+# one wavefront per row (C <= 256), and one workgroup per row (C > 512; K above 64 takes its
+# exact fallback; C % 4 == 0 and != 0 both occur among the 5 rows; values past C that would
+# win if read)
+TOPK_SCORE_CASES = [(300, 250, 16, -np.inf), (2100, 2040, 16, 1e30), (2100, 2040, 64, -np.inf),
+                    (2100, 2040, 100, 1e30), (700, 600, 32, 1e30)]
+
+
+@pytest.mark.parametrize("nblk,c0,K,tail", TOPK_SCORE_CASES)
+def test_topk_from_fp32_scores_is_exact_with_ties(nblk, c0, K, tail):
     """Selection from a score tensor equals the oracle's rule on the same fp32
     scores, ties included (scores quantized so that many are equal)."""
     rng = np.random.default_rng(5)
-    B, Hkv, n_q, nblk, K = 2, 3, 5, 300, 16
+    B, Hkv, n_q = 2, 3, 5
+    note(f"top-K from scores: nblk {nblk} C {c0}..{c0 + n_q - 1} K {K} tail {tail}")
     R = np.round(rng.standard_normal((B * Hkv * n_q, nblk)) * 4) / 4
-    q_pos0 = 64 * 250
+    q_pos0 = 64 * c0
     C = np.tile((q_pos0 + np.arange(n_q)) // 64, B * Hkv)
     for r in range(R.shape[0]):
         R[r, C[r]:] = -np.inf
     ref = orc.select(R.astype(np.float32).astype(np.float64), C, K)
+    for r in range(R.shape[0]):
+        R[r, C[r]:] = tail
     cfg = lib.make_cfg(B, Hkv * 4, Hkv, 128, top_k=K)
     idx = torch.empty((B, Hkv, n_q, K), dtype=torch.int32, device="cuda")
     scores = torch.from_numpy(R.astype(np.float32)).cuda()

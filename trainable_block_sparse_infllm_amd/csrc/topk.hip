@@ -41,6 +41,26 @@ __global__ __launch_bounds__(256) void topk_scores_kernel(const float* __restric
   wave_topk<KPL>(key, int(C), K, idx + row * K, scratch[threadIdx.x / kWave]);
 }
 
+// Few rows of many candidates (a draft tree's nodes): eight wavefronts share
+// one row (wg_topk8 of topk_select.hpp), so the row's selection is not one
+// wavefront's sort over 64*KPL keys. Only candidates j < C are read.
+template <int KPL>
+__global__ __launch_bounds__(512) void topk_scores_wg_kernel(const float* __restrict__ scores,
+                                                             int32_t* __restrict__ idx, int n_q,
+                                                             int64_t q_pos0, int is_tree,
+                                                             int64_t nblk, int K) {
+  __shared__ uint32_t scratch[2 * kWave];
+  __shared__ WgTopkLds sh;
+  const int64_t row = blockIdx.x;
+  const int node = int(row % n_q);
+  const int64_t pos = is_tree ? q_pos0 : q_pos0 + node;
+  const int C = int(min<int64_t>(pos / kBlock, nblk));
+  const float* src = scores + row * nblk;
+  // 16-byte loads when the row starts 16-byte aligned and whole quads lie below C
+  const bool vec = (C & 3) == 0 && (nblk & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
+  wg_topk8<KPL>(src, C, vec, C, K, idx + row * K, scratch, sh);
+}
+
 // ---------------------------------------------------------- fused prefill path
 // Workgroup: 4 wavefronts, 16*NT query columns holding TQ <= 16*NT/G tokens of
 // one (b, g) (TQ is smaller only when TQ score rows of 64*KPL candidates would
@@ -150,6 +170,10 @@ __global__ __launch_bounds__(256) void topk_fused_kernel(const uint16_t* __restr
   }
 }
 
+// Row count up to which the workgroup-per-row selection is used (beyond it,
+// one wavefront per row already fills the chip).
+constexpr int64_t kWgRowsMax = 1024;
+
 static int pick_kpl(int64_t cmax) {
   int kpl = 1;
   while (int64_t(kpl) * kWave < cmax) kpl <<= 1;
@@ -193,6 +217,16 @@ hipError_t launch_topk_from_scores(const Dims& d, const float* scores, int n_q, 
   int64_t cmax = pos_last / kBlock;
   if (cmax > nblk) cmax = nblk;
   const int kpl = pick_kpl(cmax);
+  if (kpl >= 8 && rows <= kWgRowsMax) {
+#define TOPK_WG_CASE(P)                                                                        \
+    if (kpl == P) {                                                                            \
+      topk_scores_wg_kernel<P><<<dim3(unsigned(rows)), 512, 0, s>>>(scores, idx, n_q, q_pos0,  \
+                                                                   is_tree, nblk, d.K);        \
+      return hipGetLastError();                                                                \
+    }
+    TOPK_WG_CASE(8) TOPK_WG_CASE(16) TOPK_WG_CASE(32) TOPK_WG_CASE(64)
+#undef TOPK_WG_CASE
+  }
   const dim3 grid(unsigned((rows + 3) / 4));
 #define TOPK_CASE(P)                                                                           \
   if (kpl == P) {                                                                              \
