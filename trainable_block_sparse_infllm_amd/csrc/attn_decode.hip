@@ -260,6 +260,17 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
   } else {
     n_e = u_count[bg];
   }
+  // A multi-row call's first entry of this wavefront, loaded with the union
+  // size rather than after it (the entry, then its K and V, would otherwise
+  // be a third dependent round trip). Clamped into the union table's row.
+  int32_t pre_j = 0;
+  uint64_t pre_m = 0;
+  const int u_pre = split0 * sb + w;
+  if (n_q > 1) {
+    const int64_t e = int64_t(bg) * max_e + min(u_pre, max_e - 1);
+    pre_j = u_blk[e];
+    pre_m = u_mask[e];
+  }
   // A multi-row call sizes its splits for the largest possible union, and its
   // combine reads only the splits that hold entries (u_count): a split past
   // the union has nothing to write. (Single-token rows keep every split: their
@@ -352,8 +363,13 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
         if (!dense1 && u < K && (j < 0 || j >= own1)) continue;
         nmask = 1ull;
       } else {
-        j = u_blk[int64_t(bg) * max_e + u];
-        nmask = u_mask[int64_t(bg) * max_e + u];
+        if (u == u_pre) {
+          j = pre_j;
+          nmask = pre_m;
+        } else {
+          j = u_blk[int64_t(bg) * max_e + u];
+          nmask = u_mask[int64_t(bg) * max_e + u];
+        }
       }
       const int64_t key0 = int64_t(uniform_u64(uint64_t(j))) * kBlock;
 
@@ -577,30 +593,12 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
 // read every split's (m, l), then every lane issues the loads of its D/64
 // columns for all splits of the chunk before using any of them.
 template <int D, int CH>
-__global__ __launch_bounds__(256) void decode_combine_kernel(
-    const float* __restrict__ part_ml, const float* __restrict__ part_o,
-    const int32_t* __restrict__ u_count, uint16_t* __restrict__ out, float* __restrict__ lse,
-    int Hq, int Hkv, int G, int n_q, int nsplit, int sb, int n_e1, int rows, int64_t nrows) {
+__device__ __forceinline__ void combine_chunks(const float* __restrict__ part_ml,
+                                               const float* __restrict__ part_o, int64_t pr0,
+                                               int rows, int ns, float& M, float& L,
+                                               float (&acc)[D / kWave]) {
   constexpr int CPL = D / kWave;
   const int l = lane_id();
-  // (b, h, i); workgroups renumbered like the split kernel's, so a row's partials
-  // are read on the XCD whose L2 holds them
-  const int64_t rid = int64_t(xcd_remap(blockIdx.x, gridDim.x)) * 4 + threadIdx.x / kWave;
-  if (rid >= nrows) return;
-  const int i = int(rid % n_q);
-  const int h = int((rid / n_q) % Hq);
-  const int b = int(rid / (int64_t(n_q) * Hq));
-  const int g = h / G;
-  const int bg = b * Hkv + g;
-  const int row = i * G + h % G;
-  const int n_e = n_q == 1 ? n_e1 : u_count[bg];
-  const int ns = min(nsplit, (n_e + sb - 1) / sb);
-  const int64_t pr0 = int64_t(bg) * nsplit * rows + row;   // split s at pr0 + s * rows
-  float M = -INFINITY, L = 0.f;
-  float acc[CPL];
-#pragma unroll
-  for (int x = 0; x < CPL; ++x) acc[x] = 0.f;
-  // chunks of CH splits (CH = 8 when every row has at most 8, else 64)
   for (int s0 = 0; s0 < ns; s0 += CH) {
     const int s = s0 + (l % CH);
     const float* ml = part_ml + (pr0 + int64_t(s) * rows) * 2;
@@ -629,6 +627,40 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
       for (int x = 0; x < CPL; ++x) acc[x] += wt * o[t][x];
     }
   }
+}
+
+// CH = 8: every row has at most 8 splits. CH = 64: a row's splits go in chunks
+// of 16 while it has at most 16 (a multi-row call's union usually fills a few
+// of the splits the grid was sized for; loads of empty slots still cost an
+// instruction each), else in chunks of 64.
+template <int D, int CH>
+__global__ __launch_bounds__(256) void decode_combine_kernel(
+    const float* __restrict__ part_ml, const float* __restrict__ part_o,
+    const int32_t* __restrict__ u_count, uint16_t* __restrict__ out, float* __restrict__ lse,
+    int Hq, int Hkv, int G, int n_q, int nsplit, int sb, int n_e1, int rows, int64_t nrows) {
+  constexpr int CPL = D / kWave;
+  const int l = lane_id();
+  // (b, h, i); workgroups renumbered like the split kernel's, so a row's partials
+  // are read on the XCD whose L2 holds them
+  const int64_t rid = int64_t(xcd_remap(blockIdx.x, gridDim.x)) * 4 + threadIdx.x / kWave;
+  if (rid >= nrows) return;
+  const int i = int(rid % n_q);
+  const int h = int((rid / n_q) % Hq);
+  const int b = int(rid / (int64_t(n_q) * Hq));
+  const int g = h / G;
+  const int bg = b * Hkv + g;
+  const int row = i * G + h % G;
+  const int n_e = n_q == 1 ? n_e1 : u_count[bg];
+  const int ns = min(nsplit, (n_e + sb - 1) / sb);
+  const int64_t pr0 = int64_t(bg) * nsplit * rows + row;   // split s at pr0 + s * rows
+  float M = -INFINITY, L = 0.f;
+  float acc[CPL];
+#pragma unroll
+  for (int x = 0; x < CPL; ++x) acc[x] = 0.f;
+  if (CH > 16 && ns <= 16)
+    combine_chunks<D, 16>(part_ml, part_o, pr0, rows, ns, M, L, acc);
+  else
+    combine_chunks<D, CH>(part_ml, part_o, pr0, rows, ns, M, L, acc);
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint16_t* dst = out + rid * D + CPL * l;
 #pragma unroll
