@@ -250,26 +250,37 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
   const uint16_t* kbase = k + int64_t(bg) * kv_cap * D;
   const uint16_t* vbase = v + int64_t(bg) * kv_cap * D;
 
-  int n_e;
+  int n_e = 0;
   bool dense1 = false;
   int64_t own1 = 0;
   if (n_q == 1) {
     own1 = (kv_len - 1) / kBlock;
     dense1 = dense_thr > 0 && kv_len < dense_thr;
     n_e = dense1 ? int(own1) + 1 : K + 1;
-  } else {
-    n_e = u_count[bg];
   }
-  // A multi-row call's first entry of this wavefront, loaded with the union
-  // size rather than after it (the entry, then its K and V, would otherwise
-  // be a third dependent round trip). Clamped into the union table's row.
+  // A multi-row call reads its union size and this wavefront's first entry
+  // together (the entry, then its K and V, would otherwise be a third
+  // dependent round trip). Vector loads (a lane offset the compiler cannot
+  // see through): as scalar loads, the kernel's scalar register pressure had
+  // them issued one after another, each waited for. The entry is clamped
+  // into the union table's row.
+  // (Two-sub-tile instances only: the single-sub-tile ones, at 168 registers,
+  // spill with the entry held across the selection.)
   int32_t pre_j = 0;
   uint64_t pre_m = 0;
-  const int u_pre = split0 * sb + w;
+  const int u_pre = NSTD > 1 ? split0 * sb + w : -1;
   if (n_q > 1) {
-    const int64_t e = int64_t(bg) * max_e + min(u_pre, max_e - 1);
-    pre_j = u_blk[e];
-    pre_m = u_mask[e];
+    if constexpr (NSTD > 1) {
+      int zo = 0;
+      asm volatile("" : "+v"(zo));
+      const int64_t e = int64_t(bg) * max_e + min(u_pre, max_e - 1) + zo;
+      const int32_t cnt = u_count[bg + zo];
+      pre_j = u_blk[e];
+      pre_m = u_mask[e];
+      n_e = __builtin_amdgcn_readfirstlane(cnt);
+    } else {
+      n_e = u_count[bg];
+    }
   }
   // A multi-row call sizes its splits for the largest possible union, and its
   // combine reads only the splits that hold entries (u_count): a split past
