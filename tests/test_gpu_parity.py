@@ -61,6 +61,8 @@ DECODE_CASES = {
     "g2_d64_k_exceeds": D0.scaled(name="d_g2", n_q_heads=4, n_kv_heads=2, head_dim=64, seq_len=1500,
                                   top_k=40, n_plant=3, dense_threshold=0),
     "decode_32k": D0,
+    # the largest K the in-kernel selection takes, over 2047 candidates
+    "k64_128k": D0.scaled(name="d_k64", seq_len=131072, top_k=64, n_plant=32),
 }
 
 TREE_CASES = {
@@ -73,6 +75,10 @@ TREE_CASES = {
                              n_tree=1, tree_depth=1, dense_threshold=0),
     # 160 (node, head) rows: the scoring kernel's two-tile wavefronts and a partial last row tile
     "p2048_n40_d128": T0.scaled(name="t_n40", seq_len=2048, top_k=8, n_plant=8, n_tree=40, tree_depth=6),
+    # GQA 8: 128 rows per group, 625 candidates (selection by eight wavefronts per row)
+    "g8_p40000": T0.scaled(name="t_g8", n_q_heads=16, n_kv_heads=2, seq_len=40000, top_k=16, n_plant=8),
+    # GQA 16: 256 rows per group (two-tile scoring wavefronts, head sums across lane pairs)
+    "g16_p3000": T0.scaled(name="t_g16", n_q_heads=16, n_kv_heads=1, seq_len=3000, top_k=8, n_plant=4),
 }
 
 
