@@ -354,8 +354,12 @@ def test_decode_from_scores_128k_batch8_full_size():
 
 
 @pytest.mark.parametrize("B,Hkv,kv_len,kv_cap", [(8, 8, 131072, 131072),      # eight-wavefront selection
-                                                (2, 4, 65636, 65636),          # one-wavefront selection
-                                                (1, 8, 64 * 1026 + 5, 64 * 1027)])  # rows not 16-byte aligned
+                                                # over 1024 candidates with three-entry splits: the
+                                                # workgroup gets five helper wavefronts for it
+                                                (2, 4, 65636, 65636),
+                                                (1, 8, 64 * 1026 + 5, 64 * 1027),  # rows not 16-byte aligned
+                                                (2, 4, 30000, 30000),          # one-wavefront selection
+                                                (1, 2, 16000, 16000)])
 def test_decode_selection_from_scores_exact(B, Hkv, kv_len, kv_cap):
     """Selection inside the decode kernel equals the oracle's rule on hand-made
     fp32 scores: quantized values (many exact ties), -0 and +0 mixed (equal as

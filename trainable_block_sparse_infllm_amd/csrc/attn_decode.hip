@@ -232,6 +232,9 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
   __shared__ float2 s_ml[kMaxWaves][WR];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int nwv = blockDim.x / kWave;
+  // Waves past the split's entries (helpers of a wide selection) hold no
+  // entry, no V tile and no partial.
+  const int nwe = min(nwv, sb);
   uint16_t* vt = dsm + w * kBlock * D;
   const int l = lane_id();
   const int r16 = l % 16, kg = l / 16;
@@ -295,15 +298,19 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
     const int C = int(min(own1, nblk));           // (dense rows ignore the list; idx_out gets it)
     const float* row = scores + int64_t(bg) * nblk;
     const bool vec = (nblk & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
+    // Over more than 1024 candidates the selection always runs on eight
+    // wavefronts (the launch adds helpers): one wavefront holding 16+ keys
+    // per lane next to the attention state spilled registers.
     bool many = false;
-    if constexpr (SKPL >= 8) many = nwv >= 8;
+    if constexpr (SKPL >= 16) many = true;
+    else if constexpr (SKPL >= 8) many = nwv >= 8;
     if constexpr (SKPL >= 8) {
       if (many) {                                 // eight wavefronts share the selection
         __shared__ WgTopkLds s_tk;
         wg_topk8<SKPL>(row, nblk, vec, C, K, s_sel, s_scr, s_tk);
       }
     }
-    if (!many && w == 0) {
+    if (SKPL < 16 && !many && w == 0) {
       // lane l holds candidates SKPL*l .. SKPL*l + SKPL-1 (lane order = index order)
       const int jl = l * SKPL;
       float val[SKPL];
@@ -531,14 +538,16 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
     // for rows that saw no key) in the wavefront's V tile, [row][D] fp32.
     wait_lds();
     float* o_s = reinterpret_cast<float*>(vt);
+    if (w < nwe) {
 #pragma unroll
-    for (int s = 0; s < NSTD; ++s) {
-      const int wr = s * 16 + r16;
-      if (kg == 0) s_ml[w][wr] = make_float2(m_run[s], l_run[s]);
+      for (int s = 0; s < NSTD; ++s) {
+        const int wr = s * 16 + r16;
+        if (kg == 0) s_ml[w][wr] = make_float2(m_run[s], l_run[s]);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<float4*>(o_s + wr * D + dt * 16 + kg * 4) =
-            make_float4(oacc[s][dt][0], oacc[s][dt][1], oacc[s][dt][2], oacc[s][dt][3]);
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<float4*>(o_s + wr * D + dt * 16 + kg * 4) =
+              make_float4(oacc[s][dt][0], oacc[s][dt][1], oacc[s][dt][2], oacc[s][dt][3]);
+      }
     }
     __syncthreads();
     // Merge the wavefronts by log-sum-exp. A thread takes 4-column units (row
@@ -556,7 +565,7 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
       f32x4 ov[MAXW];
 #pragma unroll
       for (int x = 0; x < MAXW; ++x) {
-        if (x < nwv) {
+        if (x < nwe) {
           ml[x] = s_ml[x][wr];
           ov[x] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(dsm + x * kBlock * D) + wr * D + c);
         }
@@ -564,12 +573,12 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
       float M = -INFINITY;
 #pragma unroll
       for (int x = 0; x < MAXW; ++x)
-        if (x < nwv) M = fmaxf(M, ml[x].x);
+        if (x < nwe) M = fmaxf(M, ml[x].x);
       float Lsum = 0.f;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int x = 0; x < MAXW; ++x) {
-        if (x < nwv) {
+        if (x < nwe) {
           const float wgt = ml[x].x == -INFINITY ? 0.f : exp2f(ml[x].x - M);
           Lsum += wgt * ml[x].y;
 #pragma unroll
@@ -764,6 +773,10 @@ hipError_t launch_decode(const Dims& d, const uint16_t* q, int n_q, const uint16
     skpl = 1;
     while (int64_t(skpl) * kWave < c) skpl <<= 1;
   }
+  // Wavefronts per workgroup: one per entry, and at least eight when the
+  // in-kernel selection needs them (more than 1024 candidates); helpers take
+  // no entry and no LDS tile.
+  const int nwv = skpl >= 16 ? std::max(sb, 8) : sb;
 #define SPLIT_CASE(DD, NN, SK)                                                                    \
   if (d.D == DD && nstd == NN && skpl == SK) {                                                    \
     auto kern = decode_split_kernel<DD, NN, SK>;                                                  \
@@ -771,7 +784,7 @@ hipError_t launch_decode(const Dims& d, const uint16_t* q, int n_q, const uint16
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,          \
         (NN == 1 ? kMaxWaves : kMaxWaves2) * kBlock * DD * 2);                                    \
     if (attr != hipSuccess) return attr;                                                          \
-    kern<<<grid, 64 * sb, size_t(sb) * kBlock * DD * 2, s>>>(                                     \
+    kern<<<grid, 64 * nwv, size_t(sb) * kBlock * DD * 2, s>>>(                                    \
         q, k, v, idx, tree_mask, u_blk, u_mask, u_count, part_ml, part_o, out, lse, d.Hq, d.Hkv,  \
         d.G, n_q, kv_cap, kv_len, d.K, d.dense_thr, is_tree, sb, int(L.nsplit), nsg, int(L.max_e), \
         int(L.rows), sl2, scores, nblk, idx_out, kv_lens);                                        \
