@@ -354,7 +354,7 @@ def test_decode_from_scores_128k_batch8_full_size():
 
 
 @pytest.mark.parametrize("B,Hkv,kv_len,kv_cap", [(8, 8, 131072, 131072),      # eight-wavefront selection
-                                                # over 1024 candidates with three-entry splits: the
+                                                # over 512 candidates with three-entry splits: the
                                                 # workgroup gets five helper wavefronts for it
                                                 (2, 4, 65636, 65636),
                                                 (1, 8, 64 * 1026 + 5, 64 * 1027),  # rows not 16-byte aligned

@@ -298,7 +298,7 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
     const int C = int(min(own1, nblk));           // (dense rows ignore the list; idx_out gets it)
     const float* row = scores + int64_t(bg) * nblk;
     const bool vec = (nblk & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
-    // Over more than 1024 candidates the selection always runs on eight
+    // Over more than 512 candidates the selection always runs on eight
     // wavefronts (the launch adds helpers): one wavefront holding 16+ keys
     // per lane next to the attention state spilled registers.
     bool many = false;
@@ -774,7 +774,7 @@ hipError_t launch_decode(const Dims& d, const uint16_t* q, int n_q, const uint16
     while (int64_t(skpl) * kWave < c) skpl <<= 1;
   }
   // Wavefronts per workgroup: one per entry, and at least eight when the
-  // in-kernel selection needs them (more than 1024 candidates); helpers take
+  // in-kernel selection needs them (more than 512 candidates); helpers take
   // no entry and no LDS tile.
   const int nwv = skpl >= 16 ? std::max(sb, 8) : sb;
 #define SPLIT_CASE(DD, NN, SK)                                                                    \
