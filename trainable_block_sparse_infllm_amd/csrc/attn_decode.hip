@@ -542,6 +542,7 @@ __global__ __launch_bounds__(64 * (NSTD == 1 ? kMaxWaves : kMaxWaves2)) void dec
 #pragma unroll
       for (int s = 0; s < NSTD; ++s) {
         const int wr = s * 16 + r16;
+        if (row0 + wr >= rows) continue;          // (the merge reads only the call's rows)
         if (kg == 0) s_ml[w][wr] = make_float2(m_run[s], l_run[s]);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
