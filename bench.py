@@ -118,6 +118,11 @@ ENTRY_KERNELS = {
                                      ("attn_backward.hip", "prefill_tile.hpp")),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TRACE_FILE = os.path.join(ROOT, "profiles", "kernel_durations.json")
+# Entry points whose roofline the benchmark reports, with the trace leg that holds their launches.
+TRACED_ENTRIES = {"sparse_attn_decode_scores": "decode", "score_blocks": "decode",
+                  "sparse_attn_prefill": "prefill", "sparse_attn_prefill_backward": "backward",
+                  "sliding_window_attn": "window"}
 CSRC = os.path.join(ROOT, "trainable_block_sparse_infllm_amd", "csrc")
 
 
@@ -143,6 +148,50 @@ def measured_traffic(entry: str):
     if not e or e.get("source_hash") != source_hash(entry):
         return None
     return e["bytes_per_launch"]
+
+
+def store_trace_durations(dbs: dict) -> dict:
+    """Average kernel-trace duration of each reported entry point's kernels, from the rocprofv3
+    --kernel-trace databases of the bench legs ({leg: db}); one launch runs each kernel once."""
+    import sqlite3
+    out = {"entries": {}}
+    for entry, leg in TRACED_ENTRIES.items():
+        if leg not in dbs:
+            continue
+        con = sqlite3.connect(dbs[leg])
+        rows = con.execute("select name, count(*), avg(duration) from kernels group by name").fetchall()
+        kern = {}
+        for n, c, a in rows:
+            sn = _short(n)
+            if any(sn.startswith(k + "<") or sn == k for k in ENTRY_KERNELS[entry][0]):
+                kern[sn] = {"calls": c, "avg_us": round(a / 1e3, 3)}
+        if kern:
+            out["entries"][entry] = {"kernels": kern, "launch_us": round(sum(k["avg_us"] for k in kern.values()), 3),
+                                     "source_hash": source_hash(entry)}
+    return out
+
+
+def traced_launch_us(entry: str):
+    """Sum of the entry point's kernels' average traced durations from the stored trace runs, or
+    None when none were stored or the kernel sources changed since."""
+    try:
+        with open(TRACE_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    e = t.get("entries", {}).get(entry)
+    if not e or e.get("source_hash") != source_hash(entry):
+        return None
+    return e["launch_us"]
+
+
+def traced_fields(entry: str, amount: float, peak: float) -> dict:
+    """Roofline fields from the stored kernel-trace durations: `amount` per launch (bytes or flops
+    in the unit of `peak` per microsecond)."""
+    us = traced_launch_us(entry)
+    if us is None:
+        return {"traced_launch_us": None, "frac_traced": None}
+    return {"traced_launch_us": us, "frac_traced": round(amount / us / peak, 4)}
 
 
 def _short(name: str) -> str:
@@ -745,6 +794,9 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("PMC_DB", "TRACE_DB"),
                     help="print a markdown table of the counters in a --pmc database (durations from a "
                          "--kernel-trace database of the same command) and exit")
+    ap.add_argument("--store-trace-durations", nargs="+", metavar="LEG=DB",
+                    help="write profiles/kernel_durations.json from kernel-trace databases of the bench "
+                         "legs (decode=..., prefill=..., backward=..., window=...) and exit")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="write profiles/traffic.json from FETCH_SIZE and WRITE_SIZE runs of this bench and exit")
     args = ap.parse_args()
@@ -758,6 +810,13 @@ def main():
     if args.traffic_md:
         with open(TRAFFIC_FILE) as fh:
             sys.stdout.write(traffic_markdown(json.load(fh)))
+        return
+    if args.store_trace_durations:
+        dbs = dict(x.split("=", 1) for x in args.store_trace_durations)
+        t = store_trace_durations(dbs)
+        with open(TRACE_FILE, "w") as fh:
+            json.dump(t, fh, indent=1)
+        print(json.dumps(t, indent=1))
         return
     if args.summarize_pmc:
         # the decode leg clones the 2 GiB K and V caches of decode_128k_b8 for its rotations
@@ -833,7 +892,8 @@ def main():
                          "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic(dom), "algorithmic_bytes_per_launch": dom_bytes,
                          "launch_us_median": round(dom_ms * 1e3, 3),
-                         "timing": "median of the launch's event-timed duration over the eager steps"},
+                         "timing": "median of the launch's event-timed duration over the eager steps",
+                         **traced_fields(dom, dom_bytes / 1e3, HBM_PEAK_GBS)},
             "step_hbm": {"algorithmic_bytes": b["total"], "achieved_gbs": round(step_gbs, 1),
                          "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
             "launches": per_launch,
@@ -886,7 +946,8 @@ def main():
                          "frac": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                          "algorithmic_gflop_per_launch": round(f["attn"] / 1e9, 2),
                          "launch_ms_median": round(attn_ms, 4),
-                         "traffic": measured_traffic("sparse_attn_prefill")},
+                         "traffic": measured_traffic("sparse_attn_prefill"),
+                         **traced_fields("sparse_attn_prefill", f["attn"] / 1e6, MFMA_BF16_PEAK_TFLOPS)},
         }
         configs[wp.name] = {"ms_per_step": round(ms, 4), "tflops": round(tf, 2),
                             "frac_mfma": result["prefill"]["frac_mfma"]}
@@ -905,7 +966,8 @@ def main():
             "roofline": {"bound": "mfma", "kernel": "sparse_attn_prefill_backward", "achieved": round(btf, 2),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(btf / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "traffic": measured_traffic("sparse_attn_prefill_backward")},
+                         "traffic": measured_traffic("sparse_attn_prefill_backward"),
+                         **traced_fields("sparse_attn_prefill_backward", bw["flops"] / 1e6, MFMA_BF16_PEAK_TFLOPS)},
         }
 
     if "window" in legs:
@@ -919,7 +981,8 @@ def main():
             "roofline": {"bound": "mfma", "kernel": "sliding_window_attn", "achieved": round(wtf, 2),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(wtf / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "traffic": measured_traffic("sliding_window_attn")},
+                         "traffic": measured_traffic("sliding_window_attn"),
+                         **traced_fields("sliding_window_attn", sw["flops"] / 1e6, MFMA_BF16_PEAK_TFLOPS)},
         }
 
     if "tiny" in legs:

@@ -59,3 +59,35 @@ def test_counter_summary_rates_from_counter_and_trace_databases(tmp_path):
     assert cells[1] == "2" and cells[2] == "1.5e+12" and cells[3] == "30"
     assert cells[4] == "1000.0" and cells[5] == "1500" and cells[6] == "60.0%"
     assert "fill_k" not in md
+
+
+def test_trace_durations_give_traced_roofline_while_sources_match(tmp_path, monkeypatch):
+    """A launch's traced duration is the sum of its kernels' average traced durations (one call
+    each per launch); the traced fraction is reported only while the kernel sources match."""
+    import sqlite3
+    db = tmp_path / "trace.db"
+    con = sqlite3.connect(db)
+    con.execute("create table kernels (name text, duration real)")
+    con.executemany("insert into kernels values (?, ?)",
+                    [("void infllmv2::decode_split_kernel<128, 1, 32>(int)", 18.0e3)] * 2 +
+                    [("void infllmv2::decode_split_kernel<128, 1, 32>(int)", 20.0e3)] * 2 +
+                    [("void infllmv2::decode_combine_kernel<128, 8>(int)", 5.0e3)] * 4 +
+                    [("void infllmv2::score_kernel<128, 4, 1>(int)", 17.0e3)] * 4 +
+                    [("__amd_rocclr_copyBuffer", 600.0e3)])
+    con.commit()
+    t = bench.store_trace_durations({"decode": str(db)})
+    e = t["entries"]["sparse_attn_decode_scores"]
+    assert e["launch_us"] == 24.0 and set(e["kernels"]) == {"decode_split_kernel<128, 1, 32>",
+                                                             "decode_combine_kernel<128, 8>"}
+    assert t["entries"]["score_blocks"]["launch_us"] == 17.0
+    assert "sparse_attn_prefill" not in t["entries"]
+    f = tmp_path / "durations.json"
+    f.write_text(json.dumps(t))
+    monkeypatch.setattr(bench, "TRACE_FILE", str(f))
+    # 48 MB per launch over 24 us = 2000 GB/s = 25% of 8 TB/s
+    got = bench.traced_fields("sparse_attn_decode_scores", 48e6 / 1e3, 8000.0)
+    assert got == {"traced_launch_us": 24.0, "frac_traced": 0.25}
+    t["entries"]["sparse_attn_decode_scores"]["source_hash"] = "stale"
+    f.write_text(json.dumps(t))
+    assert bench.traced_fields("sparse_attn_decode_scores", 1.0, 1.0) == {"traced_launch_us": None,
+                                                                           "frac_traced": None}
