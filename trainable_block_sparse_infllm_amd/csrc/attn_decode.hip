@@ -662,8 +662,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   constexpr int CPL = D / kWave;
   const int l = lane_id();
   // (b, h, i); workgroups numbered like the split kernel's, so a row's partials
-  // are read on the XCD that wrote them (they still come from the last-level
-  // cache: the kernel boundary writes back and drops that L2's lines)
+  // are read on the XCD that wrote them (they still arrive at last-level-cache
+  // latency across the kernel boundary)
   const int64_t rid = int64_t(xcd_remap(blockIdx.x, gridDim.x)) * 4 + threadIdx.x / kWave;
   if (rid >= nrows) return;
   const int i = int(rid % n_q);
