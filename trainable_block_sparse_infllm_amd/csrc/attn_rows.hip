@@ -14,12 +14,13 @@
 // tokens of one (b, g); each wavefront owns NST sub-tiles of 16 MFMA rows =
 // 16/G tokens x G heads (one token's heads share a block set, so a sub-tile is
 // the smallest set of rows with a common key set per token). The workgroup
-// walks the union of its tokens' blocks in ascending order: per step the next
-// block is the minimum over tokens of "next block this token needs", each
-// block's K and V are staged once in LDS (double-buffered, one barrier per
-// block, next block's global loads in flight during the current compute), and
-// each wavefront runs only the sub-tiles that contain at least one token
-// needing the block; rows of tokens not needing it are masked to -inf.
+// walks the union of its tokens' blocks in ascending order. The union (a
+// range holding the tokens' own blocks and dense tokens' whole visible range,
+// plus a bitmap of the selected blocks below it) is built in LDS first, so
+// the walk is known ahead: each block's K and V go from HBM to registers two
+// or three blocks ahead, and are staged once in LDS (two buffers, one barrier
+// per block). Each wavefront runs only the sub-tiles that contain at least one
+// token needing the block; rows of tokens not needing it are masked to -inf.
 //
 // Per active sub-tile and block (MFMA 16x16x32 bf16, fp32 accumulate):
 //   S^T = K Q^T   (A = K rows from LDS, B = Q held in registers)
@@ -28,6 +29,8 @@
 //                   straight from the S^T accumulator layout)
 // The K fragments of a key tile and the V fragments of a d tile are read from
 // LDS once per wavefront and reused across its active sub-tiles.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -115,8 +118,11 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(
   static_assert(TPW <= 64, "one lane per token of a wavefront");
 
   extern __shared__ __align__(16) uint16_t smem[];
-  int* s_next = reinterpret_cast<int*>(smem + 2 * S::BUF);   // [2][4] per-wave minima
-  int32_t* s_idx = s_next + 8;                                 // [TQ][K]
+  const int64_t last_blk = (kv_len - 1) / kBlock;
+  const int nwords = int(last_blk >> 5) + 1;
+  uint32_t* s_bits = reinterpret_cast<uint32_t*>(smem + 2 * S::BUF);   // [nwords] selected blocks
+  int* s_rng = reinterpret_cast<int*>(s_bits + nwords);                // [2][4] per-wave range bounds
+  int32_t* s_idx = s_rng + 8;                                          // [TQ][K]
 
   const int tid = threadIdx.x;
   const int w = tid / kWave;
@@ -139,6 +145,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(
       s_idx[e] = tok0 + t < n_q ? idx[(int64_t(bg) * n_q + tok0 + t) * K + e % K] : -1;
     }
   }
+  for (int e = tid; e < nwords; e += 256) s_bits[e] = 0u;
 
   // ---- Q fragments (B operand of S^T = K Q^T): row r16 = (token r16/G, head r16%G)
   bf16x8 qf[NST][KS];
@@ -158,7 +165,6 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(
   const int my_t = tok0 + w * TPW + l;
   const bool tok_ok = l < TPW && my_t < n_q;
   const int64_t my_p = pos0 + my_t;
-  const int64_t last_blk = (kv_len - 1) / kBlock;
   const int my_own = tok_ok ? int(mode == 2 ? last_blk : my_p / kBlock) : -1;
   const bool my_dense = mode != 0 || (dense_thr > 0 && my_p + 1 < dense_thr);
   // mode 3: the block holding the token's first visible key
@@ -173,12 +179,46 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(
     return my_own;                       // own block last (entries past it are ignored)
   };
   int my_nxt = next_needed(-1);
+
+  // ---- the tile's union of blocks, in ascending order the sequence of
+  // "smallest block some token still needs" of the per-token walks, known in
+  // advance so that the loads run several blocks ahead: a range [rlo, rhi]
+  // (every token's own block, and all of a dense token's visible blocks)
+  // plus the selected blocks below it, kept as bits.
+  if (tok_ok && mode == 0 && !my_dense) {
+    for (int p = 0; p < K; ++p) {
+      const int j = my_idx[p];
+      if (j >= 0 && j < my_own) atomicOr(&s_bits[j >> 5], 1u << (j & 31));
+    }
+  }
   {
-    const int wm = wave_min_i32(my_nxt);
-    if (l == 0) s_next[4 + w] = wm;      // slot set 1: the loop's first write goes to set 0
+    const int lo = wave_min_i32(tok_ok ? (my_dense ? my_lo : my_own) : kEnd);
+    const int hi = -wave_min_i32(tok_ok ? -my_own : 1);
+    if (l == 0) {
+      s_rng[w] = lo;
+      s_rng[4 + w] = hi;
+    }
   }
   __syncthreads();
-  int j_cur = min(min(s_next[4], s_next[5]), min(s_next[6], s_next[7]));
+  const int rlo = __builtin_amdgcn_readfirstlane(min(min(s_rng[0], s_rng[1]), min(s_rng[2], s_rng[3])));
+  const int rhi = __builtin_amdgcn_readfirstlane(max(max(s_rng[4], s_rng[5]), max(s_rng[6], s_rng[7])));
+  auto find_next = [&](int j) -> int {          // the union's first block after j
+    const int c = j + 1;
+    if (c > rhi) return kEnd;
+    if (c >= rlo) return c;
+    int wd = c >> 5;
+    const int wl = (rlo - 1) >> 5;
+    uint32_t m = uint32_t(__builtin_amdgcn_readfirstlane(int(s_bits[wd] & (~0u << (c & 31)))));
+    while (m == 0u && wd < wl) {
+      ++wd;
+      m = uint32_t(__builtin_amdgcn_readfirstlane(int(s_bits[wd])));
+    }
+    if (m != 0u) {
+      const int bj = (wd << 5) + __builtin_ctz(m);
+      if (bj < rlo) return bj;
+    }
+    return rlo;
+  };
 
   // ---- running softmax state per sub-tile (lane's row = r16)
   f32x4 oacc[NST][DT];
@@ -194,25 +234,41 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(
 #pragma unroll
   for (int s = 0; s < NST; ++s) row_p[s] = pos0 + tok0 + w * TPW + s * TPS + r16 / G;
 
-  KVStage<D> stage;
-  if (j_cur != kEnd) stage.load(kbase, vbase, j_cur, kv_len, tid);
+  // Register stages of the next NA union entries (entry u in stage u % NA);
+  // LDS holds two blocks (entry u in buffer u % 2). At entry u a stage is
+  // stored to LDS, the barrier makes it visible (and, every wavefront having
+  // finished entry u - 1, frees the other buffer for entry u + 1), and the
+  // stage is refilled with entry u + NA.
+  constexpr int NA = (NST == 1 && D == 64) ? 3 : 2;
+  KVStage<D> st[NA];
+  int jq[NA];
+  jq[0] = find_next(-1);
+#pragma unroll
+  for (int a = 1; a < NA; ++a) jq[a] = jq[a - 1] == kEnd ? kEnd : find_next(jq[a - 1]);
+  // Every step issues the same loads (an entry past the end reloads a valid
+  // block that is never stored), so the wait before a stage's store counts
+  // only the loads issued before that stage's.
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+    st[a].load(kbase, vbase, jq[a] == kEnd ? 0 : jq[a], kv_len, tid);
+    __builtin_amdgcn_sched_barrier(0);          // stages issue in order, as in the loop
+  }
 
   int parity = 0;
-  while (j_cur != kEnd) {
+  auto step = [&](auto slot_c) __attribute__((always_inline)) -> bool {
+    constexpr int A = decltype(slot_c)::value;
+    const int j_cur = jq[A];
+    if (j_cur == kEnd) return false;
     // tokens needing this block; advance their walk
     const bool active = my_nxt == j_cur;
     const uint64_t act = ballot64(active);
     if (active) my_nxt = next_needed(j_cur);
-    {
-      const int wm = wave_min_i32(my_nxt);
-      if (l == 0) s_next[parity * 4 + w] = wm;
-    }
     uint16_t* buf = smem + parity * S::BUF;
-    stage.store(buf, tid);
-    __syncthreads();
-    const int j_nxt = min(min(s_next[parity * 4 + 0], s_next[parity * 4 + 1]),
-                          min(s_next[parity * 4 + 2], s_next[parity * 4 + 3]));
-    if (j_nxt != kEnd) stage.load(kbase, vbase, j_nxt, kv_len, tid);
+    st[A].store(buf, tid);
+    lds_barrier();                              // no global traffic between the wavefronts here
+    const int j_last = jq[(A + NA - 1) % NA];   // the entry queued last
+    jq[A] = j_last == kEnd ? kEnd : find_next(j_last);
+    st[A].load(kbase, vbase, jq[A] == kEnd ? j_cur : jq[A], kv_len, tid);
 
     const uint16_t* ks_ = buf;
     const uint16_t* vt_ = buf + S::KSZ;
@@ -312,7 +368,15 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(
     }
 
     parity ^= 1;
-    j_cur = j_nxt;
+    return true;
+  };
+  if constexpr (NA == 3) {
+    while (step(std::integral_constant<int, 0>()) && step(std::integral_constant<int, 1>()) &&
+           step(std::integral_constant<int, 2>())) {
+    }
+  } else {
+    while (step(std::integral_constant<int, 0>()) && step(std::integral_constant<int, 1>())) {
+    }
   }
 
   // ---- epilogue: O / l -> bf16; lse in natural-log units
@@ -343,7 +407,9 @@ static hipError_t launch_rows_t(const Dims& d, int mode, const uint16_t* q, int 
   using S = AttnSmem<D>;
   constexpr int TQ = 4 * NST * (16 / G);
   const int ntile = (n_q + TQ - 1) / TQ;
-  const size_t lds = size_t(2 * S::BUF) * 2 + 8 * sizeof(int) + size_t(TQ) * (mode == 0 ? d.K : 0) * 4;
+  const int64_t nwords = ((kv_len - 1) / kBlock >> 5) + 1;      // union bitmap
+  const size_t lds = size_t(2 * S::BUF) * 2 + size_t(nwords) * 4 + 8 * sizeof(int) +
+                     size_t(TQ) * (mode == 0 ? d.K : 0) * 4;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   auto kern = attn_rows_kernel<D, G, NST>;
   // raise the dynamic-LDS limit of this instance once (the largest request any call can make)
