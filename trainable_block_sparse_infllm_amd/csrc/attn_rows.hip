@@ -120,7 +120,8 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(
   extern __shared__ __align__(16) uint16_t smem[];
   const int64_t last_blk = (kv_len - 1) / kBlock;
   const int nwords = int(last_blk >> 5) + 1;
-  uint32_t* s_bits = reinterpret_cast<uint32_t*>(smem + 2 * S::BUF);   // [nwords] selected blocks
+  constexpr int NB = (NST == 1 && D == 64) ? 2 : 1;   // blocks per step of the walk
+  uint32_t* s_bits = reinterpret_cast<uint32_t*>(smem + 2 * NB * S::BUF);   // [nwords] selected blocks
   int* s_rng = reinterpret_cast<int*>(s_bits + nwords);                // [2][4] per-wave range bounds
   int32_t* s_idx = s_rng + 8;                                          // [TQ][K]
 
@@ -234,42 +235,25 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(
 #pragma unroll
   for (int s = 0; s < NST; ++s) row_p[s] = pos0 + tok0 + w * TPW + s * TPS + r16 / G;
 
-  // Register stages of the next NA union entries (entry u in stage u % NA);
-  // LDS holds two blocks (entry u in buffer u % 2). At entry u a stage is
-  // stored to LDS, the barrier makes it visible (and, every wavefront having
-  // finished entry u - 1, frees the other buffer for entry u + 1), and the
-  // stage is refilled with entry u + NA.
-  constexpr int NA = (NST == 1 && D == 64) ? 3 : 2;
-  KVStage<D> st[NA];
-  int jq[NA];
+  // Each step takes the next NB union entries: their register stages are
+  // stored to LDS (buffers parity * NB + b), the barrier makes them visible
+  // (and, every wavefront having finished the previous step, frees the other
+  // parity's buffers), the stages are refilled with the following NB entries
+  // and the NB blocks are computed. The loads of a step have the compute of
+  // NB blocks to arrive: one-sequence calls at head_dim 64, whose per-block
+  // compute is short against a load's latency, take two blocks per step.
+  KVStage<D> st[NB];
+  int jq[NB];
   jq[0] = find_next(-1);
 #pragma unroll
-  for (int a = 1; a < NA; ++a) jq[a] = jq[a - 1] == kEnd ? kEnd : find_next(jq[a - 1]);
-  // Every step issues the same loads (an entry past the end reloads a valid
-  // block that is never stored), so the wait before a stage's store counts
-  // only the loads issued before that stage's.
+  for (int b2 = 1; b2 < NB; ++b2) jq[b2] = jq[b2 - 1] == kEnd ? kEnd : find_next(jq[b2 - 1]);
+  // an entry past the end loads a valid block that is never computed
 #pragma unroll
-  for (int a = 0; a < NA; ++a) {
-    st[a].load(kbase, vbase, jq[a] == kEnd ? 0 : jq[a], kv_len, tid);
-    __builtin_amdgcn_sched_barrier(0);          // stages issue in order, as in the loop
-  }
+  for (int b2 = 0; b2 < NB; ++b2) st[b2].load(kbase, vbase, jq[b2] == kEnd ? 0 : jq[b2], kv_len, tid);
 
-  int parity = 0;
-  auto step = [&](auto slot_c) __attribute__((always_inline)) -> bool {
-    constexpr int A = decltype(slot_c)::value;
-    const int j_cur = jq[A];
-    if (j_cur == kEnd) return false;
-    // tokens needing this block; advance their walk
-    const bool active = my_nxt == j_cur;
-    const uint64_t act = ballot64(active);
-    if (active) my_nxt = next_needed(j_cur);
-    uint16_t* buf = smem + parity * S::BUF;
-    st[A].store(buf, tid);
-    lds_barrier();                              // no global traffic between the wavefronts here
-    const int j_last = jq[(A + NA - 1) % NA];   // the entry queued last
-    jq[A] = j_last == kEnd ? kEnd : find_next(j_last);
-    st[A].load(kbase, vbase, jq[A] == kEnd ? j_cur : jq[A], kv_len, tid);
-
+  // One block of the walk: S^T, masked online softmax, O^T += V^T P^T for the
+  // wavefront's sub-tiles whose tokens need it.
+  auto compute = [&](int j_cur, const uint16_t* buf, uint64_t act) __attribute__((always_inline)) {
     const uint16_t* ks_ = buf;
     const uint16_t* vt_ = buf + S::KSZ;
     bool sub_on[NST];
@@ -366,17 +350,33 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(
         }
       }
     }
-
-    parity ^= 1;
-    return true;
   };
-  if constexpr (NA == 3) {
-    while (step(std::integral_constant<int, 0>()) && step(std::integral_constant<int, 1>()) &&
-           step(std::integral_constant<int, 2>())) {
+
+  int parity = 0;
+  while (jq[0] != kEnd) {
+    int jc[NB];
+    uint64_t act[NB];
+#pragma unroll
+    for (int b2 = 0; b2 < NB; ++b2) {
+      // tokens needing this block; advance their walk
+      jc[b2] = jq[b2];
+      const bool active = jc[b2] != kEnd && my_nxt == jc[b2];
+      act[b2] = ballot64(active);
+      if (active) my_nxt = next_needed(jc[b2]);
+      st[b2].store(smem + (parity * NB + b2) * S::BUF, tid);
     }
-  } else {
-    while (step(std::integral_constant<int, 0>()) && step(std::integral_constant<int, 1>())) {
+    lds_barrier();                              // no global traffic between the wavefronts here
+    int j_last = jc[NB - 1];
+#pragma unroll
+    for (int b2 = 0; b2 < NB; ++b2) {
+      jq[b2] = j_last == kEnd ? kEnd : find_next(j_last);
+      j_last = jq[b2];
+      st[b2].load(kbase, vbase, jq[b2] == kEnd ? jc[0] : jq[b2], kv_len, tid);
     }
+#pragma unroll
+    for (int b2 = 0; b2 < NB; ++b2)
+      if (jc[b2] != kEnd) compute(jc[b2], smem + (parity * NB + b2) * S::BUF, act[b2]);
+    parity ^= 1;
   }
 
   // ---- epilogue: O / l -> bf16; lse in natural-log units
@@ -408,7 +408,8 @@ static hipError_t launch_rows_t(const Dims& d, int mode, const uint16_t* q, int 
   constexpr int TQ = 4 * NST * (16 / G);
   const int ntile = (n_q + TQ - 1) / TQ;
   const int64_t nwords = ((kv_len - 1) / kBlock >> 5) + 1;      // union bitmap
-  const size_t lds = size_t(2 * S::BUF) * 2 + size_t(nwords) * 4 + 8 * sizeof(int) +
+  constexpr int NB = (NST == 1 && D == 64) ? 2 : 1;                // blocks per step
+  const size_t lds = size_t(2 * NB * S::BUF) * 2 + size_t(nwords) * 4 + 8 * sizeof(int) +
                      size_t(TQ) * (mode == 0 ? d.K : 0) * 4;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   auto kern = attn_rows_kernel<D, G, NST>;
