@@ -81,7 +81,9 @@ __device__ __forceinline__ void prefill_attn_body(
   const int l = lane_id();
   const int r32 = l % 32, hl = l / 32;        // MFMA column (row of the sub-tile), lane half
   const int item = xcd_remap(blockIdx.x, gridDim.x);
-  const int tile = item % ntile;
+  // tiles of a (b, g) from the last one down: the grid's last workgroups then
+  // hold the prompt's first tokens, whose unions are the shortest
+  const int tile = ntile - 1 - item % ntile;
   const int bg = item / ntile;
   const int b = bg / Hkv, g = bg % Hkv;
   const int tok0 = tile * TQ;
