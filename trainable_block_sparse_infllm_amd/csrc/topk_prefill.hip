@@ -9,6 +9,8 @@
 // index first on equal scores. Rows are written ascending, padded with -1.
 //
 // Workgroup: 4 wavefronts, 64 query rows = TQ = 64/G tokens of one (b, g).
+//   0. the item's Q rows go to LDS once (16 KB, loaded straight from global
+//      memory), and each wavefront reads its A fragments from there;
 //   1. scoring: the wavefronts split the table of candidate blocks into chunks
 //      of 32 and each computes, for all 64 rows, S = Q kbar^T with the
 //      32x32x16 bf16 MFMA (A = Q rows, B = kbar^T). An accumulator column is
@@ -22,6 +24,7 @@
 //      exact one-row routine over the whole wavefront (wave_topk).
 #include "common.hpp"
 #include "launch.hpp"
+#include "prefill_tile.hpp"
 #include "topk_select.hpp"
 
 namespace infllmv2 {
@@ -51,6 +54,8 @@ __global__ __launch_bounds__(256, 2) void topk_prefill_kernel(
   // [TQ][scs] order-preserving keys of the scores (ordered_key_nz: every sum
   // starts from +0 or ends with + 0, so none is -0)
   uint32_t* sc = reinterpret_cast<uint32_t*>(smem);
+  // then the item's Q rows, 64 x 256 bytes
+  char* qt = smem + size_t(TQ) * scs * 4;
   __shared__ uint32_t scratch[4][2 * kWave];
   __shared__ uint2 rbuf[ROWSEL ? 4 : 1][4][32];
   __shared__ int32_t obuf[ROWSEL ? 4 : 1][4][16];
@@ -81,17 +86,34 @@ __global__ __launch_bounds__(256, 2) void topk_prefill_kernel(
   // w + 4i; nmine of them.
   auto nmine_of = [&](const Item& c) { return (int((c.Cmax + 31) / 32) - w + 3) / 4; };
 
-  // A operand: row 32*st + r32 of the item (token row / G, head row % G),
-  // k-slots 8*hl .. 8*hl+7 of each 16-wide d step.
-  auto load_q = [&](const Item& c, bf16x8 (&qa)[2][DS]) {
+  // The item's 64 Q rows go to LDS once per workgroup, straight from global
+  // memory (each wavefront loads four 1 KB chunks of four rows); row r
+  // (token r / G, head r % G) keeps logical 16-byte piece p at physical piece
+  // p ^ swz(r). Rows past the item's tokens repeat its first token (their
+  // scores are never read).
+  auto issue_q = [&](const Item& c) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int ch = 4 * x + w;
+      const int row = 4 * ch + l / 16;
+      const int t = row / G;
+      const int h = c.g * G + row % G;
+      const int piece = (l % 16) ^ tile::swz(row);
+      const uint16_t* src = q + ((int64_t(c.b) * Hq + h) * n_q + c.tok0 + (t < c.ntok ? t : 0)) * kDK + 8 * piece;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), (las_void*)(qt + ch * 1024), 16,
+                                       0, 0);
+    }
+  };
+  // A operand from the LDS tile: row 32*st + r32 of the item, k-slots
+  // 8*hl .. 8*hl+7 of each 16-wide d step (piece 2*ds + hl).
+  auto read_q = [&](bf16x8 (&qa)[2][DS]) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int row = 32 * st + r32;
-      const int t = row / G;
-      const int h = c.g * G + row % G;
-      const uint16_t* qrow = q + ((int64_t(c.b) * Hq + h) * n_q + c.tok0 + (t < c.ntok ? t : 0)) * kDK + 8 * hl;
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) qa[st][ds] = as_bf16x8(ldg16_if(t < c.ntok, qrow + 16 * ds));
+      for (int ds = 0; ds < DS; ++ds)
+        qa[st][ds] = as_bf16x8(*reinterpret_cast<const uint4*>(
+            qt + row * (kDK * 2) + (((2 * ds + hl) ^ tile::swz(row)) << 4)));
     }
   };
   // A step is (chunk, kernel m); its B operand, lane l: block 32*chunk + r32,
@@ -111,11 +133,14 @@ __global__ __launch_bounds__(256, 2) void topk_prefill_kernel(
   bf16x8 qa[2][DS], kf0[DS], kf1[DS], kf2[DS];
   const Item cur = item_of(it);
   if (cur.Cmax > K) {
-    load_q(cur, qa);
+    issue_q(cur);
     if (nmine_of(cur) > 0) {
       load_step(cur, nmine_of(cur), 0, 0, kf0);
       load_step(cur, nmine_of(cur), 0, 1, kf1);
     }
+    wait_vmem();      // this wavefront's Q chunks (and first k-bar steps) landed
+    lds_barrier();    // ... and every wavefront's
+    read_q(qa);
   }
   {
     // ------------------------------------------------------------ 1. scores
@@ -301,10 +326,10 @@ static hipError_t launch_topk_prefill_t(const Dims& d, const uint16_t* q, const 
   auto kern = topk_prefill_kernel<G, KPL, ROWSEL>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     64 * 1024);
+                                                     80 * 1024);
   if (attr != hipSuccess) return attr;
   const dim3 grid(unsigned(int64_t(d.B) * d.Hkv * ntile));
-  kern<<<grid, 256, size_t(TQ) * scs * 4, s>>>(q, kbar, idx, d.Hq, d.Hkv, n_q, q_pos0, is_tree,
+  kern<<<grid, 256, size_t(TQ) * scs * 4 + 64 * kDK * 2, s>>>(q, kbar, idx, d.Hq, d.Hkv, n_q, q_pos0, is_tree,
                                                nblk, d.K, ntile, scs);
   return hipGetLastError();
 }
