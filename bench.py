@@ -112,7 +112,7 @@ ENTRY_KERNELS = {
     "score_blocks_lse": (("score_lse_kernel", "score_lse_combine_kernel"), ("score_lse.hip",)),
     "topk_blocks_fused": (("topk_prefill_kernel", "topk_fused_kernel"),
                           ("topk.hip", "topk_prefill.hip", "topk_select.hpp")),
-    "sparse_attn_prefill_backward": (("bwd_zero_kernel", "bwd_zero_rows_kernel", "bwd_prep_kernel",
+    "sparse_attn_prefill_backward": (("bwd_zero_kernel", "bwd_zero_rows_kernel",
                                       "bwd_dq_kernel", "bwd_count_kernel", "bwd_fill_kernel",
                                       "bwd_scan_kernel", "bwd_dkv_kernel"),
                                      ("attn_backward.hip", "prefill_tile.hpp")),

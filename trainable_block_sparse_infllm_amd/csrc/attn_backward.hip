@@ -12,15 +12,17 @@
 // P_t = exp(scale q.k_t - lse) is recomputed from the forward's lse.
 //
 // Kernels:
-//   prep  -- Delta and lse in log2 units per row;
 //   dq    -- query-centric, the forward's tiling: a workgroup walks the union
 //            of its tile's blocks through the LDS ring and keeps dQ^T in MFMA
 //            accumulators (S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T with
-//            K^T from transpose reads of the K tile);
+//            K^T from transpose reads of the K tile); it also computes each
+//            row's Delta and lse in log2 units, which it stores for dkv;
 //   index -- for every key block, the list of query tokens that attend it
 //            (per-tile LDS histograms, one global add per tile and block,
 //            prefix sums, fill) and its even split into segments of at most
-//            kSegRows query rows;
+//            kSegRows query rows; the dk, dv rows of blocks that no row
+//            attends, or that are split into several segments (atomic
+//            adds), are zeroed, every other block's rows are stored once;
 //   dkv   -- key-centric: a workgroup owns one segment of one block's list;
 //            K and V of the block stay in registers, chunks of 64 query rows
 //            (Q, dO and the rows' token, lse and Delta) stream through a
@@ -85,46 +87,24 @@ __global__ __launch_bounds__(256) void bwd_zero_kernel(uint4* __restrict__ p, in
     p[i] = uint4{0u, 0u, 0u, 0u};
 }
 
-// dk, dv rows < kv_len of every (b, g) -> 0 (rows past kv_len are not touched).
-__global__ __launch_bounds__(256) void bwd_zero_rows_kernel(float* __restrict__ dk,
+// dk, dv rows < kv_len of the blocks whose rows dkv does not simply store:
+// blocks no query row attends (count 0) and blocks split into several
+// segments (their partial sums are added atomically). One workgroup per
+// (b, g) and block; rows past kv_len are not touched.
+__global__ __launch_bounds__(256) void bwd_zero_rows_kernel(const int32_t* __restrict__ cnt,
+                                                            float* __restrict__ dk,
                                                             float* __restrict__ dv, int64_t kv_cap,
-                                                            int64_t kv_len, int64_t bgs) {
-  const int64_t per = kv_len * kD / 4;                  // float4 per (b, g)
-  const int64_t n = bgs * per;
-  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
-    const int64_t bg = i / per, r = i % per;
-    const int64_t o = bg * kv_cap * kD / 4 + r;
-    reinterpret_cast<float4*>(dk)[o] = make_float4(0.f, 0.f, 0.f, 0.f);
-    reinterpret_cast<float4*>(dv)[o] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-}
-
-// ------------------------------------------------------------------ prep
-// Delta = dO . O (both bf16, fp32 sum) and lse in log2 units, per row; 16
-// lanes per row, 8 columns each.
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ out,
-                                                       const uint16_t* __restrict__ dout,
-                                                       const float* __restrict__ lse,
-                                                       float* __restrict__ lse2,
-                                                       float* __restrict__ delta, int64_t rows) {
-  const int64_t r = int64_t(blockIdx.x) * 16 + threadIdx.x / 16;
-  const int c = threadIdx.x % 16;
-  float s = 0.f;
-  if (r < rows) {
-    const uint4 a = ldg16(out + r * kD + 8 * c);
-    const uint4 b = ldg16(dout + r * kD + 8 * c);
-    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s += bf2f(uint16_t(aw[i] & 0xFFFFu)) * bf2f(uint16_t(bw[i] & 0xFFFFu));
-      s += bf2f(uint16_t(aw[i] >> 16)) * bf2f(uint16_t(bw[i] >> 16));
-    }
-  }
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
-  if (r < rows && c == 0) {
-    delta[r] = s;
-    lse2[r] = lse[r] * 1.4426950408889634f;
+                                                            int64_t kv_len, int64_t nblk, int G) {
+  const int64_t bg = blockIdx.x / nblk, j = blockIdx.x % nblk;
+  const int64_t n = cnt[blockIdx.x];
+  if (n != 0 && n * G <= kSegRows) return;
+  const int64_t r0 = j * kBlock;
+  const int64_t nr = min<int64_t>(kBlock, kv_len - r0);
+  float4* k4 = reinterpret_cast<float4*>(dk + (bg * kv_cap + r0) * kD);
+  float4* v4 = reinterpret_cast<float4*>(dv + (bg * kv_cap + r0) * kD);
+  for (int64_t i = threadIdx.x; i < nr * (kD / 4); i += 256) {
+    k4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    v4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 }
 
@@ -132,8 +112,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 template <int G>
 __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ idx, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse2, const float* __restrict__ delta, float* __restrict__ dq,
+    const int32_t* __restrict__ idx, const uint16_t* __restrict__ out,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ lse2,
+    float* __restrict__ delta, float* __restrict__ dq,
     int Hq, int Hkv, int n_q, int64_t kv_cap, int64_t kv_len, int K, int dense_thr,
     float scale_log2, float scale, int ntile, int umax) {
   using Sh = PrefillShape<G>;
@@ -203,8 +184,31 @@ __global__ __launch_bounds__(PrefillShape<G>::NT, PrefillShape<G>::MINW) void bw
     qf[ds] = as_bf16x8(ldg16_if(my_t < n_q, q + rid * kD + ds * 16 + hl * 8));
     df[ds] = as_bf16x8(ldg16_if(my_t < n_q, dout + rid * kD + ds * 16 + hl * 8));
   }
-  const float row_lse2 = my_t < n_q ? lse2[rid] : 0.f;
-  const float row_delta = my_t < n_q ? delta[rid] : 0.f;
+  // Delta = dO . O over the row (bf16 products summed in fp32; this lane's
+  // 64 columns, then its partner's) and lse in log2 units; stored for dkv.
+  float row_delta;
+  {
+    float part = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      const uint4 o = ldg16_if(my_t < n_q, out + rid * kD + ds * 16 + hl * 8);
+      uint4 g;
+      __builtin_memcpy(&g, &df[ds], sizeof g);
+      const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, gw[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        part = fmaf(bf2f(uint16_t(ow[i] & 0xFFFFu)), bf2f(uint16_t(gw[i] & 0xFFFFu)), part);
+        part = fmaf(bf2f(uint16_t(ow[i] >> 16)), bf2f(uint16_t(gw[i] >> 16)), part);
+      }
+    }
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+    row_delta = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  const float row_lse2 = my_t < n_q ? lse[rid] * 1.4426950408889634f : 0.f;
+  if (my_t < n_q && hl == 0) {
+    delta[rid] = row_delta;
+    lse2[rid] = row_lse2;
+  }
 
   f32x16 dqacc[DT];
 #pragma unroll
@@ -917,13 +921,10 @@ static hipError_t launch_bwd_t(const Dims& d, const uint16_t* q, int n_q, const 
   const float sl2 = d.scale * 1.4426950408889634f;
   hipError_t e;
 
-  // counters (cnt and cur are adjacent) and dk, dv rows < kv_len -> 0
+  // counters (cnt and cur are adjacent) -> 0
   const int64_t n16 = int64_t(L.off_off - L.off_cnt) / 16;
   bwd_zero_kernel<<<dim3(unsigned(std::min<int64_t>(1024, (n16 + 255) / 256))), 256, 0, s>>>(
       reinterpret_cast<uint4*>(cnt), n16);
-  bwd_zero_rows_kernel<<<dim3(2048), 256, 0, s>>>(dk, dv, kv_cap, kv_len, L.bgs);
-  bwd_prep_kernel<<<dim3(unsigned((L.rows + 15) / 16)), 256, 0, s>>>(out, dout, lse, lse2, delta,
-                                                                     L.rows);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   // dq: the forward's tiling
@@ -937,7 +938,7 @@ static hipError_t launch_bwd_t(const Dims& d, const uint16_t* q, int n_q, const 
                                                        160 * 1024);
     if (attr != hipSuccess) return attr;
     kern<<<dim3(unsigned(L.bgs * ntile)), Sh::NT, prefill_lds(umax, Sh::TQ, d.K), s>>>(
-        q, k, v, idx, dout, lse2, delta, dq, d.Hq, d.Hkv, n_q, kv_cap, kv_len, d.K, d.dense_thr,
+        q, k, v, idx, out, dout, lse, lse2, delta, dq, d.Hq, d.Hkv, n_q, kv_cap, kv_len, d.K, d.dense_thr,
         sl2, d.scale, ntile, int(umax));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -948,6 +949,8 @@ static hipError_t launch_bwd_t(const Dims& d, const uint16_t* q, int n_q, const 
   bwd_count_kernel<<<dim3(unsigned(L.bgs * ttiles)), 256, hist_lds, s>>>(
       idx, cnt, n_q, kv_len, d.K, d.dense_thr, L.nblk, ttiles);
   bwd_scan_kernel<<<dim3(unsigned(L.bgs)), 256, 0, s>>>(cnt, off, seg, nseg, L.nblk, L.smax, G);
+  bwd_zero_rows_kernel<<<dim3(unsigned(L.bgs * L.nblk)), 256, 0, s>>>(cnt, dk, dv, kv_cap, kv_len,
+                                                                      L.nblk, G);
   bwd_fill_kernel<<<dim3(unsigned(L.bgs * ttiles)), 256, hist_lds, s>>>(
       idx, off, cur, list, n_q, kv_len, d.K, d.dense_thr, L.nblk, L.emax, ttiles);
   if ((e = hipGetLastError()) != hipSuccess) return e;
