@@ -264,10 +264,12 @@ INFLLMV2_API int infllmv2_score_blocks_lse(const infllmv2_cfg* cfg, const void* 
  * kv_lens[b] (device int64 [B], variable lengths; nullable) or kv_len (every
  * sequence; then kv_len + n_new <= kv_cap is checked). When kbar is given
  * (layout of infllmv2_pool_kernels), the kernels of every block the append
- * completes, blocks len_b/64 .. (len_b + n_new)/64 - 1, are pooled from the
- * updated cache in the same stream order. Rows that would land at or past
- * kv_cap are not written (device lengths cannot be checked on the host).
- * kv_lens is read, not updated: the caller advances it. n_new = 0 is a no-op. */
+ * completes, blocks len_b/64 .. (len_b + n_new)/64 - 1, are pooled in the
+ * same launch (from the cache rows before len_b and the appended rows of
+ * k_new). Rows that would land at or past kv_cap are not written (device
+ * lengths cannot be checked on the host). kv_lens is read, not updated: the
+ * caller advances it. n_new = 0 is a no-op. An append touching more than
+ * 2^31 - 1 (b, g, block) pairs returns INFLLMV2_UNSUPPORTED. */
 INFLLMV2_API int infllmv2_append_kv(const infllmv2_cfg* cfg, const void* k_new, const void* v_new,
                        int32_t n_new, void* k_cache, void* v_cache, int64_t kv_cap,
                        const int64_t* kv_lens, int64_t kv_len, void* kbar, void* stream);

@@ -446,6 +446,8 @@ int infllmv2_append_kv(const infllmv2_cfg* cfg, const void* k_new, const void* v
     return fail(INFLLMV2_INVALID_ARGUMENT, fn, "kv_len + n_new exceeds kv_cap");
   }
   if (n_new == 0) return INFLLMV2_OK;
+  if (int64_t(d.B) * d.Hkv * ((int64_t(n_new) + 63) / 64 + 1) > INT32_MAX)
+    return fail(INFLLMV2_UNSUPPORTED, fn, "too many blocks for one launch");
   TRY(check_device(fn));
   LAUNCH(fn, infllmv2::launch_append(d, static_cast<const uint16_t*>(k_new),
                                      static_cast<const uint16_t*>(v_new), n_new,

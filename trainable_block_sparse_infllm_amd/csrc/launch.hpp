@@ -12,14 +12,13 @@ struct Dims {
   float scale;
 };
 
-// Blocks first..last-1 of every sequence; with lens (device, [B]): the
-// blocks an append of n_new tokens completes in each sequence.
+// Blocks first..last-1 of every sequence.
 hipError_t launch_pool(const Dims& d, const uint16_t* k, int64_t kv_cap, int64_t nblk,
-                       int64_t first, int64_t last, uint16_t* kbar, hipStream_t s,
-                       const int64_t* lens = nullptr, int64_t n_new = 0);
+                       int64_t first, int64_t last, uint16_t* kbar, hipStream_t s);
 
 // Cache append of n_new tokens at each sequence's length (lens[b], or kv_len
-// when lens is null), then pooling of the blocks it completes (kbar != null).
+// when lens is null), and pooling of the blocks it completes (kbar != null),
+// in one launch.
 hipError_t launch_append(const Dims& d, const uint16_t* k_new, const uint16_t* v_new,
                          int64_t n_new, uint16_t* k_cache, uint16_t* v_cache, int64_t kv_cap,
                          const int64_t* lens, int64_t kv_len, uint16_t* kbar, hipStream_t s);

@@ -19,42 +19,23 @@
 
 namespace infllmv2 {
 
-// Blocks first .. first+nb-1 of every (b, g); with lens (a cache append of
-// n_new tokens to sequences of lengths lens[b]): the blocks of sequence b
-// that the append completes, lens[b]/64 .. (lens[b]+n_new)/64 - 1, at most
-// nb of them.
-template <int D>
-__global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ k,
-                                                   uint16_t* __restrict__ kbar, int64_t kv_cap,
-                                                   int64_t nblk, int64_t first, int64_t nb,
-                                                   int64_t total, const int64_t* __restrict__ lens,
-                                                   int64_t n_new, int Hkv) {
+// Kernels of block j of (b, g) from its 64 key rows, row r at row_of(r): one
+// wavefront, lane l owns D/64 adjacent columns.
+template <int D, typename RowOf>
+__device__ __forceinline__ void pool_block(RowOf row_of, uint16_t* __restrict__ kbar, int64_t bg,
+                                           int64_t j, int64_t nblk, int l) {
   constexpr int CPL = D / kWave;  // columns per lane: 1 or 2
-  const int w = threadIdx.x / kWave;
-  const int l = threadIdx.x % kWave;
-  const int64_t item = int64_t(blockIdx.x) * 4 + w;
-  if (item >= total) return;
-  const int64_t bg = item / nb;
-  int64_t j = first + item % nb;
-  if (lens) {
-    const int64_t len0 = lens[bg / Hkv];
-    j = len0 / kBlock + item % nb;
-    if (len0 < 0 || j >= min((len0 + n_new) / kBlock, kv_cap / kBlock)) return;
-  }
-  const uint16_t* src = k + (bg * kv_cap + j * kBlock) * D + CPL * l;
   // lane l owns columns CPL*l ..: piece CPL*l/8, offset CPL*l%8 within it
   const int piece = CPL * l / 8, within = CPL * l % 8;
-
   double s[4][CPL];
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int x = 0; x < CPL; ++x) s[c][x] = 0.0;
-
   if constexpr (CPL == 2) {
     uint32_t row[kBlock];
 #pragma unroll
-    for (int r = 0; r < kBlock; ++r) row[r] = *reinterpret_cast<const uint32_t*>(src + r * D);
+    for (int r = 0; r < kBlock; ++r) row[r] = *reinterpret_cast<const uint32_t*>(row_of(r) + CPL * l);
 #pragma unroll
     for (int r = 0; r < kBlock; ++r) {
       s[r / 16][0] += double(bf2f(uint16_t(row[r] & 0xFFFFu)));
@@ -63,7 +44,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ 
   } else {
     uint16_t row[kBlock];
 #pragma unroll
-    for (int r = 0; r < kBlock; ++r) row[r] = src[r * D];
+    for (int r = 0; r < kBlock; ++r) row[r] = row_of(r)[CPL * l];
 #pragma unroll
     for (int r = 0; r < kBlock; ++r) s[r / 16][0] += double(bf2f(row[r]));
   }
@@ -79,17 +60,32 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ 
   }
 }
 
+// Blocks first .. first+nb-1 of every (b, g), one wavefront each.
+template <int D>
+__global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ k,
+                                                   uint16_t* __restrict__ kbar, int64_t kv_cap,
+                                                   int64_t nblk, int64_t first, int64_t nb,
+                                                   int64_t total) {
+  const int w = threadIdx.x / kWave;
+  const int l = threadIdx.x % kWave;
+  const int64_t item = int64_t(blockIdx.x) * 4 + w;
+  if (item >= total) return;
+  const int64_t bg = item / nb;
+  const int64_t j = first + item % nb;
+  const uint16_t* src = k + (bg * kv_cap + j * kBlock) * D;
+  pool_block<D>([&](int r) { return src + r * D; }, kbar, bg, j, nblk, l);
+}
+
 hipError_t launch_pool(const Dims& d, const uint16_t* k, int64_t kv_cap, int64_t nblk,
-                       int64_t first, int64_t last, uint16_t* kbar, hipStream_t s,
-                       const int64_t* lens, int64_t n_new) {
-  const int64_t nb = lens ? (n_new + kBlock - 1) / kBlock + 1 : last - first;
+                       int64_t first, int64_t last, uint16_t* kbar, hipStream_t s) {
+  const int64_t nb = last - first;
   if (nb <= 0) return hipSuccess;
   const int64_t total = int64_t(d.B) * d.Hkv * nb;
   const dim3 grid(unsigned((total + 3) / 4));
   if (d.D == 128)
-    pool_kernel<128><<<grid, 256, 0, s>>>(k, kbar, kv_cap, nblk, first, nb, total, lens, n_new, d.Hkv);
+    pool_kernel<128><<<grid, 256, 0, s>>>(k, kbar, kv_cap, nblk, first, nb, total);
   else
-    pool_kernel<64><<<grid, 256, 0, s>>>(k, kbar, kv_cap, nblk, first, nb, total, lens, n_new, d.Hkv);
+    pool_kernel<64><<<grid, 256, 0, s>>>(k, kbar, kv_cap, nblk, first, nb, total);
   return hipGetLastError();
 }
 
@@ -98,46 +94,61 @@ hipError_t launch_pool(const Dims& d, const uint16_t* k, int64_t kv_cap, int64_t
 // the semantic-kernel representation is the part that grows with the
 // context): n_new tokens' K and V rows [B][Hkv][n_new][D] go to rows
 // len_b .. len_b+n_new-1 of the caches (len_b = lens[b], or kv_len for every
-// sequence); rows that would land at or past kv_cap are not written.
-// Grid-stride over 16-byte pieces, K then V.
+// sequence); rows that would land at or past kv_cap are not written. Every
+// block the append completes is pooled in the same launch.
+//
+// One workgroup per (b, g) and block the append touches (block len_b/64 + t,
+// t < nbt): it copies the appended rows that fall in the block (16-byte
+// pieces, K then V) and, if they complete it, its first wavefront pools the
+// block, taking rows before len_b from the cache and appended rows from the
+// inputs, so no row this launch writes is read back.
+template <int D>
 __global__ __launch_bounds__(256) void append_kv_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache, int64_t kv_cap,
-    const int64_t* __restrict__ lens, int64_t kv_len, int64_t n_new, int D, int Hkv,
-    int64_t total) {
-  const int64_t ppr = D / 8;                          // pieces per row
-  for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < total;
-       e += int64_t(gridDim.x) * 256) {
-    const int64_t per_t = total / 2;                  // pieces per tensor
-    const bool is_v = e >= per_t;
-    const int64_t x = is_v ? e - per_t : e;
-    const int64_t piece = x % ppr;
-    const int64_t i = (x / ppr) % n_new;
-    const int64_t bg = x / (ppr * n_new);
-    const int64_t len0 = lens ? lens[bg / Hkv] : kv_len;
-    const int64_t row = len0 + i;
-    if (len0 < 0 || row >= kv_cap) continue;
-    const uint4 val = ldg16((is_v ? v_new : k_new) + (bg * n_new + i) * D + piece * 8);
-    *reinterpret_cast<uint4*>((is_v ? v_cache : k_cache) + (bg * kv_cap + row) * D + piece * 8) = val;
+    uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache, uint16_t* __restrict__ kbar,
+    int64_t kv_cap, int64_t nblk, const int64_t* __restrict__ lens, int64_t kv_len, int64_t n_new,
+    int Hkv, int nbt) {
+  constexpr int64_t PPR = D / 8;                      // 16-byte pieces per row
+  const int64_t bg = blockIdx.x / nbt;
+  const int64_t len0 = lens ? lens[bg / Hkv] : kv_len;
+  if (len0 < 0) return;
+  const int64_t j = len0 / kBlock + blockIdx.x % nbt;
+  const int64_t r_lo = max(len0, j * kBlock);
+  const int64_t r_hi = min(min(len0 + n_new, (j + 1) * kBlock), kv_cap);
+  if (r_lo >= r_hi) return;                           // no appended row lands in this block
+  const int64_t np = (r_hi - r_lo) * PPR;
+  for (int64_t e = threadIdx.x; e < 2 * np; e += 256) {
+    const bool is_v = e >= np;
+    const int64_t x = is_v ? e - np : e;
+    const int64_t r = r_lo + x / PPR, piece = x % PPR;
+    const uint4 val = ldg16((is_v ? v_new : k_new) + (bg * n_new + (r - len0)) * D + piece * 8);
+    *reinterpret_cast<uint4*>((is_v ? v_cache : k_cache) + (bg * kv_cap + r) * D + piece * 8) = val;
   }
+  if (!kbar || r_hi != (j + 1) * kBlock || threadIdx.x >= kWave) return;
+  const uint16_t* old_rows = k_cache + (bg * kv_cap + j * kBlock) * D;
+  const int64_t r_new = len0 - j * kBlock;            // first appended row within the block
+  pool_block<D>([&](int r) {
+    return r < r_new ? old_rows + r * D : k_new + (bg * n_new + (r - r_new)) * D;
+  }, kbar, bg, j, nblk, int(threadIdx.x));
 }
 
 hipError_t launch_append(const Dims& d, const uint16_t* k_new, const uint16_t* v_new,
                          int64_t n_new, uint16_t* k_cache, uint16_t* v_cache, int64_t kv_cap,
                          const int64_t* lens, int64_t kv_len, uint16_t* kbar, hipStream_t s) {
   if (n_new <= 0) return hipSuccess;
-  const int64_t total = 2 * int64_t(d.B) * d.Hkv * n_new * (d.D / 8);
-  const unsigned blocks = unsigned(std::min<int64_t>(4096, (total + 255) / 256));
-  append_kv_kernel<<<dim3(blocks), 256, 0, s>>>(k_new, v_new, k_cache, v_cache, kv_cap, lens,
-                                                kv_len, n_new, d.D, d.Hkv, total);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !kbar) return e;
-  // the blocks the append completes, read back from the cache in stream order
   const int64_t nblk = (kv_cap + kBlock - 1) / kBlock;
-  if (lens) return launch_pool(d, k_cache, kv_cap, nblk, 0, 0, kbar, s, lens, n_new);
-  const int64_t first = kv_len / kBlock;
-  const int64_t last = std::min(kv_len + n_new, kv_cap) / kBlock;
-  return launch_pool(d, k_cache, kv_cap, nblk, first, last, kbar, s);
+  const int64_t nbt = (n_new + kBlock - 1) / kBlock + 1;   // blocks an append of n_new rows touches
+  const int64_t grid = int64_t(d.B) * d.Hkv * nbt;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  if (d.D == 128)
+    append_kv_kernel<128><<<dim3(unsigned(grid)), 256, 0, s>>>(k_new, v_new, k_cache, v_cache, kbar,
+                                                               kv_cap, nblk, lens, kv_len, n_new,
+                                                               d.Hkv, int(nbt));
+  else
+    append_kv_kernel<64><<<dim3(unsigned(grid)), 256, 0, s>>>(k_new, v_new, k_cache, v_cache, kbar,
+                                                              kv_cap, nblk, lens, kv_len, n_new,
+                                                              d.Hkv, int(nbt));
+  return hipGetLastError();
 }
 
 }  // namespace infllmv2
