@@ -15,8 +15,9 @@
 // block maxima (log2 units) and the tile's partial log-sum-exp per head
 // (max, sum of exp2 relative to it), reduced across the 32 block lanes.
 // score_lse_combine_kernel: per (b, g, node) and chunk of 512 blocks, merges
-// the tile partials into LSE_h and writes R. Workspace: hs [B*Hkv][n_q][G][nblk]
-// fp32 and part [B*Hkv][n_q][G][ntile] float2.
+// the tile partials into LSE_h (one wavefront per head) and writes R.
+// Workspace: hs [B*Hkv][n_q][G][nblk] fp32 and part [B*Hkv][n_q][G][ntile]
+// float2.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -103,9 +104,11 @@ __global__ __launch_bounds__(64) void score_lse_kernel(const uint16_t* __restric
   }
 }
 
-// One workgroup of 256 threads per (b, g, node) and chunk of 512 blocks: each
-// wavefront merges the row's tile partials into LSE_h (lanes over tiles),
-// then every thread writes R for two blocks of the chunk.
+// One workgroup of 256 threads per (b, g, node) and chunk of 512 blocks.
+// Every thread first loads the per-head block values of its two blocks;
+// meanwhile wavefront w merges the tile partials of heads w, w + 4, ... into
+// LSE_h (lanes over tiles) and shares them through LDS; then every thread
+// writes R for its two blocks.
 constexpr int kLseChunk = 512;
 
 template <int G>
@@ -115,13 +118,22 @@ __global__ __launch_bounds__(256) void score_lse_combine_kernel(const float* __r
                                                                 int n_q, int64_t q_pos0,
                                                                 int is_tree, int64_t nblk,
                                                                 int ntile) {
+  constexpr int PER = kLseChunk / 256;
+  __shared__ float s_lse2[G];
   const int l = lane_id();
+  const int w = threadIdx.x / kWave;
   const int64_t rowid = blockIdx.x;                  // (bg, node)
   const int node = int(rowid % n_q);
   const int64_t C = min((is_tree ? q_pos0 : q_pos0 + node) / kBlock, nblk);
-  float lse2[G];
+  const float* hrow = hs + rowid * G * nblk;
+  float hv[PER][G];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
+  for (int x = 0; x < PER; ++x) {
+    const int64_t j = int64_t(blockIdx.y) * kLseChunk + x * 256 + threadIdx.x;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) hv[x][hh] = j < C ? hrow[hh * nblk + j] : -INFINITY;
+  }
+  for (int hh = w; hh < G; hh += 256 / kWave) {
     const float2* pr = part + (rowid * G + hh) * ntile;
     float M = -INFINITY;
     for (int t = l; t < ntile; t += kWave) M = fmaxf(M, pr[t].x);
@@ -135,22 +147,19 @@ __global__ __launch_bounds__(256) void score_lse_combine_kernel(const float* __r
       }
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) S += __shfl_xor(S, o);
-    lse2[hh] = M + log2f(S);                         // S >= 1: the tile holding M adds >= 1
+    if (l == 0) s_lse2[hh] = M + log2f(S);           // S >= 1: the tile holding M adds >= 1
   }
+  __syncthreads();
   float* out = scores + rowid * nblk;
-  const float* hrow = hs + rowid * G * nblk;
 #pragma unroll
-  for (int x = 0; x < kLseChunk / 256; ++x) {
+  for (int x = 0; x < PER; ++x) {
     const int64_t j = int64_t(blockIdx.y) * kLseChunk + x * 256 + threadIdx.x;
     if (j >= nblk) break;
     float r = -INFINITY;
     if (j < C) {
-      float hv[G];
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) hv[hh] = hrow[hh * nblk + j];
       r = 0.f;
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) r += __builtin_amdgcn_exp2f(hv[hh] - lse2[hh]);
+      for (int hh = 0; hh < G; ++hh) r += __builtin_amdgcn_exp2f(hv[x][hh] - s_lse2[hh]);
     }
     out[j] = r;
   }
