@@ -101,12 +101,23 @@ __global__ __launch_bounds__(256) void decode_union_kernel(
   const int tid = threadIdx.x;
   const int64_t P = kv_len - n_q;
   const int nb = int((kv_len - 1) / kBlock) + 1;
+  // the first index entries are loaded before the row masks are cleared, so
+  // their latency overlaps the clearing and its barrier
+  constexpr int kPre = 4;
+  const int ne = n_q * K;
+  int jpre[kPre];
+#pragma unroll
+  for (int x = 0; x < kPre; ++x) {
+    const int e = tid + x * 256;
+    jpre[x] = e < ne ? idx[int64_t(bg) * ne + e] : -1;
+  }
   for (int j = tid; j < nb; j += 256) nm[j] = 0ull;
   __syncthreads();
-  for (int e = tid; e < n_q * K; e += 256) {
+  for (int e = tid; e < ne; e += 256) {
     const int i = e / K;
     const int64_t own = (is_tree ? P : P + i) / kBlock;
-    const int j = idx[(int64_t(bg) * n_q + i) * K + e % K];
+    const int x = (e - tid) / 256;
+    const int j = x < kPre ? jpre[x < kPre ? x : 0] : idx[int64_t(bg) * ne + e];
     if (j >= 0 && j < own) atomicOr(reinterpret_cast<unsigned long long*>(&nm[j]), 1ull << i);
   }
   for (int i = tid; i < n_q; i += 256) {
