@@ -81,6 +81,47 @@ def test_append_writes_rows_and_pools_completed_blocks(varlen, n_new, D):
                 assert (kb[b, :, j] == 0).all(), (b, j)
 
 
+def test_append_past_capacity_is_cut():
+    """Per-sequence appends that reach past the cache capacity: rows at or past kv_cap are not
+    written, and only blocks that end within the capacity are pooled (the last one completed
+    by rows of the append)."""
+    B, L, n_new = 3, 1400, 40
+    w = _workload(B, L, head_dim=128)
+    d = synth.generate(w, seed=6)
+    cap = d["kv_cap"]                                        # 1408: 22 blocks
+    lens0 = [1380, 1350, 1407]
+    note(f"append past capacity: cap {cap} n_new {n_new} lens {lens0}")
+    rng = np.random.default_rng(6)
+    kc, vc = d["k"].copy(), d["v"].copy()
+    for b, l0 in enumerate(lens0):
+        kc[b, :, l0:] = SENTINEL
+        vc[b, :, l0:] = SENTINEL
+    kn = synth.to_bf16_bits(rng.standard_normal((B, w.n_kv_heads, n_new, w.head_dim)).astype(np.float32))
+    vn = synth.to_bf16_bits(rng.standard_normal((B, w.n_kv_heads, n_new, w.head_dim)).astype(np.float32))
+    cfg = cfg_of(w)
+    k_cache, v_cache = dev_bf16(kc), dev_bf16(vc)
+    kbar = torch.zeros(ops.kbar_shape(B, w.n_kv_heads, cap, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    lens = torch.tensor(lens0, dtype=torch.int64, device="cuda")
+    ops.append_kv(cfg, dev_bf16(kn), dev_bf16(vn), k_cache, v_cache, kbar, kv_lens=lens)
+    torch.cuda.synchronize()
+    kg = k_cache.view(torch.int16).cpu().numpy().view(np.uint16)
+    vg = v_cache.view(torch.int16).cpu().numpy().view(np.uint16)
+    kb = _kbar_host(kbar)
+    for b, l0 in enumerate(lens0):
+        l1 = min(l0 + n_new, cap)
+        want_k, want_v = kc[b].copy(), vc[b].copy()
+        want_k[:, l0:l1] = kn[b, :, :l1 - l0]
+        want_v[:, l0:l1] = vn[b, :, :l1 - l0]
+        assert np.array_equal(kg[b], want_k) and np.array_equal(vg[b], want_v), b
+        ref = orc.pool(want_k[None], l1)[0]
+        done = range(l0 // 64, l1 // 64)
+        for j in range(kb.shape[2]):
+            if j in done:
+                assert np.array_equal(kb[b, :, j], ref[:, j]), (b, j)
+            else:
+                assert (kb[b, :, j] == 0).all(), (b, j)
+
+
 def _oracle_step(w, q, kf, vf, b, L):
     """The oracle's decode of sequence b's token at position L - 1 over its first L keys."""
     kbar_o = orc.pool(kf[b:b + 1], L)
