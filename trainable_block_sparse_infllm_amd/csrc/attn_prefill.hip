@@ -62,7 +62,7 @@ __device__ __forceinline__ void prefill_attn_body(
     int64_t window, float scale_log2, int ntile, int umax) {
   if constexpr (WINDOW) mode = 3;
   using Sh = PrefillShape<G>;
-  constexpr int TPS = Sh::TPS, NW = Sh::NW, TQ = Sh::TQ, NT = Sh::NT;
+  constexpr int TPS = Sh::TPS, NW = Sh::NW, TQ = Sh::TQ, NT = Sh::NT, LPS = Sh::LPS;
   constexpr int DS = kD / 16;                // k-steps of S^T = K Q^T
   constexpr int DT = kD / 32;                // 32-wide d tiles of O^T
   constexpr float kRescale = 8.f;            // log2 headroom before the running max is moved
